@@ -1,0 +1,131 @@
+"""LRU slot bank keyed by (layer, expert) (oracle).
+
+Sources:
+  * FreeToken PR #676, "Problem" and "Solution": decode loads only the
+    experts its tokens route to through the slot cache; a prefill chunk hands
+    the LRU its distinct experts one fixed-width query at a time, copies each
+    query's misses before the next query runs, and keeps these admissions out
+    of the decode frequency and the LRU statistics.
+  * Same page, author's reply: the cache is LRU-only, earlier queries need no
+    pin because LRU evicts them last, and a layer never routes to more experts
+    than the cache holds.
+  * vLLM fork PR #48, "What": one bank shared by all MoE layers, keyed
+    (layer, expert), planned by an LRU over the bank.
+
+Readings taken where the pages are silent (each one is a stated choice):
+  1. one recency stamp per query (the clock ticks once per call, also for a
+     query holding only sentinels); ties between equal stamps go to the
+     lower slot index;
+  2. a never-used slot has stamp 0, so empty slots are taken first, lowest
+     index first;
+  3. hits are touched before victims are chosen, so a query never evicts its
+     own hits;
+  4. the i-th miss (query order) takes the i-th candidate in ascending
+     (stamp, slot); candidates are the slots not stamped by this query;
+  5. with record_stats off the recency stamps still move (only the
+     statistics stay untouched);
+  6. a miss with no candidate left sets the capacity error bit and is not
+     admitted.
+key = layer * E + expert.
+
+Parity: pinned (page-printed query splits 128+32 and 3+3+2, statistics
+untouched by prefill, earlier queries evicted last, agreement with a textbook
+recency-list LRU whenever stamps are distinct, bijection invariant).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+ERR_CAPACITY = 1
+
+STAT_HITS, STAT_MISSES, STAT_EVICTIONS, STAT_QUERIES = range(4)
+
+
+@dataclass
+class SlotBankState:
+    S: int
+    L: int
+    E: int
+    slot_key: np.ndarray = None      # int32 [S], -1 empty
+    slot_stamp: np.ndarray = None    # uint64 [S], 0 never used
+    key_to_slot: np.ndarray = None   # int32 [L*E], -1 not resident
+    clock: int = 0
+    stats: np.ndarray = None         # uint64 [4]
+    decode_freq: np.ndarray = None   # uint32 [L*E]
+    err: int = 0
+
+    def __post_init__(self):
+        if self.slot_key is None:
+            self.slot_key = np.full(self.S, -1, np.int32)
+        if self.slot_stamp is None:
+            self.slot_stamp = np.zeros(self.S, np.uint64)
+        if self.key_to_slot is None:
+            self.key_to_slot = np.full(self.L * self.E, -1, np.int32)
+            for s in range(self.S):
+                if self.slot_key[s] >= 0:
+                    self.key_to_slot[self.slot_key[s]] = s
+        if self.stats is None:
+            self.stats = np.zeros(4, np.uint64)
+        if self.decode_freq is None:
+            self.decode_freq = np.zeros(self.L * self.E, np.uint32)
+
+    @classmethod
+    def from_fill(cls, fill):
+        st = cls(fill.S, fill.L, fill.E, fill.slot_key.copy(), fill.slot_stamp.copy())
+        st.clock = int(fill.clock)
+        return st
+
+    def copy(self):
+        c = SlotBankState(self.S, self.L, self.E, self.slot_key.copy(), self.slot_stamp.copy(),
+                          self.key_to_slot.copy(), self.clock, self.stats.copy(),
+                          self.decode_freq.copy(), self.err)
+        return c
+
+
+def ensure_slots(st: SlotBankState, layer: int, query, record_stats: bool):
+    """Admit one query of expert ids of ``layer``; mutates ``st``.
+
+    Returns (miss_slot list, miss_key list): the admitted misses in query
+    order, whose host rows the caller copies into the listed slots before
+    the next query.
+    """
+    st.clock += 1
+    now = st.clock
+    E = st.E
+    keys = [layer * E + int(e) for e in query if 0 <= int(e) < E]
+    hits, misses = [], []
+    for key in keys:
+        s = int(st.key_to_slot[key])
+        if s >= 0:
+            hits.append((key, s))
+        else:
+            misses.append(key)
+    for _, s in hits:
+        st.slot_stamp[s] = now
+    cand = sorted((int(st.slot_stamp[s]), s) for s in range(st.S) if int(st.slot_stamp[s]) < now)
+    miss_slot, miss_key = [], []
+    evicted = 0
+    for i, key in enumerate(misses):
+        if i >= len(cand):
+            st.err |= ERR_CAPACITY
+            continue
+        s = cand[i][1]
+        old = int(st.slot_key[s])
+        if old >= 0:
+            st.key_to_slot[old] = -1
+            evicted += 1
+        st.slot_key[s] = key
+        st.key_to_slot[key] = s
+        st.slot_stamp[s] = now
+        miss_slot.append(s)
+        miss_key.append(key)
+    if record_stats:
+        st.stats[STAT_HITS] += len(hits)
+        st.stats[STAT_MISSES] += len(miss_key)
+        st.stats[STAT_EVICTIONS] += evicted
+        st.stats[STAT_QUERIES] += 1
+        for key in keys:
+            st.decode_freq[key] += 1
+    return miss_slot, miss_key
