@@ -1,0 +1,266 @@
+"""Layer drivers over libscr: the demand (slot) path, the whole-layer stream
+path and the staged prefill path.
+
+PyTorch is used here only to own device / pinned memory and to name streams
+and events; every step of the path is a libscr entry point (HIP kernels or
+DMA).  The drivers keep every intermediate buffer so tests can compare each
+step with the oracle.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+_DEV = "cuda"
+
+
+def _stream(s=None) -> int:
+    s = s if s is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _i32(n, fill=None):
+    t = torch.empty(max(int(n), 1), dtype=torch.int32, device=_DEV)
+    if fill is not None:
+        t.fill_(fill)
+    return t
+
+
+# ------------------------------------------------------------------ records
+
+def record_layout(wdtype: int, H: int, I: int) -> L.RecordLayout:
+    return L.record_layout_of(wdtype, H, I)
+
+
+def pack_record_bf16(lay: L.RecordLayout, w13_bits: np.ndarray, w2_bits: np.ndarray) -> np.ndarray:
+    """Lays out one bf16 expert record (uint8 [record_bytes])."""
+    rec = np.zeros(lay.record_bytes, np.uint8)
+    a = np.ascontiguousarray(w13_bits, np.uint16).view(np.uint8).reshape(-1)
+    b = np.ascontiguousarray(w2_bits, np.uint16).view(np.uint8).reshape(-1)
+    rec[lay.w13_off:lay.w13_off + a.size] = a
+    rec[lay.w2_off:lay.w2_off + b.size] = b
+    return rec
+
+
+def pack_record_nvfp4(lay: L.RecordLayout, d: dict) -> np.ndarray:
+    """Lays out one NVFP4 expert record from codes, scale codes and global scales."""
+    rec = np.zeros(lay.record_bytes, np.uint8)
+    for key, off in (("w13_q", lay.w13_off), ("w13_s", lay.w13_scale_off), ("w2_q", lay.w2_off),
+                     ("w2_s", lay.w2_scale_off)):
+        a = np.ascontiguousarray(d[key], np.uint8).reshape(-1)
+        rec[off:off + a.size] = a
+    rec[lay.g13_off:lay.g13_off + 4] = np.array([d["g13"]], np.float32).view(np.uint8)
+    rec[lay.g2_off:lay.g2_off + 4] = np.array([d["g2"]], np.float32).view(np.uint8)
+    return rec
+
+
+# --------------------------------------------------------------------- bank
+
+class Bank:
+    """Device state of a slot bank plus its record rows (all caller-owned torch memory)."""
+
+    def __init__(self, S: int, n_layers: int, E: int, wdtype: int, record_bytes: int):
+        self.S, self.L, self.E, self.wdtype, self.rec = S, n_layers, E, wdtype, int(record_bytes)
+        self.slot_key = _i32(S, -1)
+        self.slot_stamp = torch.zeros(S, dtype=torch.int64, device=_DEV)
+        self.key_to_slot = _i32(n_layers * E, -1)
+        self.clock = torch.zeros(1, dtype=torch.int64, device=_DEV)
+        self.stats = torch.zeros(4, dtype=torch.int64, device=_DEV)
+        self.decode_freq = torch.zeros(n_layers * E, dtype=torch.int32, device=_DEV)
+        self.err = torch.zeros(1, dtype=torch.int32, device=_DEV)
+        self.rows = torch.zeros(S * self.rec, dtype=torch.uint8, device=_DEV)
+        self.row_table = torch.zeros(S, dtype=torch.int64, device=_DEV)
+        self.desc = L.BankDesc(S, n_layers, E, wdtype, self.slot_key.data_ptr(), self.slot_stamp.data_ptr(),
+                               self.key_to_slot.data_ptr(), self.clock.data_ptr(), self.stats.data_ptr(),
+                               self.decode_freq.data_ptr(), self.err.data_ptr(), self.rows.data_ptr(), self.rec)
+        L.fill_row_table(self.rows, S, self.rec, self.row_table, _stream())
+
+    def load_fill(self, fill, stream=None):
+        """Sets slot_key / slot_stamp / clock from a host BankFill and rebuilds key_to_slot."""
+        self.slot_key.copy_(torch.from_numpy(fill.slot_key.astype(np.int32)))
+        self.slot_stamp.copy_(torch.from_numpy(fill.slot_stamp.astype(np.int64)))
+        self.clock.fill_(int(fill.clock))
+        self.stats.zero_()
+        self.decode_freq.zero_()
+        self.err.zero_()
+        L.bank_rebuild_map(self.desc, _stream(stream))
+
+    def snapshot(self) -> dict:
+        torch.cuda.synchronize()
+        return {
+            "slot_key": self.slot_key.cpu().numpy().copy(),
+            "slot_stamp": self.slot_stamp.cpu().numpy().astype(np.uint64),
+            "key_to_slot": self.key_to_slot.cpu().numpy().copy(),
+            "clock": int(self.clock.item()),
+            "stats": self.stats.cpu().numpy().astype(np.uint64),
+            "decode_freq": self.decode_freq.cpu().numpy().astype(np.uint32),
+            "err": int(self.err.item()),
+        }
+
+    def slot_record(self, s: int) -> torch.Tensor:
+        return self.rows[s * self.rec:(s + 1) * self.rec]
+
+
+# ---------------------------------------------------------------- host pool
+
+class HostPool:
+    """Pinned host records for keys (layer, expert); keys may alias payloads."""
+
+    def __init__(self, n_layers: int, E: int, record_bytes: int, n_payloads: int, payload_of=None):
+        self.L, self.E, self.rec, self.n_payloads = n_layers, E, int(record_bytes), n_payloads
+        self.records = torch.empty(n_payloads * self.rec, dtype=torch.uint8, pin_memory=True)
+        host_base = self.records.data_ptr()
+        dev_base = L.host_device_alias(host_base)
+        keys = np.arange(n_layers * E, dtype=np.int64)
+        pay = keys if payload_of is None else np.asarray([payload_of(int(q)) for q in keys], np.int64)
+        assert pay.min() >= 0 and pay.max() < n_payloads
+        self.payload = pay
+        self.key_rows_host = (host_base + pay * self.rec).astype(np.uint64)
+        self.key_rows_dev = torch.from_numpy((dev_base + pay * self.rec).astype(np.int64)).to(_DEV)
+        self.desc = L.HostPoolDesc(n_layers, E, self.key_rows_dev.data_ptr(), self.key_rows_host.ctypes.data,
+                                   self.rec)
+
+    def write_payload(self, p: int, record: np.ndarray):
+        self.records[p * self.rec:(p + 1) * self.rec].copy_(torch.from_numpy(record))
+
+    def key_record(self, key: int) -> torch.Tensor:
+        p = int(self.payload[key])
+        return self.records[p * self.rec:(p + 1) * self.rec]
+
+
+# ----------------------------------------------------------------- buffers
+
+@dataclass
+class LayerBuffers:
+    """Per-call device buffers of one routed layer."""
+    T: int
+    E: int
+    k: int
+    H: int
+    I: int
+    num_buckets: int
+    wdtype: int
+    width: int = 128
+    y_dtype: int = L.SCR_Y_F32
+    t: dict = field(default_factory=dict)
+
+    def __post_init__(self):
+        R = self.T * self.k
+        self.R = R
+        self.cfg = L.tile_config(self.T, self.k, self.E, self.wdtype)
+        B = self.cfg.block_m
+        self.lmax = min(R, self.E)
+        self.n_queries = max(1, math.ceil(self.lmax / self.width))
+        cap = L.align_capacity(R, self.num_buckets, B)
+        m = min(R, self.num_buckets)
+        self.t = {
+            "topk_ids": _i32(R), "topk_w": torch.empty(max(R, 1), dtype=torch.float32, device=_DEV),
+            "distinct": _i32(self.lmax), "n_distinct": _i32(1), "inverse": _i32(R),
+            "miss_slot": _i32(self.n_queries * self.width, -1), "miss_key": _i32(self.n_queries * self.width, -1),
+            "n_miss": _i32(self.n_queries, 0),
+            "sorted_routes": _i32(cap), "block_bucket": _i32(max(cap // B, 1)), "n_post_pad": _i32(1),
+            "active_buckets": _i32(m), "active_block_begin": _i32(m + 1), "n_active": _i32(1),
+            "align_ws": torch.empty(L.align_workspace(R, self.num_buckets), dtype=torch.uint8, device=_DEV),
+            "moe_ws": torch.empty(L.moe_workspace(self.T, self.k, self.E, self.H, self.I, self.cfg),
+                                  dtype=torch.uint8, device=_DEV),
+            "a_scale": torch.zeros(1, dtype=torch.float32, device=_DEV),
+            "y": torch.empty((self.T, self.H), dtype=torch.float32 if self.y_dtype == L.SCR_Y_F32 else torch.bfloat16,
+                             device=_DEV),
+        }
+        self.cap = cap
+
+    def __getitem__(self, k):
+        return self.t[k]
+
+
+def make_view(layer, E, k, H, I, wdtype, num_buckets, bucket_rows: torch.Tensor, input_scale: torch.Tensor):
+    return L.RoutedExperts(layer, E, k, H, I, wdtype, num_buckets, bucket_rows.data_ptr(), input_scale.data_ptr())
+
+
+# ------------------------------------------------------------------ steps
+
+def route_dedup(buf: LayerBuffers, logits: torch.Tensor, stream=None):
+    s = _stream(stream)
+    L.route(logits, buf.T, buf.E, buf.k, buf["topk_ids"], buf["topk_w"], s)
+    L.dedup(buf["topk_ids"], buf.R, buf.E, buf["distinct"], buf["n_distinct"], buf["inverse"], s)
+
+
+def admit(buf: LayerBuffers, bank: Bank, pool: HostPool, layer: int, record_stats: bool, stream=None):
+    """Hands the distinct list to the LRU one query at a time, copying each
+    query's misses before the next query runs (same stream, no host sync)."""
+    s = _stream(stream)
+    W = buf.width
+    for q in range(buf.n_queries):
+        q0 = q * W
+        w = min(W, buf.lmax - q0)
+        if w <= 0:
+            break
+        ms = buf["miss_slot"][q * W:(q + 1) * W]
+        mk = buf["miss_key"][q * W:(q + 1) * W]
+        nm = buf["n_miss"][q:q + 1]
+        L.ensure_slots(bank.desc, layer, buf["distinct"], q0, w, record_stats, ms, mk, nm, s)
+        L.copy_misses(bank.desc, pool.desc, ms, mk, nm, w, s)
+
+
+def align(buf: LayerBuffers, id_to_bucket, num_ids, stream=None):
+    s = _stream(stream)
+    L.align_blocks(buf["topk_ids"], buf.R, id_to_bucket, num_ids, buf.num_buckets, buf.cfg.block_m,
+                   buf["sorted_routes"], buf["block_bucket"], buf["n_post_pad"], buf["active_buckets"],
+                   buf["active_block_begin"], buf["n_active"], buf["align_ws"], buf["align_ws"].numel(), s)
+
+
+def forward(buf: LayerBuffers, view: L.RoutedExperts, x: torch.Tensor, stream=None, marks=None) -> L.TileCfg:
+    s = _stream(stream)
+    return L.grouped_moe_forward(view, x, buf.T, buf["topk_w"], buf["sorted_routes"], buf["active_buckets"],
+                                 buf["active_block_begin"], buf["n_active"], buf["y"], buf.y_dtype,
+                                 buf["moe_ws"], buf["moe_ws"].numel(), buf["a_scale"], s, marks=marks)
+
+
+def demand_layer(bank: Bank, pool: HostPool, layer: int, logits, x, input_scale, width=128, record_stats=False,
+                 y_dtype=L.SCR_Y_F32, buf: LayerBuffers | None = None, stream=None, shape=None):
+    """Demand (slot) path of one layer: route, dedup, per-query ensure + miss copy,
+    align over the bank's slots through key_to_slot, grouped GEMM at the slots."""
+    T, E = logits.shape
+    k, H, I = shape
+    if buf is None:
+        buf = LayerBuffers(T, E, k, H, I, bank.S, bank.wdtype, width=width, y_dtype=y_dtype)
+    route_dedup(buf, logits, stream)
+    admit(buf, bank, pool, layer, record_stats, stream)
+    id_map = bank.key_to_slot.data_ptr() + layer * E * 4
+    align(buf, id_map, E, stream)
+    view = make_view(layer, E, k, H, I, bank.wdtype, bank.S, bank.row_table, input_scale)
+    buf.cfg_used = forward(buf, view, x, stream)
+    return buf
+
+
+class LayerStreamBuffer:
+    """A device buffer holding every expert record of one layer, plus its row table."""
+
+    def __init__(self, E: int, record_bytes: int):
+        self.E, self.rec = E, int(record_bytes)
+        self.data = torch.empty(E * self.rec, dtype=torch.uint8, device=_DEV)
+        self.row_table = torch.zeros(E, dtype=torch.int64, device=_DEV)
+        L.fill_row_table(self.data, E, self.rec, self.row_table, _stream())
+
+
+def stream_layer(pool: HostPool, layer: int, logits, x, input_scale, layer_buf: LayerStreamBuffer, wdtype,
+                 y_dtype=L.SCR_Y_F32, buf: LayerBuffers | None = None, stream=None, shape=None, copy=True):
+    """Whole-layer path: copy every expert of the layer, align over its experts,
+    same grouped GEMM."""
+    T, E = logits.shape
+    k, H, I = shape
+    if buf is None:
+        buf = LayerBuffers(T, E, k, H, I, E, wdtype, y_dtype=y_dtype)
+    s = _stream(stream)
+    L.route(logits, T, E, k, buf["topk_ids"], buf["topk_w"], s)
+    if copy:
+        L.stream_layer_async(pool.desc, layer, layer_buf.data, s)
+    align(buf, None, 0, stream)
+    view = make_view(layer, E, k, H, I, wdtype, E, layer_buf.row_table, input_scale)
+    buf.cfg_used = forward(buf, view, x, stream)
+    return buf

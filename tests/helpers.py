@@ -1,0 +1,78 @@
+"""Shared set-up for the GPU tests: synthetic pools and banks from the seeded
+generators, and the oracle's view of the same inputs (taken from the
+generators, never from device buffers)."""
+from __future__ import annotations
+
+import os
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+import workloads as W
+from oracle.mlp import bf16_bits_to_f64
+from oracle.nvfp4 import dequant_nvfp4
+
+N_THREADS = min(16, os.cpu_count() or 4)
+
+
+def flush(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_of_f32(a):
+    return W.f32_to_bf16_bits(a)
+
+
+class ExpertSource:
+    """Generator-side expert weights of one workload, by payload id."""
+
+    def __init__(self, seed, H, I, wdtype):
+        self.seed, self.H, self.I, self.wdtype = seed, H, I, wdtype
+        self._cache = {}
+
+    def raw(self, payload):
+        if self.wdtype == "nvfp4":
+            return W.expert_nvfp4(self.seed, payload, self.H, self.I)
+        if self.wdtype == "fp32":
+            w13, w2 = W.expert_f32(self.seed, payload, self.H, self.I)
+            return W.f32_to_bf16_bits(w13), W.f32_to_bf16_bits(w2)
+        return W.expert_bf16(self.seed, payload, self.H, self.I)
+
+    def f64(self, payload):
+        """Decoded fp64 weights, exactly the values the device receives."""
+        if payload in self._cache:
+            return self._cache[payload]
+        r = self.raw(payload)
+        if self.wdtype == "nvfp4":
+            out = (dequant_nvfp4(r["w13_q"], r["w13_s"], r["g13"]), dequant_nvfp4(r["w2_q"], r["w2_s"], r["g2"]))
+        else:
+            out = (bf16_bits_to_f64(r[0]), bf16_bits_to_f64(r[1]))
+        if len(self._cache) < 64:
+            self._cache[payload] = out
+        return out
+
+    def f32_original(self, payload):
+        return W.expert_f32(self.seed, payload, self.H, self.I)
+
+
+def fill_pool(pool, src: ExpertSource, lay, payloads):
+    import slot_cache_routed_amd.layer as LY
+
+    def one(p):
+        r = src.raw(p)
+        rec = LY.pack_record_nvfp4(lay, r) if src.wdtype == "nvfp4" else LY.pack_record_bf16(lay, r[0], r[1])
+        pool.write_payload(p, rec)
+
+    with ThreadPoolExecutor(N_THREADS) as ex:
+        list(ex.map(one, payloads))
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.square(np.asarray(a, np.float64)))))
+
+
+def rel_max_err(y, ref):
+    """max |y - ref| / rms(ref)"""
+    return float(np.max(np.abs(np.asarray(y, np.float64) - ref)) / rms(ref))

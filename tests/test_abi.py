@@ -1,0 +1,101 @@
+"""The C ABI: the library loads, exports every declared entry point, and
+rejects bad arguments before touching the device (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+L = pytest.importorskip("slot_cache_routed_amd._lib")
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "scr.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(scr_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libscr.so not built")
+    return L.load()
+
+
+def test_every_declared_entry_point_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_version_and_host_helpers(lib):
+    assert "gfx950" in L.version()
+    assert L.prefill_on_demand(96, 96) and not L.prefill_on_demand(97, 96)
+    assert not L.prefill_on_demand(1, 0) and L.prefill_on_demand(2, 2)
+    assert L.demand_capacity_ok(96, 10, 512, 1100) and not L.demand_capacity_ok(96, 10, 512, 100)
+
+
+def test_tile_config_depends_on_the_layer_only(lib):
+    a = L.tile_config(600, 2, 8, L.SCR_W_BF16).as_tuple()
+    assert a == L.tile_config(600, 2, 8, L.SCR_W_BF16).as_tuple()
+    assert L.tile_config(96, 10, 512, L.SCR_W_BF16).m_chunk == 64      # ~2 rows per expert
+    assert L.tile_config(4096, 10, 512, L.SCR_W_NVFP4).m_chunk == 128  # ~80 rows per expert
+
+
+def test_record_layouts(lib):
+    b = L.record_layout_of(L.SCR_W_BF16, 2048, 512)
+    assert b.record_bytes == 6291456 and b.w2_off == 4194304
+    f = L.record_layout_of(L.SCR_W_NVFP4, 2048, 512)
+    assert f.w13_scale_off == 1 << 20 and f.w2_off == (1 << 20) + (128 << 10)
+    assert f.g13_off == 1769472 and f.record_bytes % 256 == 0 and f.record_bytes >= 1769472 + 8
+
+
+def test_align_capacity_formula(lib):
+    assert L.align_capacity(960, 1100, 16) == 960 + 960 * 15
+    assert L.align_capacity(40960, 512, 16) == 40960 + 512 * 15
+    assert L.align_capacity(0, 8, 16) == 0
+    assert L.align_workspace(40960, 512) > 0
+
+
+@pytest.mark.parametrize("call", [
+    lambda: L.route(0, 4, 8, 0, 0, 0, None),                 # k = 0
+    lambda: L.route(0, 4, 8, 9, 0, 0, None),                 # k > E
+    lambda: L.route(0, 4, 5000, 2, 0, 0, None),              # E too large
+    lambda: L.route(0, 4, 64, 33, 0, 0, None),               # k > 32
+    lambda: L.route(None, 4, 8, 2, None, None, None),        # null pointers
+    lambda: L.dedup(None, 10, 0, None, None, None, None),    # E = 0
+    lambda: L.align_blocks(0, 10, None, 0, 0, 16, 1, 1, 1, 1, 1, 1, 1, 1 << 20, None),   # 0 buckets
+    lambda: L.align_blocks(0, 10, None, 0, 8, 24, 1, 1, 1, 1, 1, 1, 1, 1 << 20, None),   # block 24
+    lambda: L.align_blocks(1, 10, None, 0, 20000, 16, 1, 1, 1, 1, 1, 1, 1, 1 << 30, None),  # > max buckets
+    lambda: L.align_blocks(1, 10, None, 0, 8, 16, 1, 1, 1, 1, 1, 1, 1, 4, None),         # tiny workspace
+    lambda: L.tile_config(1, 0, 8, 0),
+    lambda: L.tile_config(1, 1, 8, 7),
+])
+def test_bad_arguments_are_rejected_before_any_launch(lib, call):
+    with pytest.raises(L.ScrError) as ei:
+        call()
+    assert ei.value.code in (L.SCR_EINVAL, L.SCR_ENOTSUP)
+
+
+def test_bank_and_view_validation(lib):
+    bank = L.BankDesc(0, 1, 8, 0, 1, 1, 1, 1, 1, 1, 1, 1, 16)        # S = 0
+    with pytest.raises(L.ScrError):
+        L.ensure_slots(bank, 0, 1, 0, 4, 0, 1, 1, 1, None)
+    bank = L.BankDesc(16, 2, 8, 0, 1, 1, 1, 1, 1, 1, 1, 1, 16)
+    with pytest.raises(L.ScrError):
+        L.ensure_slots(bank, 2, 1, 0, 4, 0, 1, 1, 1, None)          # layer out of range
+    with pytest.raises(L.ScrError):
+        L.ensure_slots(bank, 0, 1, 0, 2000, 0, 1, 1, 1, None)       # width too large
+    pool = L.HostPoolDesc(2, 8, 1, 1, 32)
+    with pytest.raises(L.ScrError):
+        L.copy_misses(bank, pool, 1, 1, 1, 4, None)                 # record sizes differ
+    view = L.RoutedExperts(0, 8, 2, 100, 512, 0, 8, 1, 1)            # H not a multiple of 64
+    with pytest.raises(L.ScrError):
+        L.grouped_moe_forward(view, 1, 4, 1, 1, 1, 1, 1, 1, 0, 1, 1 << 30, None, None)
+    view = L.RoutedExperts(0, 8, 2, 256, 128, 0, 8, 1, 1)
+    with pytest.raises(L.ScrError):                                  # workspace too small
+        L.grouped_moe_forward(view, 1, 4, 1, 1, 1, 1, 1, 1, 0, 1, 16, None, None)

@@ -1,0 +1,229 @@
+"""GPU parity of the whole routed layer: demand (slot) path against the
+oracle, slot path bit-identical to the whole-layer stream path, the layer
+view's tiles and scales, NVFP4 decode in the GEMM, and 64-bit row offsets."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from helpers import ExpertSource, fill_pool, flush, rel_max_err
+from oracle import moe_layer, moe_layer_tokens, route_topk_softmax
+from oracle.mlp import bf16_bits_to_f64
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2   # max |y - y_ref| / rms(y_ref)
+TOL_FP4 = 5e-2
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+@functools.lru_cache(maxsize=None)
+def _setup(name, S=None, W_=None, prefill=None, wdtype=None, T=None, E=None, k=None, H=None, I=None, NL=None):
+    """Pool, bank and inputs of one workload (cached per process)."""
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    cfg = W.CONFIGS.get(name)
+    T = T or cfg.T
+    E = E or cfg.shape.E
+    k = k or cfg.shape.k
+    H = H or cfg.shape.H
+    I = I or cfg.shape.I
+    wd = wdtype or cfg.shape.wdtype
+    S = S or cfg.S
+    NL = NL or cfg.L
+    seed = cfg.seed if cfg else 77
+    wcode = L.SCR_W_NVFP4 if wd == "nvfp4" else L.SCR_W_BF16
+    lay = LY.record_layout(wcode, H, I)
+    src = ExpertSource(seed, H, I, wd)
+    flush(f"setup {name}: T={T} E={E} k={k} H={H} I={I} {wd} S={S} layers={NL}")
+    pool = LY.HostPool(NL, E, lay.record_bytes, E, payload_of=lambda key: key % E)
+    fill_pool(pool, src, lay, range(E))
+    if name == "short_prefill_96":
+        lg, D = W.logits_with_chosen(seed, T, E, k, 160)
+    else:
+        lg = W.logits_normal(seed, 0, T, E)
+    xb = W.f32_to_bf16_bits(W.activations_normal(seed, T, H))
+    return dict(LY=LY, L=L, T=T, E=E, k=k, H=H, I=I, wd=wd, wcode=wcode, S=S, NL=NL, seed=seed, lay=lay, src=src,
+                pool=pool, logits=lg, xbits=xb, W=W_ or (cfg.W if cfg else 8), prefill=prefill)
+
+
+def _bank_for(s, fill=None):
+    bank = s["LY"].Bank(s["S"], s["NL"], s["E"], s["wcode"], s["lay"].record_bytes)
+    if fill is not None:
+        bank.load_fill(fill)
+    return bank
+
+
+def _run_demand(s, bank, input_scale, y_dtype=0, width=None):
+    LY = s["LY"]
+    return LY.demand_layer(bank, s["pool"], 0, _dev(s["logits"]), _dev(s["xbits"].view(np.int16)),
+                           _dev(input_scale), width=width or s["W"], record_stats=False, y_dtype=y_dtype,
+                           shape=(s["k"], s["H"], s["I"]))
+
+
+def _run_stream(s, input_scale, y_dtype=0):
+    LY = s["LY"]
+    lb = LY.LayerStreamBuffer(s["E"], s["lay"].record_bytes)
+    return LY.stream_layer(s["pool"], 0, _dev(s["logits"]), _dev(s["xbits"].view(np.int16)), _dev(input_scale),
+                           lb, s["wcode"], y_dtype=y_dtype, shape=(s["k"], s["H"], s["I"]))
+
+
+def _oracle(s, tokens=None):
+    ids, w = route_topk_softmax(s["logits"], s["k"])
+    x = bf16_bits_to_f64(s["xbits"])
+    if tokens is None:
+        return moe_layer(x, ids, w, s["src"].f64), ids, w
+    return moe_layer_tokens(x, ids, w, s["src"].f64, tokens), ids, w
+
+
+def _y(buf):
+    torch.cuda.synchronize()
+    return buf["y"].float().cpu().numpy()
+
+
+def test_tiny_layer_demand_vs_oracle_and_stream():
+    s = _setup("tiny")
+    bank = _bank_for(s)
+    sc = np.ones(s["E"], np.float32)
+    d = _run_demand(s, bank, sc)
+    y = _y(d)
+    y_ref, ids, w = _oracle(s)
+    assert np.array_equal(d["topk_ids"].cpu().numpy().reshape(ids.shape), ids)
+    err = rel_max_err(y, y_ref)
+    flush(f"tiny: rel max err vs oracle on the bf16 weights = {err:.3e}")
+    assert err <= TOL_BF16
+    # against the fp32 originals the difference also includes the bf16 upload
+    x = bf16_bits_to_f64(s["xbits"])
+    y_f32w = moe_layer(x, ids, w, lambda e: tuple(a.astype(np.float64) for a in s["src"].f32_original(e)))
+    flush(f"tiny: rel max err vs fp32 original weights = {rel_max_err(y, y_f32w):.3e}")
+    st = _run_stream(s, sc)
+    assert torch.equal(d["y"], st["y"]), "slot path equals the whole-layer path bit for bit"
+
+
+def test_short_prefill_96_demand_path():
+    s = _setup("short_prefill_96")
+    fill = W.bank_prefilled(s["seed"], s["S"], s["NL"], s["E"], 600, exclude_layer=0)
+    bank = _bank_for(s, fill)
+    sc = np.ones(s["E"], np.float32)
+    d = _run_demand(s, bank, sc)
+    y = _y(d)
+    nm = d["n_miss"].cpu().numpy().tolist()
+    assert nm == [128, 32, 0, 0], nm
+    assert np.all(bank.snapshot()["stats"] == 0) and np.all(bank.snapshot()["decode_freq"] == 0)
+    flush("short prefill: oracle over 96 tokens")
+    y_ref, ids, _ = _oracle(s)
+    err = rel_max_err(y, y_ref)
+    flush(f"short prefill: rel max err = {err:.3e}")
+    assert err <= TOL_BF16
+    # the 160 admitted rows hold the pool's bytes
+    snap = bank.snapshot()
+    for e in np.unique(ids)[:8]:
+        slot = snap["key_to_slot"][e]
+        assert torch.equal(bank.slot_record(slot).cpu(), s["pool"].key_record(int(e)))
+    st = _run_stream(s, sc)
+    assert torch.equal(d["y"], st["y"]), "slot path equals the whole-layer path bit for bit"
+    # bf16 output mode is the same numbers rounded
+    d2 = _run_demand(s, bank, sc, y_dtype=1)
+    assert torch.equal(d2["y"].float(), d["y"].to(torch.bfloat16).float())
+
+
+def test_layer_view_sizes_tiles_and_scales_by_the_layer():
+    s = _setup("layer_view_600")
+    L = s["L"]
+    fill = W.bank_prefilled(s["seed"], s["S"], s["NL"], s["E"], s["S"], exclude_layer=0)   # full bank
+    bank = _bank_for(s, fill)
+    layer_scales = W.c3_input_scales(s["E"])
+    d = _run_demand(s, bank, layer_scales)
+    y = _y(d)
+    want = L.tile_config(600, 2, 8, L.SCR_W_BF16).as_tuple()
+    assert d.cfg_used.as_tuple() == want
+    assert want != L.tile_config(600, 2, s["S"], L.SCR_W_BF16).as_tuple(), "a bank-sized config would differ"
+    assert float(d["a_scale"].item()) == 3.0        # the layer's max, not the bank's 9.0
+    assert d["n_miss"].cpu().numpy()[0] == 8
+    st = _run_stream(s, layer_scales)
+    assert torch.equal(d["y"], st["y"])
+    y_ref, _, _ = _oracle(s, tokens=range(0, 600, 7))
+    assert rel_max_err(y[0:600:7], y_ref) <= TOL_BF16
+
+
+def test_layer_view_one_layer_cache_three_per_query():
+    s = _setup("layer_view_600_s8")
+    fill = W.bank_prefilled(s["seed"], 8, s["NL"], s["E"], 8, exclude_layer=0)
+    bank = _bank_for(s, fill)
+    sc = W.c3_input_scales(s["E"])
+    d = _run_demand(s, bank, sc, width=3)
+    assert d["n_miss"].cpu().numpy().tolist() == [3, 3, 2]
+    st = _run_stream(s, sc)
+    assert torch.equal(d["y"], st["y"])
+
+
+@pytest.mark.parametrize("T,E,k,H,I", [(64, 16, 4, 256, 128), (200, 32, 6, 512, 256), (37, 8, 3, 128, 64)])
+def test_nvfp4_layer_vs_oracle_and_stream(T, E, k, H, I):
+    s = _setup(f"fp4_{T}_{E}", S=2 * E, W_=8, wdtype="nvfp4", T=T, E=E, k=k, H=H, I=I, NL=2)
+    bank = _bank_for(s)
+    sc = np.ones(E, np.float32)
+    d = _run_demand(s, bank, sc)
+    y = _y(d)
+    y_ref, _, _ = _oracle(s)
+    err = rel_max_err(y, y_ref)
+    flush(f"nvfp4 {T}x{E} k={k} H={H} I={I}: rel max err = {err:.3e}")
+    assert err <= TOL_FP4
+    st = _run_stream(s, sc)
+    assert torch.equal(d["y"], st["y"])
+
+
+def test_bf16_ragged_shapes_vs_oracle():
+    # many tiles with a ragged tail of rows per bucket
+    s = _setup("ragged", S=100, W_=16, wdtype="bf16", T=333, E=24, k=5, H=384, I=192, NL=3)
+    bank = _bank_for(s)
+    sc = np.ones(s["E"], np.float32)
+    d = _run_demand(s, bank, sc)
+    y_ref, _, _ = _oracle(s)
+    assert rel_max_err(_y(d), y_ref) <= TOL_BF16
+    st = _run_stream(s, sc)
+    assert torch.equal(d["y"], st["y"])
+
+
+def test_rows_past_32_gib_of_bank():
+    """The same expert at slot 0 and at a slot whose byte offset is past 2^35
+    gives identical outputs; a zero record gives a different one."""
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    H, I, T = 2048, 512, 8
+    lay = LY.record_layout(L.SCR_W_BF16, H, I)
+    S = (1 << 35) // lay.record_bytes + 2
+    far = S - 1
+    assert far * lay.record_bytes > (1 << 35)
+    src = ExpertSource(91, H, I, "bf16")
+    pool = LY.HostPool(1, 1, lay.record_bytes, 1)
+    fill_pool(pool, src, lay, [0])
+    lg = np.zeros((T, 1), np.float32)
+    x = _dev(W.f32_to_bf16_bits(W.activations_normal(91, T, H)).view(np.int16))
+    sc = _dev(np.ones(1, np.float32))
+    bank = LY.Bank(S, 1, 1, L.SCR_W_BF16, lay.record_bytes)
+    outs = []
+    for slot, zero in ((0, False), (far, False), (far, True)):
+        fill = W.bank_empty(S, 1, 1)
+        fill.slot_key[slot] = 0
+        fill.slot_stamp[slot] = 1
+        fill.clock = 1
+        bank.load_fill(fill)
+        rec = bank.slot_record(slot)
+        if zero:
+            rec.zero_()
+        else:
+            rec.copy_(pool.key_record(0).cuda())
+        d = LY.demand_layer(bank, pool, 0, _dev(lg), x, sc, width=1, shape=(1, H, I))
+        assert d["n_miss"].cpu().numpy()[0] == 0
+        outs.append(_y(d))
+        if slot != 0:
+            rec.zero_()
+    assert np.array_equal(outs[0], outs[1])
+    assert not np.array_equal(outs[0], outs[2])
+    del bank
+    torch.cuda.empty_cache()
