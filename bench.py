@@ -1,0 +1,379 @@
+#!/usr/bin/env python
+"""Routed MoE layer over a shared slot cache: layer ms and grouped-GEMM
+TFLOP/s on one MI355X.
+
+Workload (one step = the whole hot path over one 96-token chunk): a layer of
+512 experts (top-10, hidden 2048, intermediate 512, bf16 weights), a chunk
+routed to exactly 160 distinct experts, a 1100-slot bank pre-filled with 600
+experts of other layers, admission in queries of 128.  Each step runs route,
+dedup, four LRU queries each followed by its miss copy, align over the
+bank's slots, the gate/up and down grouped GEMMs and the combine.
+
+`value` is measured with the chunk's experts already resident in HBM (a
+warm bank: every query hits, every miss copy has nothing to move), so the
+timed region holds no PCIe transfer.  The cold step (bank reset to its
+pre-filled state, 160 misses copied from pinned host memory) is reported
+beside it under "cold".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "routed MoE layer ms + grouped-GEMM TFLOP/s at 96 and 4096 tokens, 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--cold-reps", type=int, default=3)
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle's CPU sample")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-long", action="store_true", help="skip the 4096-token staged NVFP4 measurement")
+    p.add_argument("--long-layers", type=int, default=8)
+    p.add_argument("--long-reps", type=int, default=3)
+    p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gateup_short_prefill_96.json"),
+                   help="HBM traffic of the dominant kernel from rocprofv3 counters (JSON), if present")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain device copy of known size (counter calibration) and exit")
+    return p.parse_args()
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def calibrate_copy(steps: int):
+    import torch
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        torch.add(a, 0.0, out=b)   # reads 1 GiB, writes 1 GiB
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "elementwise add", "read_bytes": n, "write_bytes": n, "launches": steps}))
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported on this build "
+              f"(multi-GPU sharding is described, not run)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(max(1, args.steps))
+        return
+
+    import workloads as W
+    import slot_cache_routed_amd._lib as L
+    import slot_cache_routed_amd.layer as LY
+
+    torch.cuda.set_device(0)
+    L.load()
+    cfg = W.C2
+    T, E, k, H, I = cfg.T, cfg.shape.E, cfg.shape.k, cfg.shape.H, cfg.shape.I
+    S, NL, Wd = cfg.S, cfg.L, cfg.W
+    R = T * k
+    lay = LY.record_layout(L.SCR_W_BF16, H, I)
+    rec = int(lay.record_bytes)
+
+    # ------------------------------------------------------------ inputs
+    t0 = time.time()
+    pool = LY.HostPool(NL, E, rec, E, payload_of=lambda key: key % E)
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(e):
+        b13, b2 = W.expert_bf16(cfg.seed, e, H, I)
+        pool.write_payload(e, LY.pack_record_bf16(lay, b13, b2))
+
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+        list(ex.map(one, range(E)))
+    lg, D = W.logits_with_chosen(cfg.seed, T, E, k, 160)
+    xb = W.f32_to_bf16_bits(W.activations_normal(cfg.seed, T, H))
+    fill = W.bank_prefilled(cfg.seed, S, NL, E, 600, exclude_layer=0)
+    _log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    logits, x = dev(lg), dev(xb.view(np.int16))
+    scales = dev(np.ones(E, np.float32))
+    bank = LY.Bank(S, NL, E, L.SCR_W_BF16, rec)
+    buf = LY.LayerBuffers(T, E, k, H, I, S, L.SCR_W_BF16, width=Wd, y_dtype=L.SCR_Y_BF16)
+    id_map = bank.key_to_slot.data_ptr()        # layer 0
+    view = LY.make_view(0, E, k, H, I, L.SCR_W_BF16, S, bank.row_table, scales)
+    stream = torch.cuda.current_stream()
+
+    def step(marks=None, phase_events=None):
+        if phase_events:
+            LY.record_timer(phase_events[0])
+        LY.route_dedup(buf, logits)
+        if phase_events:
+            LY.record_timer(phase_events[1])
+        LY.admit(buf, bank, pool, 0, record_stats=False)
+        if phase_events:
+            LY.record_timer(phase_events[2])
+        LY.align(buf, id_map, E)
+        LY.forward(buf, view, x, marks=marks)
+        if phase_events:
+            LY.record_timer(phase_events[3])
+
+    ev = L.Timer
+
+    # ------------------------------------------------------------ cold
+    cold = []
+    for _ in range(args.cold_reps):
+        bank.load_fill(fill)
+        torch.cuda.synchronize()
+        pe = [ev() for _ in range(4)]
+        step(phase_events=pe)
+        torch.cuda.synchronize()
+        cold.append((pe[0].elapsed_ms(pe[3]), pe[1].elapsed_ms(pe[2])))
+    n_miss = buf["n_miss"].cpu().numpy().tolist()
+    assert n_miss[:2] == [128, 32], n_miss
+    cold_ms = statistics.median(c[0] for c in cold)
+    copy_ms = statistics.median(c[1] for c in cold)
+    copy_bytes = 160 * rec
+
+    # ------------------------------------------------------------ warm
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_active = int(buf["n_active"].item())
+    marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    handles = [[m.handle for m in ms] for ms in marks]
+    # the same steps without timing events, for the cost of the events themselves
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_no_events = (time.perf_counter() - t_start) * 1e3 / args.steps
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(marks=handles[i])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    assert buf["n_miss"].cpu().numpy().sum() == 0, "warm steps admit nothing"
+    ms_per_step = (t_end - t_start) * 1e3 / args.steps
+    gu_ms = [m[1].elapsed_ms(m[2]) for m in marks]
+    dn_ms = [m[2].elapsed_ms(m[3]) for m in marks]
+    cb_ms = [m[3].elapsed_ms(m[4]) for m in marks]
+    gu = statistics.mean(gu_ms)
+    dn = statistics.mean(dn_ms)
+    cb = statistics.mean(cb_ms)
+    flops = 6.0 * R * H * I
+    gemm_tflops = flops / ((gu + dn) * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: gate/up, HBM-bound (6 flop per weight byte pair at ~6 rows/expert)
+    w13_bytes = 2 * I * H * 2
+    gu_bytes = n_active * w13_bytes + R * H * 2 + R * I * 2
+    achieved = gu_bytes / (gu * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            tr = json.load(f)
+        traffic = tr.get("bytes_per_launch")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "short_prefill_96: 96 tokens, 512 experts, top-10, hidden 2048, intermediate 512, "
+                               "bf16 weights, 160 distinct experts, 1100-slot bank (600 other-layer experts), "
+                               "queries of 128, warm bank",
+                   "tokens": T, "experts": E, "top_k": k, "hidden": H, "intermediate": I, "slots": S,
+                   "distinct": n_active, "query_width": Wd},
+        "layer_ms": round(ms_per_step, 4),
+        "ms_per_step_without_timing_events": round(ms_no_events, 4),
+        "gemm_tflops": round(gemm_tflops, 3),
+        "kernels_us": {"gate_up": round(gu * 1e3, 2), "down": round(dn * 1e3, 2), "combine": round(cb * 1e3, 2)},
+        "cold": {"ms_per_step": round(cold_ms, 3), "miss_copy_ms": round(copy_ms, 3),
+                 "miss_copy_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 2), "misses": 160,
+                 "note": "bank reset to its pre-filled state before each step; includes PCIe host-to-HBM copies"},
+        "roofline": {"bound": "hbm", "kernel": "gateup_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": gu_bytes},
+    }
+    del bank, buf, pool
+    torch.cuda.empty_cache()
+    if not args.no_long:
+        out["long_prefill_4096"] = long_prefill(args)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out))
+
+
+def long_prefill(args) -> dict:
+    """4096-token chunk, 512 NVFP4 experts per layer, 193 resident per layer:
+    staged prefill over consecutive layers with next-layer prefetch, and the
+    grouped GEMM alone on resident data."""
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    import workloads as W
+    import slot_cache_routed_amd._lib as L
+    import slot_cache_routed_amd.layer as LY
+
+    cfg = W.C5
+    T, E, k, H, I = cfg.T, cfg.shape.E, cfg.shape.k, cfg.shape.H, cfg.shape.I
+    NL = args.long_layers
+    n_res = cfg.notes["resident_per_layer"]
+    R = T * k
+    lay = LY.record_layout(L.SCR_W_NVFP4, H, I)
+    rec = int(lay.record_bytes)
+    t0 = time.time()
+    pool = LY.HostPool(NL, E, rec, NL * E)
+
+    def one(key):
+        pool.write_payload(key, LY.pack_record_nvfp4(lay, W.expert_nvfp4(cfg.seed, key, H, I)))
+
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+        list(ex.map(one, range(NL * E)))
+    _log(f"long prefill: {NL} layers of NVFP4 records ready in {time.time() - t0:.1f}s")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    bank = LY.Bank(cfg.S, NL, E, L.SCR_W_NVFP4, rec)
+    s = torch.cuda.current_stream().cuda_stream
+    for layer in range(NL):
+        res = dev(W.resident_experts(cfg.seed, layer, E, n_res))
+        ms = torch.zeros(n_res, dtype=torch.int32, device="cuda")
+        mk = torch.zeros(n_res, dtype=torch.int32, device="cuda")
+        nm = torch.zeros(1, dtype=torch.int32, device="cuda")
+        L.ensure_slots(bank.desc, layer, res, 0, n_res, 0, ms, mk, nm, s)
+        L.copy_misses(bank.desc, pool.desc, ms, mk, nm, n_res, s)
+    torch.cuda.synchronize()
+    logits = [dev(W.logits_normal(cfg.seed, layer, T, E)) for layer in range(NL)]
+    x = dev(W.f32_to_bf16_bits(W.activations_normal(cfg.seed, T, H)).view(np.int16))
+    sc = dev(np.ones(E, np.float32))
+    bufs = [LY.LayerBuffers(T, E, k, H, I, E, L.SCR_W_NVFP4, y_dtype=L.SCR_Y_BF16) for _ in range(NL)]
+    sp = LY.StagedPrefill(bank, pool)
+    layers = list(range(NL))
+
+    reps = []
+    for rep in range(args.long_reps + 1):        # the first pass warms up
+        timers = [[L.Timer() for _ in range(5)] for _ in layers]
+        t_a, t_b = L.Timer(), L.Timer()
+        torch.cuda.synchronize()
+        t_a.record(s)
+        sp.plan(0, NL)                           # the step's one host sync
+        sp.run(layers, logits, x, sc, bufs, timers=timers)
+        t_b.record(s)
+        total = t_a.elapsed_ms(t_b)
+        gu = [t[1].elapsed_ms(t[2]) for t in timers]
+        dn = [t[2].elapsed_ms(t[3]) for t in timers]
+        if rep:
+            reps.append((total, gu, dn))
+    staged_bytes = sum(sp.staged_bytes(l) for l in layers)
+    total = statistics.median(r[0] for r in reps)
+    # grouped GEMM alone, data resident (the last staged layer's view), repeated
+    b = bufs[-1]
+    view = LY.make_view(layers[-1], E, k, H, I, L.SCR_W_NVFP4, E, sp.tables[(NL - 1) % 2], sc)
+    gus, dns = [], []
+    for i in range(10):
+        tm = [L.Timer() for _ in range(5)]
+        LY.forward(b, view, x, marks=[t.handle for t in tm])
+        torch.cuda.synchronize()
+        if i >= 2:
+            gus.append(tm[1].elapsed_ms(tm[2]))
+            dns.append(tm[2].elapsed_ms(tm[3]))
+    gu, dn = statistics.mean(gus), statistics.mean(dns)
+    flops = 6.0 * R * H * I
+    tflops = flops / ((gu + dn) * 1e-3) / 1e12
+    wbytes = E * (rec - 256)
+    return {
+        "workload": f"long_prefill_4096: 4096 tokens, 512 experts, top-10, hidden 2048, intermediate 512, NVFP4 "
+                    f"(e2m1 + e4m3/16 + fp32 global), {n_res} resident rows per layer, {NL} layers staged with "
+                    f"next-layer prefetch",
+        "layer_ms_staged": round(total / NL, 3),
+        "staging_GBps": round(staged_bytes / (total * 1e-3) / 1e9, 2),
+        "staged_bytes_per_layer": staged_bytes // NL,
+        "gemm_tflops": round(tflops, 2),
+        "gemm_frac_bf16_mfma_peak": round(tflops / 2500.0, 4),
+        "kernels_us": {"gate_up": round(gu * 1e3, 1), "down": round(dn * 1e3, 1)},
+        "gemm_us_in_pipeline": {"gate_up": round(statistics.mean(x for r in reps for x in r[1]) * 1e3, 1),
+                                "down": round(statistics.mean(x for r in reps for x in r[2]) * 1e3, 1)},
+        "weight_bytes_per_layer": wbytes,
+    }
+
+
+def cpu_baseline(budget_s: float) -> dict:
+    """The oracle, as it stands, over a bounded sample of the same workload."""
+    import numpy as np
+    import workloads as W
+    from oracle import (SlotBankState, align_blocks, dedup_sorted, ensure_slots, moe_layer_tokens,
+                        route_topk_softmax)
+    from oracle.mlp import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    cfg = W.C2
+    T, E, k, H, I = cfg.T, cfg.shape.E, cfg.shape.k, cfg.shape.H, cfg.shape.I
+    lg, _ = W.logits_with_chosen(cfg.seed, T, E, k, 160)
+    x = bf16_bits_to_f64(W.f32_to_bf16_bits(W.activations_normal(cfg.seed, T, H)))
+    fill = W.bank_prefilled(cfg.seed, cfg.S, cfg.L, E, 600, exclude_layer=0)
+    # the oracle's inputs (fp64 weights of the 160 routed experts) are made
+    # before the clock starts: generating them is not the oracle's work
+    from concurrent.futures import ThreadPoolExecutor
+    ids0, _ = route_topk_softmax(lg, k)
+
+    def gen(e):
+        b13, b2 = W.expert_bf16(cfg.seed, int(e), H, I)
+        return int(e), (bf16_bits_to_f64(b13), bf16_bits_to_f64(b2))
+
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+        cache = dict(ex.map(gen, np.unique(ids0)))
+    weights = cache.__getitem__
+
+    # sample: whole-chunk passes of the oracle path (route, dedup, the four
+    # LRU queries, align over the slots, expert MLP and combine) repeated
+    # until the time budget is used
+    flops = 6.0 * T * k * H * I
+    passes, spent = 0, 0.0
+    while spent < budget_s:
+        t0 = time.perf_counter()
+        ids, w = route_topk_softmax(lg, k)
+        distinct, _, _ = dedup_sorted(ids.reshape(-1), E)
+        st = SlotBankState.from_fill(fill)
+        for q0 in range(0, distinct.size, cfg.W):
+            ensure_slots(st, 0, distinct[q0:q0 + cfg.W], False)
+        align_blocks(ids.reshape(-1), st.key_to_slot[:E], cfg.S, 16)
+        moe_layer_tokens(x, ids, w, weights, range(T))
+        spent += time.perf_counter() - t0
+        passes += 1
+    per = spent / passes
+    return {"value": round(flops / per / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{passes} whole-chunk passes of the 96-token short-prefill path (route, dedup, LRU "
+                      f"queries, align, expert MLP, combine); {per * 1e3:.1f} ms per chunk",
+            "seconds": round(spent, 2)}
+
+
+if __name__ == "__main__":
+    main()

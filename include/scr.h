@@ -264,7 +264,8 @@ int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cf
  *               (what an activation-quantising GEMM would quantise under)
  *   marks       host array of 5 events or NULL: recorded on `stream` before
  *               the prologue and after the prologue, gate/up, down and
- *               combine kernels (per-kernel timing on the launching stream)
+ *               combine kernels (per-kernel timing on the launching stream);
+ *               NULL entries are skipped
  * H % 64 == 0, I % 64 == 0 (NVFP4 as well), 64 <= H, I <= 16384. */
 int scr_grouped_moe_forward(const scr_routed_experts* view, const void* x, int T,
                             const float* topk_w, const int32_t* sorted_routes,
@@ -322,6 +323,14 @@ int scr_host_device_alias(const void* host_ptr, void** dev_ptr);
 int scr_prefill_on_demand(int T, int threshold);
 /* capacity guard [P1 author's reply; P2 commit 2]: min(T*k, E) <= S (or <= S/2) */
 int scr_demand_capacity_ok(int T, int k, int E, int S, int half);
+
+/* timing events for per-kernel measurement on the launching stream: created
+ * with hipEventDisableSystemFence, so recording one between kernels costs no
+ * cache write-back.  elapsed waits for `stop`, then reports stop - start in ms. */
+int scr_timer_create(hipEvent_t* ev);
+int scr_timer_record(hipEvent_t ev, hipStream_t stream);
+int scr_timer_elapsed_ms(hipEvent_t start, hipEvent_t stop, float* ms);
+int scr_timer_destroy(hipEvent_t ev);
 
 const char* scr_last_error(void);
 const char* scr_version(void);

@@ -29,8 +29,8 @@ EXPORTS = (
     "scr_align_capacity", "scr_align_workspace", "scr_align_blocks", "scr_tile_config",
     "scr_moe_workspace", "scr_grouped_moe_forward", "scr_stream_layer_async", "scr_stage_plan",
     "scr_stage_rows_async", "scr_fill_row_table", "scr_fill_staged_rows", "scr_bank_rebuild_map",
-    "scr_host_device_alias", "scr_prefill_on_demand", "scr_demand_capacity_ok", "scr_last_error",
-    "scr_version",
+    "scr_host_device_alias", "scr_prefill_on_demand", "scr_demand_capacity_ok", "scr_timer_create",
+    "scr_timer_record", "scr_timer_elapsed_ms", "scr_timer_destroy", "scr_last_error", "scr_version",
 )
 
 
@@ -103,6 +103,10 @@ _SIGS = {
     "scr_host_device_alias": (_I, [_P, C.POINTER(_P)]),
     "scr_prefill_on_demand": (_I, [_I, _I]),
     "scr_demand_capacity_ok": (_I, [_I, _I, _I, _I, _I]),
+    "scr_timer_create": (_I, [C.POINTER(_P)]),
+    "scr_timer_record": (_I, [_P, _P]),
+    "scr_timer_elapsed_ms": (_I, [_P, _P, C.POINTER(C.c_float)]),
+    "scr_timer_destroy": (_I, [_P]),
     "scr_last_error": (C.c_char_p, []),
     "scr_version": (C.c_char_p, []),
 }
@@ -203,7 +207,7 @@ def grouped_moe_forward(view: RoutedExperts, x, T, topk_w, sorted_routes, active
     cfg = TileCfg()
     ev = None
     if marks is not None:
-        ev = (C.c_void_p * 5)(*[int(m) for m in marks])
+        ev = (C.c_void_p * 5)(*[int(m) if m else None for m in marks])
     _check("scr_grouped_moe_forward", load().scr_grouped_moe_forward(
         C.byref(view), _p(x), T, _p(topk_w), _p(sorted_routes), _p(active_buckets), _p(active_block_begin),
         _p(n_active), _p(y), y_dtype, _p(ws), ws_bytes, C.byref(cfg), _p(a_scale_out),
@@ -252,6 +256,30 @@ def prefill_on_demand(T, threshold) -> bool:
 
 def demand_capacity_ok(T, k, E, S, half=False) -> bool:
     return bool(load().scr_demand_capacity_ok(T, k, E, S, int(half)))
+
+
+class Timer:
+    """A timing event of the library (no system-scope fence); .handle is the hipEvent_t."""
+
+    def __init__(self):
+        h = C.c_void_p(0)
+        _check("scr_timer_create", load().scr_timer_create(C.byref(h)))
+        self.handle = int(h.value)
+
+    def record(self, stream: int):
+        _check("scr_timer_record", load().scr_timer_record(self.handle, stream))
+
+    def elapsed_ms(self, stop: "Timer") -> float:
+        ms = C.c_float(0.0)
+        _check("scr_timer_elapsed_ms", load().scr_timer_elapsed_ms(self.handle, stop.handle, C.byref(ms)))
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            if self.handle and _lib is not None:
+                _lib.scr_timer_destroy(self.handle)
+        except Exception:
+            pass
 
 
 def version() -> str:

@@ -54,3 +54,28 @@ extern "C" int scr_record_layout_of(int wdtype, int H, int I, scr_record_layout*
   scr::set_error("record_layout: unknown wdtype %d", wdtype);
   return SCR_ENOTSUP;
 }
+
+extern "C" int scr_timer_create(hipEvent_t* ev) {
+  SCR_CHECK_ARG(ev != nullptr, "timer_create: null pointer");
+  SCR_CHECK_HIP(hipEventCreateWithFlags(ev, hipEventDisableSystemFence));
+  return SCR_OK;
+}
+
+extern "C" int scr_timer_record(hipEvent_t ev, hipStream_t stream) {
+  SCR_CHECK_ARG(ev != nullptr, "timer_record: null event");
+  SCR_CHECK_HIP(hipEventRecord(ev, stream));
+  return SCR_OK;
+}
+
+extern "C" int scr_timer_elapsed_ms(hipEvent_t start, hipEvent_t stop, float* ms) {
+  SCR_CHECK_ARG(start && stop && ms, "timer_elapsed: null argument");
+  SCR_CHECK_HIP(hipEventSynchronize(stop));
+  SCR_CHECK_HIP(hipEventElapsedTime(ms, start, stop));
+  return SCR_OK;
+}
+
+extern "C" int scr_timer_destroy(hipEvent_t ev) {
+  SCR_CHECK_ARG(ev != nullptr, "timer_destroy: null event");
+  SCR_CHECK_HIP(hipEventDestroy(ev));
+  return SCR_OK;
+}

@@ -297,10 +297,10 @@ static int launch_gemms(const GemmArgs& a, int max_active, hipEvent_t* marks, hi
   dim3 gu(a.I / kNTile, max_active), dn(a.H / kNTile, max_active);
   hipLaunchKernelGGL((gateup_kernel<WDT, MT>), gu, dim3(kGemmThreads), 0, s, a);
   SCR_CHECK_LAUNCH();
-  if (marks) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
+  if (marks && marks[2]) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
   hipLaunchKernelGGL((down_kernel<WDT, MT>), dn, dim3(kGemmThreads), 0, s, a);
   SCR_CHECK_LAUNCH();
-  if (marks) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
+  if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
   return SCR_OK;
 }
 
@@ -377,13 +377,13 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   a.B = cfg.block_m;
   a.h_rows = wl.h_rows;
 
-  if (marks) SCR_CHECK_HIP(hipEventRecord(marks[0], stream));
+  if (marks && marks[0]) SCR_CHECK_HIP(hipEventRecord(marks[0], stream));
   int pgrid = (R + 255) / 256;
   if (pgrid > 256) pgrid = 256;
   hipLaunchKernelGGL(scr::prologue_kernel, dim3(pgrid), dim3(256), 0, stream, a.flags, R, view->input_scale, E,
                      a_scale_out);
   SCR_CHECK_LAUNCH();
-  if (marks) SCR_CHECK_HIP(hipEventRecord(marks[1], stream));
+  if (marks && marks[1]) SCR_CHECK_HIP(hipEventRecord(marks[1], stream));
 
   // the grid covers at most min(R, E_layer) active buckets: a layer size
   const int max_active = R < E ? R : E;
@@ -404,6 +404,6 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   else
     hipLaunchKernelGGL(scr::combine_kernel<false>, dim3(cgrid), dim3(256), 0, stream, a.o, a.flags, T, k, H, y);
   SCR_CHECK_LAUNCH();
-  if (marks) SCR_CHECK_HIP(hipEventRecord(marks[4], stream));
+  if (marks && marks[4]) SCR_CHECK_HIP(hipEventRecord(marks[4], stream));
   return SCR_OK;
 }

@@ -24,6 +24,11 @@ def _stream(s=None) -> int:
     return s.cuda_stream
 
 
+def record_timer(t: L.Timer, stream=None):
+    """Records a library timing event on the stream (default: torch's current stream)."""
+    t.record(_stream(stream))
+
+
 def _i32(n, fill=None):
     t = torch.empty(max(int(n), 1), dtype=torch.int32, device=_DEV)
     if fill is not None:
@@ -264,3 +269,73 @@ def stream_layer(pool: HostPool, layer: int, logits, x, input_scale, layer_buf: 
     view = make_view(layer, E, k, H, I, wdtype, E, layer_buf.row_table, input_scale)
     buf.cfg_used = forward(buf, view, x, stream)
     return buf
+
+
+# ------------------------------------------------------------- staging
+
+class StagedPrefill:
+    """Prefill staging over consecutive layers.
+
+    Two device buffers, each the size of a whole layer, alternate by layer;
+    the non-resident map of every layer is read back once (scr_stage_plan,
+    the step's one host sync) and turned into runs; layer i+1's runs are
+    copied by DMA on a side stream while layer i computes, ordered with events
+    (the copy into a buffer waits for the layer that last read it).  Each
+    layer then runs route, align over its experts and the grouped GEMM on a
+    view whose rows point into the bank (resident) or the staging buffer.
+    """
+
+    def __init__(self, bank: Bank, pool: HostPool, max_runs: int | None = None):
+        self.bank, self.pool = bank, pool
+        E, rec = bank.E, bank.rec
+        self.staging = [torch.empty(E * rec, dtype=torch.uint8, device=_DEV) for _ in range(2)]
+        self.tables = [torch.zeros(E, dtype=torch.int64, device=_DEV) for _ in range(2)]
+        self.side = torch.cuda.Stream()          # default priority
+        self.max_runs = max_runs or bank.L * E
+        self.runs = (L.Run * self.max_runs)()
+        self.host_map = torch.empty(bank.L * E, dtype=torch.int32, pin_memory=True)
+        self.n_runs = 0
+
+    def plan(self, layer_begin: int, n_layers: int, stream=None) -> int:
+        self.n_runs = L.stage_plan(self.bank.desc, self.pool.desc, layer_begin, n_layers, self.host_map,
+                                   self.runs, self.max_runs, _stream(stream))
+        return self.n_runs
+
+    def staged_bytes(self, layer: int) -> int:
+        return sum(r.count for r in self.runs[:self.n_runs] if r.layer == layer) * self.bank.rec
+
+    def run(self, layers, logits, x, input_scale, bufs, timers=None, stream=None):
+        """Runs the layers in order; logits[i] is layer i's [T, E] router input,
+        bufs[i] its LayerBuffers.  timers (optional) maps layer index to a
+        LayerTimers-like dict of 5 library timers passed as forward marks."""
+        comp = stream if stream is not None else torch.cuda.current_stream()
+        n = len(layers)
+        staged = [torch.cuda.Event() for _ in range(n)]
+        done = [torch.cuda.Event() for _ in range(n)]
+        for e in staged + done:              # creates the events
+            e.record(comp)
+        E, k, H, I = self.bank.E, bufs[0].k, bufs[0].H, bufs[0].I
+        side = self.side.cuda_stream
+
+        def stage(i):
+            wait = done[i - 2].cuda_event if i >= 2 else None
+            L.stage_rows_async(self.pool.desc, self.runs, self.n_runs, layers[i], self.staging[i % 2], side,
+                               wait, staged[i].cuda_event)
+
+        stage(0)
+        for i, layer in enumerate(layers):
+            if i + 1 < n:
+                stage(i + 1)
+            comp.wait_event(staged[i])
+            b = bufs[i]
+            s = comp.cuda_stream
+            L.route(logits[i], b.T, E, k, b["topk_ids"], b["topk_w"], s)
+            L.align_blocks(b["topk_ids"], b.R, None, 0, E, b.cfg.block_m, b["sorted_routes"], b["block_bucket"],
+                           b["n_post_pad"], b["active_buckets"], b["active_block_begin"], b["n_active"],
+                           b["align_ws"], b["align_ws"].numel(), s)
+            L.fill_staged_rows(self.bank.desc, layer, self.staging[i % 2], self.tables[i % 2], s)
+            view = make_view(layer, E, k, H, I, self.bank.wdtype, E, self.tables[i % 2], input_scale)
+            marks = None if timers is None else [t.handle for t in timers[i]]
+            b.cfg_used = forward(b, view, x, stream=comp, marks=marks)
+            done[i].record(comp)
+        return bufs

@@ -1,0 +1,86 @@
+"""GPU parity of prefill staging: staged layers equal the whole-layer stream
+bit for bit, resident bank rows stay untouched, staged rows equal the host
+records, and sampled tokens match the oracle (NVFP4)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from helpers import ExpertSource, fill_pool, flush, rel_max_err
+from oracle import moe_layer_tokens, route_topk_softmax
+from oracle.mlp import bf16_bits_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _staging_case(T, n_layers, E, k, H, I, n_res, seed, S):
+    import slot_cache_routed_amd._lib as L
+    import slot_cache_routed_amd.layer as LY
+    lay = LY.record_layout(L.SCR_W_NVFP4, H, I)
+    src = ExpertSource(seed, H, I, "nvfp4")
+    flush(f"staging case T={T} layers={n_layers} E={E} H={H} I={I} resident={n_res}")
+    pool = LY.HostPool(n_layers, E, lay.record_bytes, n_layers * E)
+    fill_pool(pool, src, lay, range(n_layers * E))
+    bank = LY.Bank(S, n_layers, E, L.SCR_W_NVFP4, lay.record_bytes)
+    # make each layer's resident set resident through the library's own admission
+    s = torch.cuda.current_stream().cuda_stream
+    for layer in range(n_layers):
+        res = W.resident_experts(seed, layer, E, n_res)
+        d = _dev(res)
+        ms = torch.zeros(n_res, dtype=torch.int32, device="cuda")
+        mk = torch.zeros(n_res, dtype=torch.int32, device="cuda")
+        nm = torch.zeros(1, dtype=torch.int32, device="cuda")
+        L.ensure_slots(bank.desc, layer, d, 0, n_res, 0, ms, mk, nm, s)
+        L.copy_misses(bank.desc, pool.desc, ms, mk, nm, n_res, s)
+    torch.cuda.synchronize()
+    return L, LY, lay, src, pool, bank
+
+
+@pytest.mark.parametrize("T,n_layers,E,k,H,I,n_res,S", [
+    (256, 3, 64, 6, 512, 256, 24, 100),
+    (4096, 2, 512, 10, 2048, 512, 193, 1650),
+])
+def test_staged_layers_equal_stream_and_oracle(T, n_layers, E, k, H, I, n_res, S):
+    seed = 5
+    L, LY, lay, src, pool, bank = _staging_case(T, n_layers, E, k, H, I, n_res, seed, S)
+    rows_before = bank.rows.clone()
+    sp = LY.StagedPrefill(bank, pool)
+    n_runs = sp.plan(0, n_layers)
+    for layer in range(n_layers):
+        assert sp.staged_bytes(layer) == (E - n_res) * lay.record_bytes
+    logits = [_dev(W.logits_normal(seed, layer, T, E)) for layer in range(n_layers)]
+    xb = W.f32_to_bf16_bits(W.activations_normal(seed, T, H))
+    x = _dev(xb.view(np.int16))
+    sc = _dev(np.ones(E, np.float32))
+    bufs = [LY.LayerBuffers(T, E, k, H, I, E, L.SCR_W_NVFP4) for _ in range(n_layers)]
+    sp.run(list(range(n_layers)), logits, x, sc, bufs)
+    torch.cuda.synchronize()
+    assert torch.equal(bank.rows, rows_before), "resident rows untouched"
+    # the last staged layer's non-resident rows equal the host records
+    last = n_layers - 1
+    snap = bank.snapshot()
+    buf = sp.staging[last % 2]
+    for e in range(E):
+        if snap["key_to_slot"][last * E + e] < 0:
+            got = buf[e * lay.record_bytes:(e + 1) * lay.record_bytes]
+            assert torch.equal(got.cpu(), pool.key_record(last * E + e)), e
+            break
+    # whole-layer stream partner, same kernel and tiles
+    lb = LY.LayerStreamBuffer(E, lay.record_bytes)
+    for layer in range(n_layers):
+        st = LY.stream_layer(pool, layer, logits[layer], x, sc, lb, L.SCR_W_NVFP4, shape=(k, H, I))
+        torch.cuda.synchronize()
+        assert torch.equal(bufs[layer]["y"], st["y"]), f"layer {layer}: staged equals stream bit for bit"
+        # sampled tokens against the oracle
+        lg = W.logits_normal(seed, layer, T, E)
+        ids, w = route_topk_softmax(lg, k)
+        toks = list(range(0, T, max(1, T // 12)))[:12]
+        y_ref = moe_layer_tokens(bf16_bits_to_f64(xb), ids, w, lambda e: src.f64(layer * E + e), toks)
+        y = bufs[layer]["y"].cpu().numpy()[toks]
+        err = rel_max_err(y, y_ref)
+        flush(f"layer {layer}: sampled rel max err {err:.3e}")
+        assert err <= 5e-2
