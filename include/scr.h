@@ -76,13 +76,23 @@ extern "C" {
 /* ------------------------------------------------------- expert record
  * One expert's weights form one contiguous record, identical in the pinned
  * host pool, in a bank slot and in a staging buffer, so a miss copy is a
- * single contiguous byte range.  Layout (offsets from scr_record_layout):
+ * single contiguous byte range.  Logical tensors (offsets from
+ * scr_record_layout_of):
  *   SCR_W_BF16 : w13 bf16 [2I][H] (rows 0..I-1 gate, I..2I-1 up), w2 bf16 [H][I]
- *   SCR_W_NVFP4: w13_q u8 [2I][H/2]  two e2m1 codes per byte, low nibble = even column
- *                w13_s u8 [2I][H/16] e4m3 (OCP E4M3FN) scale per 16 input columns
- *                w2_q  u8 [H][I/2], w2_s u8 [H][I/16]
- *                g13 f32, g2 f32     global scales; record padded to 256 bytes
+ *   SCR_W_NVFP4: w13 e2m1 codes [2I][H], w13 e4m3 (OCP E4M3FN) scales [2I][H/16]
+ *                (one per 16 consecutive input columns of a row), w2 codes [H][I],
+ *                w2 scales [H][I/16], then g13 f32, g2 f32 (global scales);
+ *                record padded to 256 bytes.
  * Decoded weight = e2m1(code) * e4m3(scale) * global.
+ * Storage is tile-major so each load of the GEMM is one contiguous range: a
+ * tensor of N rows and K columns is a sequence of tile-blocks (t, kb), t over
+ * the N/16 row tiles, kb over the K/128 column blocks (t-major).  Inside a
+ * tile-block, with r = row % 16:
+ *   bf16   4096 B: element (r, 32 s + 8 g + e) at byte 1024 s + 16 (16 g + r) + 2 e
+ *   codes  1024 B: code (r, 32 g + j) in byte 16 (16 g + r) + j / 2, low nibble = even j
+ *   scales  128 B: scale (r, 2 g + h) (the 16-column block 8 kb + 2 g + h) at byte
+ *                  2 (16 g + r) + h
+ * H and I must be multiples of 128.
  */
 typedef struct scr_record_layout {
   uint64_t w13_off, w13_scale_off, w2_off, w2_scale_off, g13_off, g2_off;
@@ -242,7 +252,8 @@ int scr_align_blocks(const int32_t* ids, int n, const int32_t* id_to_bucket, int
 /* tile config [P1 Solution fourth bullet, Tests: tiles sized by the routed
  * layer's experts, never by the slot count]. */
 int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_cfg* cfg);
-/* workspace of scr_grouped_moe_forward: h [cap][I] bf16 + per-route rows [T*k][H] f32 */
+/* workspace of scr_grouped_moe_forward: h [cap][I] bf16 + per-route rows [T*k][H]
+ * (fp32 for bf16 weights, bf16 for NVFP4 weights) + per-route flags */
 int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cfg* cfg,
                       size_t* bytes);
 
@@ -266,7 +277,7 @@ int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cf
  *               the prologue and after the prologue, gate/up, down and
  *               combine kernels (per-kernel timing on the launching stream);
  *               NULL entries are skipped
- * H % 64 == 0, I % 64 == 0 (NVFP4 as well), 64 <= H, I <= 16384. */
+ * H % 128 == 0, I % 128 == 0, 128 <= H, I <= 16384 (the GEMM's K block is 128). */
 int scr_grouped_moe_forward(const scr_routed_experts* view, const void* x, int T,
                             const float* topk_w, const int32_t* sorted_routes,
                             const int32_t* active_buckets, const int32_t* active_block_begin,

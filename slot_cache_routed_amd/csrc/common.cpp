@@ -29,7 +29,8 @@ extern "C" int scr_demand_capacity_ok(int T, int k, int E, int S, int half) {
 
 extern "C" int scr_record_layout_of(int wdtype, int H, int I, scr_record_layout* out) {
   SCR_CHECK_ARG(out != nullptr, "record_layout: out is null");
-  SCR_CHECK_ARG(H > 0 && I > 0, "record_layout: H and I must be positive");
+  SCR_CHECK_ARG(H >= 128 && I >= 128 && H % 128 == 0 && I % 128 == 0,
+                "record_layout: H and I must be positive multiples of 128 (tile-major records)");
   memset(out, 0, sizeof(*out));
   const uint64_t h = (uint64_t)H, i = (uint64_t)I;
   if (wdtype == SCR_W_BF16) {
@@ -41,7 +42,6 @@ extern "C" int scr_record_layout_of(int wdtype, int H, int I, scr_record_layout*
     return SCR_OK;
   }
   if (wdtype == SCR_W_NVFP4) {
-    SCR_CHECK_ARG(H % 32 == 0 && I % 32 == 0, "record_layout: NVFP4 needs H, I multiples of 32");
     out->w13_off = 0;
     out->w13_scale_off = out->w13_off + 2 * i * h / 2;
     out->w2_off = out->w13_scale_off + 2 * i * h / 16;

@@ -42,11 +42,36 @@ def record_layout(wdtype: int, H: int, I: int) -> L.RecordLayout:
     return L.record_layout_of(wdtype, H, I)
 
 
+# Tile-major record layout (include/scr.h): a weight tensor [N rows][K cols] is
+# stored as tile-blocks (t, kb) of 16 rows x 128 columns, t-major then kb, each
+# in the order the GEMM's lanes load it.  These are byte permutations only.
+
+def tile_bf16(w_bits: np.ndarray) -> np.ndarray:
+    """bf16 [N][K] -> tile-blocks [t][kb][step s][group g][row r][8 elements], k = 128 kb + 32 s + 8 g + e."""
+    N, K = w_bits.shape
+    w = np.ascontiguousarray(w_bits, np.uint16).reshape(N // 16, 16, K // 128, 4, 4, 8)
+    return np.ascontiguousarray(w.transpose(0, 2, 3, 4, 1, 5)).view(np.uint8).reshape(-1)
+
+
+def tile_fp4_codes(q: np.ndarray) -> np.ndarray:
+    """packed e2m1 [N][K/2] -> [t][kb][group g][row r][16 bytes], codes 128 kb + 32 g + j (byte j/2)."""
+    N, Kh = q.shape
+    w = np.ascontiguousarray(q, np.uint8).reshape(N // 16, 16, Kh // 64, 4, 16)
+    return np.ascontiguousarray(w.transpose(0, 2, 3, 1, 4)).reshape(-1)
+
+
+def tile_fp4_scales(sc: np.ndarray) -> np.ndarray:
+    """e4m3 scales [N][K/16] -> [t][kb][group g][row r][2], scale 8 kb + 2 g + h."""
+    N, Ks = sc.shape
+    w = np.ascontiguousarray(sc, np.uint8).reshape(N // 16, 16, Ks // 8, 4, 2)
+    return np.ascontiguousarray(w.transpose(0, 2, 3, 1, 4)).reshape(-1)
+
+
 def pack_record_bf16(lay: L.RecordLayout, w13_bits: np.ndarray, w2_bits: np.ndarray) -> np.ndarray:
     """Lays out one bf16 expert record (uint8 [record_bytes])."""
     rec = np.zeros(lay.record_bytes, np.uint8)
-    a = np.ascontiguousarray(w13_bits, np.uint16).view(np.uint8).reshape(-1)
-    b = np.ascontiguousarray(w2_bits, np.uint16).view(np.uint8).reshape(-1)
+    a = tile_bf16(w13_bits)
+    b = tile_bf16(w2_bits)
     rec[lay.w13_off:lay.w13_off + a.size] = a
     rec[lay.w2_off:lay.w2_off + b.size] = b
     return rec
@@ -55,9 +80,9 @@ def pack_record_bf16(lay: L.RecordLayout, w13_bits: np.ndarray, w2_bits: np.ndar
 def pack_record_nvfp4(lay: L.RecordLayout, d: dict) -> np.ndarray:
     """Lays out one NVFP4 expert record from codes, scale codes and global scales."""
     rec = np.zeros(lay.record_bytes, np.uint8)
-    for key, off in (("w13_q", lay.w13_off), ("w13_s", lay.w13_scale_off), ("w2_q", lay.w2_off),
-                     ("w2_s", lay.w2_scale_off)):
-        a = np.ascontiguousarray(d[key], np.uint8).reshape(-1)
+    for key, off, fn in (("w13_q", lay.w13_off, tile_fp4_codes), ("w13_s", lay.w13_scale_off, tile_fp4_scales),
+                         ("w2_q", lay.w2_off, tile_fp4_codes), ("w2_s", lay.w2_scale_off, tile_fp4_scales)):
+        a = fn(d[key])
         rec[off:off + a.size] = a
     rec[lay.g13_off:lay.g13_off + 4] = np.array([d["g13"]], np.float32).view(np.uint8)
     rec[lay.g2_off:lay.g2_off + 4] = np.array([d["g2"]], np.float32).view(np.uint8)

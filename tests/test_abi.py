@@ -93,7 +93,7 @@ def test_bank_and_view_validation(lib):
     pool = L.HostPoolDesc(2, 8, 1, 1, 32)
     with pytest.raises(L.ScrError):
         L.copy_misses(bank, pool, 1, 1, 1, 4, None)                 # record sizes differ
-    view = L.RoutedExperts(0, 8, 2, 100, 512, 0, 8, 1, 1)            # H not a multiple of 64
+    view = L.RoutedExperts(0, 8, 2, 192, 512, 0, 8, 1, 1)            # H not a multiple of 128
     with pytest.raises(L.ScrError):
         L.grouped_moe_forward(view, 1, 4, 1, 1, 1, 1, 1, 1, 0, 1, 1 << 30, None, None)
     view = L.RoutedExperts(0, 8, 2, 256, 128, 0, 8, 1, 1)

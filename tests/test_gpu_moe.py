@@ -162,7 +162,7 @@ def test_layer_view_one_layer_cache_three_per_query():
     assert torch.equal(d["y"], st["y"])
 
 
-@pytest.mark.parametrize("T,E,k,H,I", [(64, 16, 4, 256, 128), (200, 32, 6, 512, 256), (37, 8, 3, 128, 64)])
+@pytest.mark.parametrize("T,E,k,H,I", [(64, 16, 4, 256, 128), (200, 32, 6, 512, 256), (37, 8, 3, 256, 128)])
 def test_nvfp4_layer_vs_oracle_and_stream(T, E, k, H, I):
     s = _setup(f"fp4_{T}_{E}", S=2 * E, W_=8, wdtype="nvfp4", T=T, E=E, k=k, H=H, I=I, NL=2)
     bank = _bank_for(s)
@@ -179,7 +179,7 @@ def test_nvfp4_layer_vs_oracle_and_stream(T, E, k, H, I):
 
 def test_bf16_ragged_shapes_vs_oracle():
     # many tiles with a ragged tail of rows per bucket
-    s = _setup("ragged", S=100, W_=16, wdtype="bf16", T=333, E=24, k=5, H=384, I=192, NL=3)
+    s = _setup("ragged", S=100, W_=16, wdtype="bf16", T=333, E=24, k=5, H=384, I=256, NL=3)
     bank = _bank_for(s)
     sc = np.ones(s["E"], np.float32)
     d = _run_demand(s, bank, sc)
