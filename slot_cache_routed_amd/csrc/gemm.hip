@@ -28,6 +28,15 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGemmThreads = 256;  // 4 waves per workgroup
 
+// Load through a global-address-space pointer.  Pointers read from tables
+// (bucket_rows) are generic; a generic load compiles to a FLAT instruction,
+// which also counts on the LDS counter, so every wait for an LDS read would
+// wait for the in-flight weight stream as well.
+template <typename T>
+__device__ __forceinline__ T ldg(const void* p) {
+  return *(const __attribute__((address_space(1))) T*)(p);
+}
+
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -135,7 +144,7 @@ struct BFrag<SCR_W_BF16, NT> {
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int st = 0; st < 4; ++st)
-        raw[t][st] = *reinterpret_cast<const u32x4*>(tile[t] + (size_t)kb * 4096 + st * 1024 + lane * 16);
+        raw[t][st] = ldg<u32x4>(tile[t] + (size_t)kb * 4096 + st * 1024 + lane * 16);
   }
   __device__ __forceinline__ bf16x8 get(int t, int st) const { return __builtin_bit_cast(bf16x8, raw[t][st]); }
 };
@@ -147,8 +156,8 @@ struct BFrag<SCR_W_NVFP4, NT> {
   __device__ __forceinline__ void load(const uint8_t* const* tile, const uint8_t* const* stile, int kb, int lane) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      codes[t] = *reinterpret_cast<const u32x4*>(tile[t] + (size_t)kb * 1024 + lane * 16);
-      sc[t] = *reinterpret_cast<const unsigned short*>(stile[t] + (size_t)kb * 128 + lane * 2);
+      codes[t] = ldg<u32x4>(tile[t] + (size_t)kb * 1024 + lane * 16);
+      sc[t] = ldg<unsigned short>(stile[t] + (size_t)kb * 128 + lane * 2);
     }
   }
   __device__ __forceinline__ bf16x8 get(int t, int st) const {
@@ -196,7 +205,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
   };
   auto load_a = [&](AStage& st, int kb) {
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) st.v[u] = *reinterpret_cast<const u32x4*>(asrc[u] + kb * kKB);
+    for (int u = 0; u < kPerThread; ++u) st.v[u] = ldg<u32x4>(asrc[u] + kb * kKB);
   };
   auto store_a = [&](const AStage& st, int buf) {
     bf16* base = &As[buf][0][0];
@@ -377,6 +386,231 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
   }
 }
 
+// ------------------------------------------------- expert-persistent GEMM
+//
+// For chunks with many rows per expert: one workgroup of 8 waves owns one
+// active bucket and walks all of its N chunks, so the weight stream of the
+// expert never restarts (the prefetch ring runs across chunk boundaries) and
+// no other workgroup re-reads the bucket's activation rows for it.  A chunk
+// is 256 weight rows: each wave owns NTW = 2 tiles of 16 rows (gate/up: one
+// gate tile and the matching up tile, 16 h columns; down: 32 output columns).
+// Down keeps the bucket's whole h block (K = I <= 512) resident in LDS for
+// all chunks; gate/up stages x blocks of 128 columns double-buffered.
+constexpr int kExpWaves = 8;
+constexpr int kExpThreads = 64 * kExpWaves;
+constexpr int kNTW = 2;
+constexpr int kResMaxKB = 4;  // resident activation blocks (K <= 512)
+
+template <int WDT, int MT, bool GATEUP, bool ARES>
+struct ExpSmem {
+  static constexpr int kBufs = ARES ? kResMaxKB : 2;
+  bf16 As[kBufs][MT * 16 + 1][kAStride];  // the extra row takes the stores of unused staging lanes
+  int src_row[MT * 16];
+};
+
+template <int WDT, int MT, bool GATEUP, bool ARES, int MTC>
+__device__ __forceinline__ void expert_pass(const GemmArgs& a, ExpSmem<WDT, MT, GATEUP, ARES>& sm, int m0,
+                                            const uint8_t* const* tile0, const uint8_t* const* stile0,
+                                            float gs, int nkb, int nchunks) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const bf16* abase = GATEUP ? a.x : a.h;
+  constexpr int kRowChunks = kKB / 8;
+  constexpr int kChunks = MTC * 16 * kRowChunks;
+  constexpr int kPerThread = (kChunks + kExpThreads - 1) / kExpThreads;
+  constexpr int CT = GATEUP ? kExpWaves * kNTW / 2 : kExpWaves * kNTW;  // row tiles per chunk and tensor half
+  constexpr size_t tile_bytes = WDT == SCR_W_NVFP4 ? 1024 : 4096;
+
+  // staging addresses of this thread (fixed for the pass)
+  const bf16* asrc[kPerThread];
+  bool avalid[kPerThread];
+  int adst[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; ++u) {
+    const int ci = u * kExpThreads + tid;
+    const bool in = ci < kChunks;
+    const int r = in ? ci / kRowChunks : 0, ch = ci % kRowChunks;
+    const int off = sm.src_row[r];
+    avalid[u] = in && off >= 0;
+    asrc[u] = abase + (off >= 0 ? off : 0) + ch * 8;
+    adst[u] = (in ? r : MT * 16) * kAStride + ch * 8;
+  }
+  struct AStage {
+    u32x4 v[kPerThread];
+  };
+  auto load_a = [&](AStage& st, int kb) {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) st.v[u] = ldg<u32x4>(asrc[u] + kb * kKB);
+  };
+  auto store_a = [&](const AStage& st, int buf) {
+    bf16* base = &sm.As[buf][0][0];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(base + adst[u]) = avalid[u] ? st.v[u] : z;
+    }
+  };
+  // weights of flat step s = chunk * nkb + kb
+  auto load_b = [&](BFrag<WDT, kNTW>& f, int s) {
+    const int ch = s / nkb, kb = s - ch * nkb;
+    const size_t blk = (size_t)ch * CT * nkb + kb;
+    const uint8_t* tp[kNTW];
+    const uint8_t* sp[kNTW];
+#pragma unroll
+    for (int t = 0; t < kNTW; ++t) {
+      tp[t] = tile0[t] + blk * tile_bytes;
+      sp[t] = stile0[t] + blk * 128;
+    }
+    f.load(tp, sp, 0, lane);
+  };
+
+  f32x4 acc[MTC][kNTW];
+  auto zero_acc = [&]() {  // (defined before use below)
+#pragma unroll
+    for (int mt = 0; mt < MTC; ++mt)
+#pragma unroll
+      for (int t = 0; t < kNTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto compute = [&](const BFrag<WDT, kNTW>& bc, int buf) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8 bf[kNTW];
+#pragma unroll
+      for (int t = 0; t < kNTW; ++t) bf[t] = bc.get(t, st);
+#pragma unroll
+      for (int mt = 0; mt < MTC; ++mt) {
+        const bf16x8 av =
+            *reinterpret_cast<const bf16x8*>(&sm.As[buf][mt * 16 + col][kcol<WDT>(grp, st)]);
+#pragma unroll
+        for (int t = 0; t < kNTW; ++t) acc[mt][t] = mfma16(av, bf[t], acc[mt][t]);
+      }
+    }
+  };
+  auto epilogue = [&](int ch) {
+#pragma unroll
+    for (int mt = 0; mt < MTC; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pos = m0 + mt * 16 + grp * 4 + i;
+        if (GATEUP) {
+          constexpr int HW = 8 * kNTW;  // h columns per wave
+#pragma unroll
+          for (int t = 0; t < kNTW / 2; ++t) {
+            const int hc = ch * (HW * kExpWaves) + wave * HW + 16 * t + col;
+            const float hv = silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + kNTW / 2][i]);
+            a.h[(size_t)pos * a.I + hc] = static_cast<bf16>(hv);
+          }
+        } else {
+          const int r = a.sorted_routes[pos];
+          if (r >= 0 && r < a.R) {
+            const float w = a.topk_w[r];
+            typedef typename RowT<WDT>::type OT;
+            OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + ch * (16 * kNTW * kExpWaves) + wave * 16 * kNTW + col;
+#pragma unroll
+            for (int t = 0; t < kNTW; ++t) orow[16 * t] = static_cast<OT>(w * (gs * acc[mt][t][i]));
+            if (ch == 0 && wave == 0 && col == 0) a.flags[r] = 1;
+          }
+        }
+      }
+    }
+  };
+
+  const int S = nchunks * nkb;  // flat steps s = chunk * nkb + kb
+  constexpr int D = WDT == SCR_W_NVFP4 ? 4 : 2;  // the launcher guarantees nkb % D == 0
+  BFrag<WDT, kNTW> ring[D];
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i) load_b(ring[i], min(i, S - 1));
+  AStage A0;
+  if (ARES) {
+    // the whole K of the bucket's rows, once for all chunks (two blocks in flight)
+    AStage A1;
+    for (int b = 0; b < nkb; b += 2) {
+      load_a(A0, b);
+      if (b + 1 < nkb) load_a(A1, b + 1);
+      store_a(A0, b);
+      if (b + 1 < nkb) store_a(A1, b + 1);
+    }
+  } else {
+    load_a(A0, 0);
+    store_a(A0, 0);
+  }
+  __syncthreads();
+  auto step = [&](int s, int kb, const BFrag<WDT, kNTW>& bc, BFrag<WDT, kNTW>& bl) {
+    if (!ARES) load_a(A0, (s + 1) % nkb);  // next step's activation block
+    load_b(bl, min(s + D - 1, S - 1));
+    compute(bc, ARES ? kb : (s & 1));
+    if (!ARES) {
+      store_a(A0, (s + 1) & 1);
+      __syncthreads();
+    }
+  };
+  for (int ch = 0; ch < nchunks; ++ch) {
+    zero_acc();
+    for (int kb0 = 0; kb0 < nkb; kb0 += D) {
+#pragma unroll
+      for (int i = 0; i < D; ++i) step(ch * nkb + kb0 + i, kb0 + i, ring[i], ring[(i + D - 1) % D]);
+    }
+    epilogue(ch);
+  }
+}
+
+template <int WDT, int MT, bool GATEUP, bool ARES>
+__global__ __launch_bounds__(kExpThreads) void moe_expert_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) ExpSmem<WDT, MT, GATEUP, ARES> sm;
+  // XCD-aware order: bucket j runs on XCD j mod 8
+  const int bid = blockIdx.x, j = 8 * (bid >> 3) + (bid & 7);
+  if (j >= *a.n_active) return;
+  const int b = a.active_buckets[j];
+  const int p0 = a.active_block_begin[j] * a.B, p1 = a.active_block_begin[j + 1] * a.B;
+  if (p1 > a.h_rows || p0 >= p1) return;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int K = GATEUP ? a.H : a.I;
+  const int nkb = K / kKB;
+  const int nchunks = GATEUP ? a.I / (8 * kNTW * kExpWaves) : a.H / (16 * kNTW * kExpWaves);
+  const uint8_t* rec = static_cast<const uint8_t*>(a.bucket_rows[b]);
+  constexpr size_t tile_bytes = WDT == SCR_W_NVFP4 ? 1024 : 4096;
+  // tile-block (t, 0) of this wave's tiles in chunk 0
+  const uint8_t* tile0[kNTW];
+  const uint8_t* stile0[kNTW];
+#pragma unroll
+  for (int t = 0; t < kNTW; ++t) {
+    const int row0 = GATEUP ? (t < kNTW / 2 ? 0 : a.I) + wave * 8 * kNTW + 16 * (t % (kNTW / 2))
+                            : wave * 16 * kNTW + 16 * t;
+    const size_t tb = (size_t)(row0 / 16) * nkb;
+    tile0[t] = rec + (GATEUP ? a.lay.w13_off : a.lay.w2_off) + tb * tile_bytes;
+    stile0[t] = rec + (GATEUP ? a.lay.w13_scale_off : a.lay.w2_scale_off) + tb * 128;
+  }
+  const float gs = WDT == SCR_W_NVFP4
+                       ? *reinterpret_cast<const float*>(rec + (GATEUP ? a.lay.g13_off : a.lay.g2_off))
+                       : 1.0f;
+  for (int m0 = p0; m0 < p1; m0 += MT * 16) {
+    const int rows = min(MT * 16, p1 - m0);
+    for (int i = tid; i < MT * 16; i += kExpThreads) {
+      int off = -1;
+      if (i < rows) {
+        if (GATEUP) {
+          const int r = a.sorted_routes[m0 + i];
+          if (r >= 0 && r < a.R) off = (r / a.k) * K;
+        } else {
+          off = (m0 + i) * K;
+        }
+      }
+      sm.src_row[i] = off;
+    }
+    __syncthreads();
+    switch (rows / 16) {
+      case 1: expert_pass<WDT, MT, GATEUP, ARES, 1>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
+      case 2: if constexpr (MT >= 2) expert_pass<WDT, MT, GATEUP, ARES, 2>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
+      case 3: if constexpr (MT >= 3) expert_pass<WDT, MT, GATEUP, ARES, 3>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
+      case 4: if constexpr (MT >= 4) expert_pass<WDT, MT, GATEUP, ARES, 4>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
+      case 5: if constexpr (MT >= 5) expert_pass<WDT, MT, GATEUP, ARES, 5>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
+      case 6: if constexpr (MT >= 6) expert_pass<WDT, MT, GATEUP, ARES, 6>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
+      default: break;
+    }
+    __syncthreads();  // src_row and As are reused by the next pass
+  }
+}
+
 // clears the per-route written flags and reports the layer's activation scale
 __global__ __launch_bounds__(256) void prologue_kernel(int32_t* __restrict__ flags, int R,
                                                        const float* __restrict__ input_scale, int E,
@@ -468,6 +702,32 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
   w.flags_off = align256(w.o_off + (size_t)R * H * row_bytes);
   w.bytes = align256(w.flags_off + (size_t)R * sizeof(int32_t));
   return w;
+}
+
+template <int WDT, int MT>
+static bool expert_gemms_fit(const GemmArgs& a) {
+  constexpr int D = WDT == SCR_W_NVFP4 ? 4 : 2;
+  return (a.H / kKB) % D == 0 && (a.I / kKB) % D == 0 && a.I % (8 * kNTW * kExpWaves) == 0 &&
+         a.H % (16 * kNTW * kExpWaves) == 0;
+}
+
+// many rows per expert: gate/up as (bucket, N tile) workgroups (measured
+// faster for the long K = H loop), down as one expert-persistent workgroup per
+// bucket with its h rows resident in LDS
+template <int WDT, int MT>
+static int launch_expert_gemms(const GemmArgs& a, int max_active, hipEvent_t* marks, hipStream_t s) {
+  const int grid = 8 * ((max_active + 7) / 8);
+  const int ntx_gu = (a.I + 4 * 8 * 2 - 1) / (4 * 8 * 2);
+  hipLaunchKernelGGL((moe_gemm_kernel<WDT, MT, 2, true>), dim3(grid * ntx_gu), dim3(kGemmThreads), 0, s, a, ntx_gu);
+  SCR_CHECK_LAUNCH();
+  if (marks && marks[2]) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
+  if (a.I / kKB <= kResMaxKB)
+    hipLaunchKernelGGL((moe_expert_kernel<WDT, MT, false, true>), dim3(grid), dim3(kExpThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((moe_expert_kernel<WDT, MT, false, false>), dim3(grid), dim3(kExpThreads), 0, s, a);
+  SCR_CHECK_LAUNCH();
+  if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
+  return SCR_OK;
 }
 
 template <int WDT, int MT, int NT>
@@ -575,11 +835,13 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   // the grid covers at most min(R, E_layer) active buckets: a layer size
   const int max_active = R < E ? R : E;
   if (view->wdtype == SCR_W_BF16) {
-    rc = cfg.m_chunk == 32 ? scr::launch_gemms<SCR_W_BF16, 2, 2>(a, max_active, marks, stream)
-                           : scr::launch_gemms<SCR_W_BF16, 6, 2>(a, max_active, marks, stream);
+    rc = cfg.m_chunk == 32                              ? scr::launch_gemms<SCR_W_BF16, 2, 2>(a, max_active, marks, stream)
+         : scr::expert_gemms_fit<SCR_W_BF16, 6>(a) ? scr::launch_expert_gemms<SCR_W_BF16, 6>(a, max_active, marks, stream)
+                                                    : scr::launch_gemms<SCR_W_BF16, 6, 2>(a, max_active, marks, stream);
   } else {
-    rc = cfg.m_chunk == 32 ? scr::launch_gemms<SCR_W_NVFP4, 2, 2>(a, max_active, marks, stream)
-                           : scr::launch_gemms<SCR_W_NVFP4, 6, 2>(a, max_active, marks, stream);
+    rc = cfg.m_chunk == 32                               ? scr::launch_gemms<SCR_W_NVFP4, 2, 2>(a, max_active, marks, stream)
+         : scr::expert_gemms_fit<SCR_W_NVFP4, 6>(a) ? scr::launch_expert_gemms<SCR_W_NVFP4, 6>(a, max_active, marks, stream)
+                                                     : scr::launch_gemms<SCR_W_NVFP4, 6, 2>(a, max_active, marks, stream);
   }
   if (rc) return rc;
 
