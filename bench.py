@@ -46,6 +46,9 @@ def _args():
     p.add_argument("--no-long", action="store_true", help="skip the 4096-token staged NVFP4 measurement")
     p.add_argument("--long-layers", type=int, default=8)
     p.add_argument("--long-reps", type=int, default=3)
+    p.add_argument("--no-decode", action="store_true", help="skip the decode-stream measurement")
+    p.add_argument("--decode-steps", type=int, default=48)
+    p.add_argument("--no-align", action="store_true", help="skip the align measurements")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gateup_short_prefill_96.json"),
                    help="HBM traffic of the dominant kernel from rocprofv3 counters (JSON), if present")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -171,6 +174,31 @@ def main():
     t_end = time.perf_counter()
     assert buf["n_miss"].cpu().numpy().sum() == 0, "warm steps admit nothing"
     ms_per_step = (t_end - t_start) * 1e3 / args.steps
+
+    # the same warm step captured once as a HIP graph and replayed (the path
+    # holds no host sync, so the whole step is capturable)
+    graph_ms = None
+    try:
+        y_eager = buf["y"].clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(buf["y"], y_eager), "graph replay equals the eager step"
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+        del g
+    except Exception as e:  # capture is an extra measurement; report why it is missing
+        graph_ms = f"unavailable: {type(e).__name__}: {e}"
     gu_ms = [m[1].elapsed_ms(m[2]) for m in marks]
     dn_ms = [m[2].elapsed_ms(m[3]) for m in marks]
     cb_ms = [m[3].elapsed_ms(m[4]) for m in marks]
@@ -211,6 +239,7 @@ def main():
                    "distinct": n_active, "query_width": Wd},
         "layer_ms": round(ms_per_step, 4),
         "ms_per_step_without_timing_events": round(ms_no_events, 4),
+        "ms_per_step_hip_graph": graph_ms if not isinstance(graph_ms, float) else round(graph_ms, 4),
         "gemm_tflops": round(gemm_tflops, 3),
         "kernels_us": {"gate_up": round(gu * 1e3, 2), "down": round(dn * 1e3, 2), "combine": round(cb * 1e3, 2)},
         "cold": {"ms_per_step": round(cold_ms, 3), "miss_copy_ms": round(copy_ms, 3),
@@ -224,6 +253,12 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_long:
         out["long_prefill_4096"] = long_prefill(args)
+        torch.cuda.empty_cache()
+    if not args.no_decode:
+        out["decode_stream"] = decode_stream(args)
+        torch.cuda.empty_cache()
+    if not args.no_align:
+        out["align"] = align_bench()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out))
@@ -320,6 +355,97 @@ def long_prefill(args) -> dict:
                                 "down": round(statistics.mean(x for r in reps for x in r[2]) * 1e3, 1)},
         "weight_bytes_per_layer": wbytes,
     }
+
+
+def decode_stream(args) -> dict:
+    """48 layers x 512 experts (bf16) over a 1650-slot bank, 4-token steps with
+    Zipf(1.1) routing, decode statistics on, from an empty bank.  Keys alias
+    512 host records (bounded pinned memory)."""
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    import workloads as W
+    import slot_cache_routed_amd._lib as L
+    import slot_cache_routed_amd.layer as LY
+
+    cfg = W.C4
+    E, k, H, I, S, NL, T = cfg.shape.E, cfg.shape.k, cfg.shape.H, cfg.shape.I, cfg.S, cfg.L, cfg.T
+    lay = LY.record_layout(L.SCR_W_BF16, H, I)
+    rec = int(lay.record_bytes)
+    P = 512
+    pool = LY.HostPool(NL, E, rec, P, payload_of=lambda key: key % P)
+
+    def one(e):
+        b13, b2 = W.expert_bf16(cfg.seed, e, H, I)
+        pool.write_payload(e, LY.pack_record_bf16(lay, b13, b2))
+
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+        list(ex.map(one, range(P)))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    steps = args.decode_steps
+    logits = [[dev(W.zipf_gumbel_logits(cfg.seed, l, st, T, E)) for l in range(NL)] for st in range(steps)]
+    xs = [[dev(W.f32_to_bf16_bits(W.decode_activations(cfg.seed, l, st, T, H)).view(np.int16)) for l in range(NL)]
+          for st in range(steps)]
+    sc = dev(np.ones(E, np.float32))
+    bank = LY.Bank(S, NL, E, L.SCR_W_BF16, rec)
+    buf = LY.LayerBuffers(T, E, k, H, I, S, L.SCR_W_BF16, width=128, y_dtype=L.SCR_Y_BF16)
+    s = torch.cuda.current_stream().cuda_stream
+    t_a, t_b = L.Timer(), L.Timer()
+    torch.cuda.synchronize()
+    t_a.record(s)
+    for st in range(steps):
+        for l in range(NL):
+            LY.demand_layer(bank, pool, l, logits[st][l], xs[st][l], sc, width=128, record_stats=True, buf=buf,
+                            shape=(k, H, I))
+    t_b.record(s)
+    total = t_a.elapsed_ms(t_b)
+    snap = bank.snapshot()
+    hits, misses, evictions, queries = [int(v) for v in snap["stats"]]
+    return {
+        "workload": f"decode_stream: {NL} layers x {E} experts, top-{k}, bf16, {S}-slot bank, {steps} steps of {T} "
+                    f"tokens, Zipf(1.1) routing, from an empty bank",
+        "step_ms": round(total / steps, 3),
+        "layer_step_ms": round(total / (steps * NL), 4),
+        "hit_rate": round(hits / max(1, hits + misses), 4),
+        "misses": misses, "evictions": evictions, "queries": queries,
+        "miss_copy_GBps_effective": round(misses * rec / (total * 1e-3) / 1e9, 2),
+        "note": "wall time of all layer-steps on the compute stream, PCIe-inclusive",
+    }
+
+
+def align_bench() -> dict:
+    """align_blocks at the workloads' shapes (launch-bound) and at a bandwidth shape."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    import slot_cache_routed_amd._lib as L
+
+    s = torch.cuda.current_stream().cuda_stream
+    out = {}
+    for name, n, nb, B in (("short_prefill_96", 960, 1100, 16), ("long_prefill_4096", 40960, 512, 16),
+                           ("decode_step", 40, 1650, 16), ("uniform_2100", 960, 2100, 16),
+                           ("bandwidth_655360x2100", 655360, 2100, 16)):
+        ids = torch.from_numpy(W.uniform_ids(4, n, nb)).cuda()
+        cap = L.align_capacity(n, nb, B)
+        m = min(n, nb)
+        bufs = [torch.empty(max(x, 1), dtype=torch.int32, device="cuda") for x in (cap, cap // B, 1, m, m + 1, 1)]
+        ws = torch.empty(L.align_workspace(n, nb), dtype=torch.uint8, device="cuda")
+        call = lambda: L.align_blocks(ids, n, None, 0, nb, B, *bufs, ws, ws.numel(), s)
+        for _ in range(3):
+            call()
+        reps = 20
+        t_a, t_b = L.Timer(), L.Timer()
+        torch.cuda.synchronize()
+        t_a.record(s)
+        for _ in range(reps):
+            call()
+        t_b.record(s)
+        us = t_a.elapsed_ms(t_b) * 1e3 / reps
+        moved = 4 * n + 4 * cap + 4 * (cap // B)     # ids in, sorted routes and block ids out
+        out[name] = {"routes": n, "buckets": nb, "us": round(us, 2), "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
+    return out
 
 
 def cpu_baseline(budget_s: float) -> dict:
