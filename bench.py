@@ -128,7 +128,7 @@ def main():
         LY.route_dedup(buf, logits)
         if phase_events:
             LY.record_timer(phase_events[1])
-        LY.admit(buf, bank, pool, 0, record_stats=False)
+        LY.admit(buf, bank, pool, 0, record_stats=False, batched=True)
         if phase_events:
             LY.record_timer(phase_events[2])
         LY.align(buf, id_map, E)
@@ -396,7 +396,7 @@ def decode_stream(args) -> dict:
     t_a.record(s)
     for st in range(steps):
         for l in range(NL):
-            LY.demand_layer(bank, pool, l, logits[st][l], xs[st][l], sc, width=128, record_stats=True, buf=buf,
+            LY.demand_layer(bank, pool, l, logits[st][l], xs[st][l], sc, width=128, record_stats=True, buf=buf, batched=True,
                             shape=(k, H, I))
     t_b.record(s)
     total = t_a.elapsed_ms(t_b)

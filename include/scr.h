@@ -215,12 +215,28 @@ int scr_ensure_slots(const scr_bank_desc* bank, int layer, const int32_t* distin
                      int width, int record_stats, int32_t* miss_slot, int32_t* miss_key,
                      int32_t* n_miss, hipStream_t stream);
 
+/* ensure_slots_batched [P1 Solution second bullet and the author's reply].
+ * The queries distinct[i*width .. i*width + width) for i < ceil(n / width), in
+ * order, in one launch; each is exactly one scr_ensure_slots call (its own
+ * clock tick, same slot decisions).  n_miss[i] receives query i's admitted
+ * count; the admitted misses of all queries are appended to miss_slot /
+ * miss_key, *n_total of them.  An entry whose slot a later query of the same
+ * call took again is marked superseded (slot -1), so one scr_copy_misses over
+ * the list (max_miss = n) moves each slot's final record.  Under LRU with
+ * min(T*k, E) <= S no query evicts an earlier query's admission (LRU evicts
+ * them last), so this equals copying each query's misses before the next.
+ *   n_miss device i32 [ceil(n / width)], miss_slot/miss_key device i32 [n],
+ *   n_total device i32 [1]; 1 <= width <= SCR_MAX_QUERY_WIDTH, n >= 1. */
+int scr_ensure_slots_batched(const scr_bank_desc* bank, int layer, const int32_t* distinct, int n,
+                             int width, int record_stats, int32_t* miss_slot, int32_t* miss_key,
+                             int32_t* n_miss, int32_t* n_total, hipStream_t stream);
+
 /* copy_misses [P1 Solution second bullet; P3 What: fixed-grid row copies from
  * the host source's device-mapped view].  For i < *n_miss (read on the
  * device) copies the record of key miss_key[i] from the pool into bank slot
  * miss_slot[i].  The grid depends only on max_miss, not on *n_miss, so the
  * call needs no host sync.  pool->record_bytes must equal bank->record_bytes.
- * 0 <= *n_miss <= max_miss <= SCR_MAX_QUERY_WIDTH. */
+ * Entries with miss_slot < 0 are skipped.  0 <= *n_miss <= max_miss <= 65536. */
 int scr_copy_misses(const scr_bank_desc* bank, const scr_host_pool* pool, const int32_t* miss_slot,
                     const int32_t* miss_key, const int32_t* n_miss, int max_miss,
                     hipStream_t stream);

@@ -25,7 +25,8 @@ SCR_MAX_SLOTS = 262144
 SCR_MAX_BUCKETS = 16384
 
 EXPORTS = (
-    "scr_record_layout_of", "scr_route", "scr_dedup", "scr_ensure_slots", "scr_copy_misses",
+    "scr_record_layout_of", "scr_route", "scr_dedup", "scr_ensure_slots", "scr_ensure_slots_batched",
+    "scr_copy_misses",
     "scr_align_capacity", "scr_align_workspace", "scr_align_blocks", "scr_tile_config",
     "scr_moe_workspace", "scr_grouped_moe_forward", "scr_stream_layer_async", "scr_stage_plan",
     "scr_stage_rows_async", "scr_fill_row_table", "scr_fill_staged_rows", "scr_bank_rebuild_map",
@@ -85,6 +86,7 @@ _SIGS = {
     "scr_route": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "scr_dedup": (_I, [_P, _I, _I, _P, _P, _P, _P]),
     "scr_ensure_slots": (_I, [C.POINTER(BankDesc), _I, _P, _I, _I, _I, _P, _P, _P, _P]),
+    "scr_ensure_slots_batched": (_I, [C.POINTER(BankDesc), _I, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
     "scr_copy_misses": (_I, [C.POINTER(BankDesc), C.POINTER(HostPoolDesc), _P, _P, _P, _I, _P]),
     "scr_align_capacity": (_SZ, [_I, _I, _I]),
     "scr_align_workspace": (_I, [_I, _I, C.POINTER(_SZ)]),
@@ -165,6 +167,13 @@ def ensure_slots(bank: BankDesc, layer, distinct, q_begin, width, record_stats, 
     _check("scr_ensure_slots", load().scr_ensure_slots(C.byref(bank), layer, _p(distinct), q_begin, width,
                                                        int(record_stats), _p(miss_slot), _p(miss_key),
                                                        _p(n_miss), stream))
+
+
+def ensure_slots_batched(bank: BankDesc, layer, distinct, n, width, record_stats, miss_slot, miss_key, n_miss,
+                         n_total, stream):
+    _check("scr_ensure_slots_batched", load().scr_ensure_slots_batched(
+        C.byref(bank), layer, _p(distinct), n, width, int(record_stats), _p(miss_slot), _p(miss_key), _p(n_miss),
+        _p(n_total), stream))
 
 
 def copy_misses(bank: BankDesc, pool: HostPoolDesc, miss_slot, miss_key, n_miss, max_miss, stream):

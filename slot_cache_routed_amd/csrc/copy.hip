@@ -109,7 +109,7 @@ extern "C" int scr_copy_misses(const scr_bank_desc* bank, const scr_host_pool* p
   SCR_CHECK_ARG(pool->key_rows_dev != nullptr, "copy_misses: pool has no device-mapped table");
   SCR_CHECK_ARG(pool->record_bytes == bank->record_bytes, "copy_misses: record sizes differ");
   SCR_CHECK_ARG(pool->L == bank->L && pool->E == bank->E, "copy_misses: pool and bank key spaces differ");
-  SCR_CHECK_ARG(max_miss >= 0 && max_miss <= SCR_MAX_QUERY_WIDTH, "copy_misses: max_miss out of range");
+  SCR_CHECK_ARG(max_miss >= 0 && max_miss <= 65536, "copy_misses: max_miss out of range");
   SCR_CHECK_ARG(miss_slot && miss_key && n_miss, "copy_misses: null pointer");
   if (max_miss == 0) return SCR_OK;
   const uint64_t chunks = (pool->record_bytes + scr::kCopyChunk - 1) / scr::kCopyChunk;

@@ -17,31 +17,43 @@ __device__ __forceinline__ uint64_t cand_key(uint64_t stamp, int slot) {
   return (stamp << kSlotBits) | (uint64_t)slot;
 }
 
-__global__ __launch_bounds__(kLruThreads) void ensure_slots_kernel(
-    int S, int E, int layer, int32_t* __restrict__ slot_key, uint64_t* __restrict__ slot_stamp,
-    int32_t* __restrict__ key_to_slot, uint64_t* __restrict__ clock, uint64_t* __restrict__ stats,
-    uint32_t* __restrict__ decode_freq, uint32_t* __restrict__ err, const int32_t* __restrict__ query,
-    int width, int record_stats, int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_key,
-    int32_t* __restrict__ n_miss) {
-  __shared__ uint32_t hit_bits[SCR_MAX_SLOTS / 32];
-  __shared__ int q_key[SCR_MAX_QUERY_WIDTH];
-  __shared__ int q_miss_rank[SCR_MAX_QUERY_WIDTH];  // -1: not a miss
-  __shared__ uint64_t sel_key[SCR_MAX_QUERY_WIDTH];
-  __shared__ int victim[SCR_MAX_QUERY_WIDTH];
-  __shared__ unsigned hist[256];
-  __shared__ int wave_tot[kWave + 1];
-  __shared__ int s_nhit, s_nmiss, s_nsel, s_evict;
-  __shared__ uint64_t s_prefix;
-  __shared__ unsigned s_rank;
+struct EnsureShared {
+  uint32_t hit_bits[SCR_MAX_SLOTS / 32];
+  int q_key[SCR_MAX_QUERY_WIDTH];
+  int q_miss_rank[SCR_MAX_QUERY_WIDTH];  // -1: not a miss
+  uint64_t sel_key[SCR_MAX_QUERY_WIDTH];
+  int victim[SCR_MAX_QUERY_WIDTH];
+  unsigned hist[256];
+  int wave_tot[kWave + 1];
+  int nhit, nmiss, nsel, evict;
+  uint64_t prefix;
+  unsigned rank;
+};
 
+struct BankRefs {
+  int S, E, layer;
+  int32_t* slot_key;
+  uint64_t* slot_stamp;
+  int32_t* key_to_slot;
+  uint64_t* stats;
+  uint32_t* decode_freq;
+  uint32_t* err;
+};
+
+// One LRU query with recency stamp `now`; the admitted misses are written in
+// query order to miss_slot/miss_key[0 ..) and their number returned (in every
+// thread).  Called by all threads of the workgroup.
+__device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, const int32_t* __restrict__ query,
+                            int width, int record_stats, int32_t* __restrict__ miss_slot,
+                            int32_t* __restrict__ miss_key) {
   const int tid = threadIdx.x;
-  const uint64_t now = *clock + 1;
+  const int S = bk.S, E = bk.E;
   const int nwords = (S + 31) / 32;
-  for (int i = tid; i < nwords; i += blockDim.x) hit_bits[i] = 0;
+  for (int i = tid; i < nwords; i += blockDim.x) sh.hit_bits[i] = 0;
   if (tid == 0) {
-    s_nhit = 0;
-    s_evict = 0;
-    s_nsel = 0;
+    sh.nhit = 0;
+    sh.evict = 0;
+    sh.nsel = 0;
   }
   __syncthreads();
 
@@ -50,12 +62,12 @@ __global__ __launch_bounds__(kLruThreads) void ensure_slots_kernel(
   if (tid < width) {
     const int e = query[tid];
     if (e >= 0 && e < E) {
-      my_key = layer * E + e;
-      const int s = key_to_slot[my_key];
+      my_key = bk.layer * E + e;
+      const int s = bk.key_to_slot[my_key];
       if (s >= 0) {
-        slot_stamp[s] = now;  // touch the hit
-        atomicOr(&hit_bits[s >> 5], 1u << (s & 31));
-        atomicAdd(&s_nhit, 1);
+        bk.slot_stamp[s] = now;  // touch the hit
+        atomicOr(&sh.hit_bits[s >> 5], 1u << (s & 31));
+        atomicAdd(&sh.nhit, 1);
       } else {
         is_miss = 1;
       }
@@ -70,95 +82,95 @@ __global__ __launch_bounds__(kLruThreads) void ensure_slots_kernel(
       const int o = __shfl_up(v, off, kWave);
       if (lane >= off) v += o;
     }
-    if (lane == kWave - 1) wave_tot[wv] = v;
+    if (lane == kWave - 1) sh.wave_tot[wv] = v;
     __syncthreads();
     if (wv == 0) {
-      int t = lane < nw ? wave_tot[lane] : 0;
+      int t = lane < nw ? sh.wave_tot[lane] : 0;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
         const int o = __shfl_up(t, off, kWave);
         if (lane >= off) t += o;
       }
-      if (lane < nw) wave_tot[lane] = t;
+      if (lane < nw) sh.wave_tot[lane] = t;
     }
     __syncthreads();
-    const int before = wv > 0 ? wave_tot[wv - 1] : 0;
+    const int before = wv > 0 ? sh.wave_tot[wv - 1] : 0;
     if (tid < SCR_MAX_QUERY_WIDTH) {
-      q_key[tid] = my_key;
-      q_miss_rank[tid] = is_miss ? before + v - 1 : -1;
+      sh.q_key[tid] = my_key;
+      sh.q_miss_rank[tid] = is_miss ? before + v - 1 : -1;
     }
-    if (tid == 0) s_nmiss = wave_tot[nw - 1];
+    if (tid == 0) sh.nmiss = sh.wave_tot[nw - 1];
   }
   __syncthreads();
 
-  const int m = s_nmiss;
-  const int n_cand = S - s_nhit;
+  const int m = sh.nmiss;
+  const int n_cand = S - sh.nhit;
   const int m_adm = m < n_cand ? m : n_cand;
 
   if (m_adm > 0) {
     // radix select: the m_adm-th smallest candidate key, 8 bits at a time
     if (tid == 0) {
-      s_prefix = 0;
-      s_rank = (unsigned)m_adm;
+      sh.prefix = 0;
+      sh.rank = (unsigned)m_adm;
     }
     __syncthreads();
     for (int shift = 56; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += blockDim.x) hist[i] = 0;
+      for (int i = tid; i < 256; i += blockDim.x) sh.hist[i] = 0;
       __syncthreads();
-      const uint64_t prefix = s_prefix;
+      const uint64_t prefix = sh.prefix;
       for (int s = tid; s < S; s += blockDim.x) {
-        if ((hit_bits[s >> 5] >> (s & 31)) & 1u) continue;
-        const uint64_t key = cand_key(slot_stamp[s], s);
+        if ((sh.hit_bits[s >> 5] >> (s & 31)) & 1u) continue;
+        const uint64_t key = cand_key(bk.slot_stamp[s], s);
         const bool match = (shift == 56) ? true : ((key >> (shift + 8)) == prefix);
-        if (match) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        if (match) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
       }
       __syncthreads();
       if (tid == 0) {
-        unsigned r = s_rank, acc = 0;
+        unsigned r = sh.rank, acc = 0;
         int d = 0;
         for (; d < 256; ++d) {
-          if (acc + hist[d] >= r) break;
-          acc += hist[d];
+          if (acc + sh.hist[d] >= r) break;
+          acc += sh.hist[d];
         }
-        s_rank = r - acc;
-        s_prefix = (prefix << 8) | (uint64_t)d;
+        sh.rank = r - acc;
+        sh.prefix = (prefix << 8) | (uint64_t)d;
       }
       __syncthreads();
     }
-    const uint64_t thresh = s_prefix;
+    const uint64_t thresh = sh.prefix;
     // collect the selected candidates (exactly m_adm distinct keys <= thresh)
     for (int s = tid; s < S; s += blockDim.x) {
-      if ((hit_bits[s >> 5] >> (s & 31)) & 1u) continue;
-      const uint64_t key = cand_key(slot_stamp[s], s);
+      if ((sh.hit_bits[s >> 5] >> (s & 31)) & 1u) continue;
+      const uint64_t key = cand_key(bk.slot_stamp[s], s);
       if (key <= thresh) {
-        const int idx = atomicAdd(&s_nsel, 1);
-        if (idx < SCR_MAX_QUERY_WIDTH) sel_key[idx] = key;
+        const int idx = atomicAdd(&sh.nsel, 1);
+        if (idx < SCR_MAX_QUERY_WIDTH) sh.sel_key[idx] = key;
       }
     }
     __syncthreads();
     // order the selection ascending: rank = number of smaller selected keys
-    const int nsel = s_nsel < m_adm ? s_nsel : m_adm;
+    const int nsel = sh.nsel < m_adm ? sh.nsel : m_adm;
     for (int i = tid; i < nsel; i += blockDim.x) {
-      const uint64_t ki = sel_key[i];
+      const uint64_t ki = sh.sel_key[i];
       int rank = 0;
-      for (int j = 0; j < nsel; ++j) rank += sel_key[j] < ki;
-      victim[rank] = (int)(ki & ((1ull << kSlotBits) - 1));
+      for (int j = 0; j < nsel; ++j) rank += sh.sel_key[j] < ki;
+      sh.victim[rank] = (int)(ki & ((1ull << kSlotBits) - 1));
     }
     __syncthreads();
     // the i-th miss takes the i-th victim
     if (tid < width) {
-      const int r = q_miss_rank[tid];
+      const int r = sh.q_miss_rank[tid];
       if (r >= 0 && r < nsel) {
-        const int v = victim[r];
-        const int key = q_key[tid];
-        const int old = slot_key[v];
+        const int v = sh.victim[r];
+        const int key = sh.q_key[tid];
+        const int old = bk.slot_key[v];
         if (old >= 0) {
-          key_to_slot[old] = -1;
-          atomicAdd(&s_evict, 1);
+          bk.key_to_slot[old] = -1;
+          atomicAdd(&sh.evict, 1);
         }
-        slot_key[v] = key;
-        key_to_slot[key] = v;
-        slot_stamp[v] = now;
+        bk.slot_key[v] = key;
+        bk.key_to_slot[key] = v;
+        bk.slot_stamp[v] = now;
         miss_slot[r] = v;
         miss_key[r] = key;
       }
@@ -167,17 +179,60 @@ __global__ __launch_bounds__(kLruThreads) void ensure_slots_kernel(
   }
 
   if (tid == 0) {
-    *n_miss = m_adm;
-    *clock = now;
-    if (m > m_adm) atomicOr(err, SCR_ERR_CAPACITY);
+    if (m > m_adm) atomicOr(bk.err, SCR_ERR_CAPACITY);
     if (record_stats) {
-      stats[0] += (uint64_t)s_nhit;
-      stats[1] += (uint64_t)m_adm;
-      stats[2] += (uint64_t)s_evict;
-      stats[3] += 1;
+      bk.stats[0] += (uint64_t)sh.nhit;
+      bk.stats[1] += (uint64_t)m_adm;
+      bk.stats[2] += (uint64_t)sh.evict;
+      bk.stats[3] += 1;
     }
   }
-  if (record_stats && my_key >= 0) decode_freq[my_key] += 1u;
+  if (record_stats && my_key >= 0) bk.decode_freq[my_key] += 1u;
+  __syncthreads();
+  return m_adm;
+}
+
+__global__ __launch_bounds__(kLruThreads) void ensure_slots_kernel(BankRefs bk, uint64_t* __restrict__ clock,
+                                                                  const int32_t* __restrict__ query, int width,
+                                                                  int record_stats, int32_t* __restrict__ miss_slot,
+                                                                  int32_t* __restrict__ miss_key,
+                                                                  int32_t* __restrict__ n_miss) {
+  __shared__ EnsureShared sh;
+  const uint64_t now = *clock + 1;
+  const int m = ensure_query(sh, bk, now, query, width, record_stats, miss_slot, miss_key);
+  if (threadIdx.x == 0) {
+    *n_miss = m;
+    *clock = now;
+  }
+}
+
+// Several consecutive queries in one launch, each with its own clock tick.
+// Their admitted misses are appended to one list; an entry whose slot was
+// taken again by a later query of the same call is marked superseded (slot -1)
+// so that one copy over the list moves only each slot's final record.
+__global__ __launch_bounds__(kLruThreads) void ensure_slots_batched_kernel(
+    BankRefs bk, uint64_t* __restrict__ clock, const int32_t* __restrict__ distinct, int width, int n_queries,
+    int last_width, int record_stats, int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_key,
+    int32_t* __restrict__ n_miss, int32_t* __restrict__ n_total) {
+  __shared__ EnsureShared sh;
+  uint64_t now = *clock;
+  int total = 0;
+  for (int q = 0; q < n_queries; ++q) {
+    now += 1;
+    const int w = q + 1 < n_queries ? width : last_width;
+    const int m = ensure_query(sh, bk, now, distinct + (size_t)q * width, w, record_stats, miss_slot + total,
+                               miss_key + total);
+    if (threadIdx.x == 0) n_miss[q] = m;
+    total += m;
+  }
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int v = miss_slot[i];
+    if (v >= 0 && bk.slot_key[v] != miss_key[i]) miss_slot[i] = -1;
+  }
+  if (threadIdx.x == 0) {
+    *clock = now;
+    *n_total = total;
+  }
 }
 
 __global__ void rebuild_map_clear(int32_t* __restrict__ key_to_slot, int n) {
@@ -203,11 +258,25 @@ int check_bank(const scr_bank_desc* b) {
   return SCR_OK;
 }
 
+static BankRefs bank_refs(const scr_bank_desc* b, int layer) {
+  BankRefs r;
+  r.S = b->S;
+  r.E = b->E;
+  r.layer = layer;
+  r.slot_key = b->slot_key;
+  r.slot_stamp = b->slot_stamp;
+  r.key_to_slot = b->key_to_slot;
+  r.stats = b->stats;
+  r.decode_freq = b->decode_freq;
+  r.err = b->err;
+  return r;
+}
+
 }  // namespace scr
 
-extern "C" int scr_ensure_slots(const scr_bank_desc* bank, int layer, const int32_t* distinct,
-                                int q_begin, int width, int record_stats, int32_t* miss_slot,
-                                int32_t* miss_key, int32_t* n_miss, hipStream_t stream) {
+extern "C" int scr_ensure_slots(const scr_bank_desc* bank, int layer, const int32_t* distinct, int q_begin,
+                                int width, int record_stats, int32_t* miss_slot, int32_t* miss_key,
+                                int32_t* n_miss, hipStream_t stream) {
   int rc = scr::check_bank(bank);
   if (rc) return rc;
   SCR_CHECK_ARG(layer >= 0 && layer < bank->L, "ensure_slots: layer %d out of [0, %d)", layer, bank->L);
@@ -215,10 +284,28 @@ extern "C" int scr_ensure_slots(const scr_bank_desc* bank, int layer, const int3
                 SCR_MAX_QUERY_WIDTH);
   SCR_CHECK_ARG(q_begin >= 0, "ensure_slots: q_begin must be >= 0");
   SCR_CHECK_ARG(distinct && miss_slot && miss_key && n_miss, "ensure_slots: null pointer");
-  hipLaunchKernelGGL(scr::ensure_slots_kernel, dim3(1), dim3(scr::kLruThreads), 0, stream, bank->S,
-                     bank->E, layer, bank->slot_key, bank->slot_stamp, bank->key_to_slot, bank->clock,
-                     bank->stats, bank->decode_freq, bank->err, distinct + q_begin, width,
-                     record_stats ? 1 : 0, miss_slot, miss_key, n_miss);
+  hipLaunchKernelGGL(scr::ensure_slots_kernel, dim3(1), dim3(scr::kLruThreads), 0, stream,
+                     scr::bank_refs(bank, layer), bank->clock, distinct + q_begin, width, record_stats ? 1 : 0,
+                     miss_slot, miss_key, n_miss);
+  SCR_CHECK_LAUNCH();
+  return SCR_OK;
+}
+
+extern "C" int scr_ensure_slots_batched(const scr_bank_desc* bank, int layer, const int32_t* distinct, int n,
+                                        int width, int record_stats, int32_t* miss_slot, int32_t* miss_key,
+                                        int32_t* n_miss, int32_t* n_total, hipStream_t stream) {
+  int rc = scr::check_bank(bank);
+  if (rc) return rc;
+  SCR_CHECK_ARG(layer >= 0 && layer < bank->L, "ensure_slots_batched: layer %d out of [0, %d)", layer, bank->L);
+  SCR_CHECK_ARG(width >= 1 && width <= SCR_MAX_QUERY_WIDTH, "ensure_slots_batched: width must be in [1, %d]",
+                SCR_MAX_QUERY_WIDTH);
+  SCR_CHECK_ARG(n >= 1, "ensure_slots_batched: n must be >= 1");
+  SCR_CHECK_ARG(distinct && miss_slot && miss_key && n_miss && n_total, "ensure_slots_batched: null pointer");
+  const int n_queries = (n + width - 1) / width;
+  const int last_width = n - (n_queries - 1) * width;
+  hipLaunchKernelGGL(scr::ensure_slots_batched_kernel, dim3(1), dim3(scr::kLruThreads), 0, stream,
+                     scr::bank_refs(bank, layer), bank->clock, distinct, width, n_queries, last_width,
+                     record_stats ? 1 : 0, miss_slot, miss_key, n_miss, n_total);
   SCR_CHECK_LAUNCH();
   return SCR_OK;
 }

@@ -192,7 +192,7 @@ class LayerBuffers:
             "topk_ids": _i32(R), "topk_w": torch.empty(max(R, 1), dtype=torch.float32, device=_DEV),
             "distinct": _i32(self.lmax), "n_distinct": _i32(1), "inverse": _i32(R),
             "miss_slot": _i32(self.n_queries * self.width, -1), "miss_key": _i32(self.n_queries * self.width, -1),
-            "n_miss": _i32(self.n_queries, 0),
+            "n_miss": _i32(self.n_queries, 0), "n_total": _i32(1, 0),
             "sorted_routes": _i32(cap), "block_bucket": _i32(max(cap // B, 1)), "n_post_pad": _i32(1),
             "active_buckets": _i32(m), "active_block_begin": _i32(m + 1), "n_active": _i32(1),
             "align_ws": torch.empty(L.align_workspace(R, self.num_buckets), dtype=torch.uint8, device=_DEV),
@@ -220,11 +220,20 @@ def route_dedup(buf: LayerBuffers, logits: torch.Tensor, stream=None):
     L.dedup(buf["topk_ids"], buf.R, buf.E, buf["distinct"], buf["n_distinct"], buf["inverse"], s)
 
 
-def admit(buf: LayerBuffers, bank: Bank, pool: HostPool, layer: int, record_stats: bool, stream=None):
+def admit(buf: LayerBuffers, bank: Bank, pool: HostPool, layer: int, record_stats: bool, stream=None,
+          batched: bool = False):
     """Hands the distinct list to the LRU one query at a time, copying each
-    query's misses before the next query runs (same stream, no host sync)."""
+    query's misses before the next query runs (same stream, no host sync).
+    batched=True plans every query in one launch and copies all final misses
+    in one launch (the same slot decisions and bank contents under LRU)."""
     s = _stream(stream)
     W = buf.width
+    if batched:
+        n = buf.lmax
+        L.ensure_slots_batched(bank.desc, layer, buf["distinct"], n, W, record_stats, buf["miss_slot"],
+                               buf["miss_key"], buf["n_miss"], buf["n_total"], s)
+        L.copy_misses(bank.desc, pool.desc, buf["miss_slot"], buf["miss_key"], buf["n_total"], n, s)
+        return
     for q in range(buf.n_queries):
         q0 = q * W
         w = min(W, buf.lmax - q0)
@@ -252,7 +261,7 @@ def forward(buf: LayerBuffers, view: L.RoutedExperts, x: torch.Tensor, stream=No
 
 
 def demand_layer(bank: Bank, pool: HostPool, layer: int, logits, x, input_scale, width=128, record_stats=False,
-                 y_dtype=L.SCR_Y_F32, buf: LayerBuffers | None = None, stream=None, shape=None):
+                 y_dtype=L.SCR_Y_F32, buf: LayerBuffers | None = None, stream=None, shape=None, batched=False):
     """Demand (slot) path of one layer: route, dedup, per-query ensure + miss copy,
     align over the bank's slots through key_to_slot, grouped GEMM at the slots."""
     T, E = logits.shape
@@ -260,7 +269,7 @@ def demand_layer(bank: Bank, pool: HostPool, layer: int, logits, x, input_scale,
     if buf is None:
         buf = LayerBuffers(T, E, k, H, I, bank.S, bank.wdtype, width=width, y_dtype=y_dtype)
     route_dedup(buf, logits, stream)
-    admit(buf, bank, pool, layer, record_stats, stream)
+    admit(buf, bank, pool, layer, record_stats, stream, batched=batched)
     id_map = bank.key_to_slot.data_ptr() + layer * E * 4
     align(buf, id_map, E, stream)
     view = make_view(layer, E, k, H, I, bank.wdtype, bank.S, bank.row_table, input_scale)

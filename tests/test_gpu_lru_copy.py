@@ -179,3 +179,70 @@ def test_copy_misses_bytes_equal_host_and_others_untouched():
     for s in range(S):
         if s not in touched:
             assert torch.equal(bank.slot_record(s), before[s * rec:(s + 1) * rec]), s
+
+
+def test_batched_admission_equals_query_by_query():
+    """One launch for all queries of a chunk gives the per-query splits, bank
+    state and output bits of the query-by-query admission."""
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    from helpers import ExpertSource, fill_pool
+    cfg = W.C2
+    E, k, H, I, S, NL, T = cfg.shape.E, cfg.shape.k, cfg.shape.H, cfg.shape.I, cfg.S, cfg.L, cfg.T
+    lay = LY.record_layout(L.SCR_W_BF16, H, I)
+    src = ExpertSource(cfg.seed, H, I, "bf16")
+    pool = LY.HostPool(NL, E, lay.record_bytes, E, payload_of=lambda key: key % E)
+    fill_pool(pool, src, lay, range(E))
+    lg, _ = W.logits_with_chosen(cfg.seed, T, E, k, 160)
+    xb = W.f32_to_bf16_bits(W.activations_normal(cfg.seed, T, H))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    sc = dev(np.ones(E, np.float32))
+    fill = W.bank_prefilled(cfg.seed, S, NL, E, 600, exclude_layer=0)
+    res = []
+    for batched in (False, True):
+        bank = LY.Bank(S, NL, E, L.SCR_W_BF16, lay.record_bytes)
+        bank.load_fill(fill)
+        d = LY.demand_layer(bank, pool, 0, dev(lg), dev(xb.view(np.int16)), sc, width=128, shape=(k, H, I),
+                            batched=batched)
+        torch.cuda.synchronize()
+        res.append((d["n_miss"].cpu().numpy().tolist(), bank.snapshot(), d["y"].clone(), bank.rows.clone()))
+    assert res[0][0] == res[1][0] == [128, 32, 0, 0]
+    for key in ("slot_key", "key_to_slot", "slot_stamp", "stats", "clock"):
+        assert np.array_equal(np.asarray(res[0][1][key]), np.asarray(res[1][1][key])), key
+    assert torch.equal(res[0][2], res[1][2]) and torch.equal(res[0][3], res[1][3])
+
+
+def test_batched_admission_supersedes_re_evicted_entries():
+    """A bank too small for the chunk (10 experts, 6 slots, queries of 4): later
+    queries take the first query's slots again; the list marks those entries
+    superseded and every slot ends with its final owner's record."""
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    S, NL, E, rec = 6, 1, 16, 4096
+    g = np.random.default_rng(4)
+    pool = LY.HostPool(NL, E, rec, E)
+    for p in range(E):
+        pool.write_payload(p, g.integers(0, 256, size=rec, dtype=np.uint8))
+    bank = LY.Bank(S, NL, E, 0, rec)
+    distinct = torch.arange(10, dtype=torch.int32, device="cuda")      # 10 experts, 6 slots, queries of 4
+    ms = torch.full((10,), -9, dtype=torch.int32, device="cuda")
+    mk = torch.full((10,), -9, dtype=torch.int32, device="cuda")
+    nm = torch.zeros(3, dtype=torch.int32, device="cuda")
+    nt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    L.ensure_slots_batched(bank.desc, 0, distinct, 10, 4, 0, ms, mk, nm, nt, s)
+    L.copy_misses(bank.desc, pool.desc, ms, mk, nt, 10, s)
+    torch.cuda.synchronize()
+    st = SlotBankState(S, NL, E)
+    splits = []
+    for q0 in range(0, 10, 4):
+        splits.append(len(ensure_slots(st, 0, np.arange(q0, min(10, q0 + 4), dtype=np.int32), False)[0]))
+    snap = bank.snapshot()
+    for key in ("slot_key", "key_to_slot", "slot_stamp", "clock"):
+        assert np.array_equal(np.asarray(snap[key]), np.asarray(getattr(st, key))), key
+    assert nm.cpu().numpy().tolist() == splits == [4, 4, 2] and snap["err"] == st.err == 0
+    slots = ms.cpu().numpy()[:int(nt.item())]
+    assert (slots < 0).sum() == 4, "the first query's four admissions were taken again"
+    for sl in range(S):
+        key = int(snap["slot_key"][sl])
+        assert torch.equal(bank.slot_record(sl).cpu(), pool.key_record(key))
