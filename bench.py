@@ -21,6 +21,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -217,7 +218,12 @@ def main():
     if os.path.exists(args.traffic):
         with open(args.traffic) as f:
             tr = json.load(f)
-        traffic = tr.get("bytes_per_launch")
+        # counters describe the kernel as it was built when they were taken
+        src = os.path.join(ROOT, "slot_cache_routed_amd", "csrc", "gemm.hip")
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()[:16]
+        if tr.get("gemm_source_sha256_16") == digest:
+            traffic = tr.get("bytes_per_launch")
 
     out = {
         "metric": METRIC,
@@ -245,7 +251,7 @@ def main():
         "cold": {"ms_per_step": round(cold_ms, 3), "miss_copy_ms": round(copy_ms, 3),
                  "miss_copy_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 2), "misses": 160,
                  "note": "bank reset to its pre-filled state before each step; includes PCIe host-to-HBM copies"},
-        "roofline": {"bound": "hbm", "kernel": "gateup_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "moe_gemm_kernel<bf16,2,2,gate/up>", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes": gu_bytes},
     }
