@@ -42,12 +42,14 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 }
 
 // ------------------------------------------------------------ NVFP4 decode
-// e4m3 (OCP E4M3FN) code -> float (finite codes only)
+// e4m3 (OCP E4M3FN) code -> float (finite codes only), without branches:
+// |v| = (m + 8 [e > 0]) * 2^(max(e, 1) - 10), exact in fp32 (the subnormal
+// case e = 0 is m/8 * 2^-6)
 __device__ __forceinline__ float e4m3_to_f32(unsigned c) {
   const unsigned e = (c >> 3) & 0xFu, m = c & 7u;
-  float mag = e == 0u ? (float)m * 0.001953125f  // m/8 * 2^-6
-                      : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (c & 0x80u) ? -mag : mag;
+  const unsigned mant = m | (min(e, 1u) << 3);
+  const float mag = __builtin_amdgcn_ldexpf((float)mant, (int)max(e, 1u) - 10);
+  return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
 }
 
 // per-route rows: fp32 for bf16 weights (their output tolerance is tighter),
@@ -146,7 +148,16 @@ struct BFrag<SCR_W_BF16, NT> {
       for (int st = 0; st < 4; ++st)
         raw[t][st] = ldg<u32x4>(tile[t] + (size_t)kb * 4096 + st * 1024 + lane * 16);
   }
+  // through a buffer resource: the wave-uniform tile offsets go in scalar
+  // registers, the per-lane part is the constant lane * 16
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, const int* toff, const int*, int lane) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) raw[t][st] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, toff[t] + st * 1024, 0);
+  }
   __device__ __forceinline__ bf16x8 get(int t, int st) const { return __builtin_bit_cast(bf16x8, raw[t][st]); }
+  __device__ __forceinline__ bf16x8 get_hw(int t, int st) const { return get(t, st); }
 };
 
 template <int NT>
@@ -160,8 +171,20 @@ struct BFrag<SCR_W_NVFP4, NT> {
       sc[t] = ldg<unsigned short>(stile[t] + (size_t)kb * 128 + lane * 2);
     }
   }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, const int* toff, const int* soff, int lane) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      codes[t] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, toff[t], 0);
+      sc[t] = __builtin_amdgcn_raw_buffer_load_b16(r, lane * 2, soff[t], 0);
+    }
+  }
   __device__ __forceinline__ bf16x8 get(int t, int st) const {
     return dequant8_hw(codes[t][st], e4m3_to_f32((sc[t] >> (8 * (st >> 1))) & 0xFFu));
+  }
+  // the same with the scale decoded by the hardware OCP E4M3 conversion
+  __device__ __forceinline__ bf16x8 get_hw(int t, int st) const {
+    const float scale = (st >> 1) ? __builtin_amdgcn_cvt_f32_fp8((int)sc[t], 1) : __builtin_amdgcn_cvt_f32_fp8((int)sc[t], 0);
+    return dequant8_hw(codes[t][st], scale);
   }
 };
 
@@ -386,106 +409,116 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
   }
 }
 
-// ------------------------------------------------- expert-persistent GEMM
+// ------------------------------------------------------- wide-tile GEMM
 //
-// For chunks with many rows per expert: one workgroup of 8 waves owns one
-// active bucket and walks all of its N chunks, so the weight stream of the
-// expert never restarts (the prefetch ring runs across chunk boundaries) and
-// no other workgroup re-reads the bucket's activation rows for it.  A chunk
-// is 256 weight rows: each wave owns NTW = 2 tiles of 16 rows (gate/up: one
-// gate tile and the matching up tile, 16 h columns; down: 32 output columns).
-// Down keeps the bucket's whole h block (K = I <= 512) resident in LDS for
-// all chunks; gate/up stages x blocks of 128 columns double-buffered.
-constexpr int kExpWaves = 8;
-constexpr int kExpThreads = 64 * kExpWaves;
-constexpr int kNTW = 2;
-constexpr int kResMaxKB = 4;  // resident activation blocks (K <= 512)
+// For chunks with many rows per expert (the MFMA-bound shapes).  One
+// workgroup of EW waves owns one active bucket and a contiguous range of its
+// N chunks; the weight stream of that range never restarts (the prefetch ring
+// runs across chunk boundaries).  Each wave owns NTW row tiles of 16 weight
+// rows per chunk (gate/up: NTW/2 gate tiles and the matching up tiles; down:
+// NTW tiles of output columns), so every activation fragment read from LDS
+// feeds NTW MFMAs.  Two workgroups share a CU (256 registers per wave), so
+// the decode, the waits and the barriers of one overlap the MFMAs of the
+// other.
+//
+// Activations reach LDS by direct global-to-LDS loads (no register staging):
+// two K-block buffers, each a [rows][128] bf16 tile whose 16-byte chunks are
+// XOR-swizzled by (row mod 16), so the fragment reads hit distinct banks.
+// The buffers are separate arrays so that the compiler can tell a read of one
+// from the direct loads still in flight into the other.
+constexpr int kWideBufs = 4;  // activation K-block buffers in LDS (loaded kWideBufs - 1 blocks ahead)
+constexpr int kWideRing = 2;  // NVFP4 weight ring depth in K blocks (deeper measured slower)
 
-template <int WDT, int MT, bool GATEUP, bool ARES>
-struct ExpSmem {
-  static constexpr int kBufs = ARES ? kResMaxKB : 2;
-  bf16 As[kBufs][MT * 16 + 1][kAStride];  // the extra row takes the stores of unused staging lanes
-  int src_row[MT * 16];
+// s_waitcnt immediate that waits until at most n vector memory operations are
+// outstanding (gfx9 encoding; the LDS and export counters are left alone)
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
+template <int WDT, int NTW>
+struct BLoads {  // vector memory instructions per wave for one K block of weights
+  static constexpr int value = WDT == SCR_W_NVFP4 ? 2 * NTW : 4 * NTW;
 };
 
-template <int WDT, int MT, bool GATEUP, bool ARES, int MTC>
-__device__ __forceinline__ void expert_pass(const GemmArgs& a, ExpSmem<WDT, MT, GATEUP, ARES>& sm, int m0,
-                                            const uint8_t* const* tile0, const uint8_t* const* stile0,
-                                            float gs, int nkb, int nchunks) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int WDT, int MT, bool GATEUP, int EW, int NTW, int MTC>
+__device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row, bf16* As0, bf16* As1, bf16* As2,
+                                          bf16* As3, uint32_t* pfbuf, int m0, __amdgpu_buffer_rsrc_t wrsrc,
+                                          const int* toff0, const int* soff0, float gs, int nkb, int c_begin,
+                                          int c_end) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const bf16* abase = GATEUP ? a.x : a.h;
-  constexpr int kRowChunks = kKB / 8;
-  constexpr int kChunks = MTC * 16 * kRowChunks;
-  constexpr int kPerThread = (kChunks + kExpThreads - 1) / kExpThreads;
-  constexpr int CT = GATEUP ? kExpWaves * kNTW / 2 : kExpWaves * kNTW;  // row tiles per chunk and tensor half
-  constexpr size_t tile_bytes = WDT == SCR_W_NVFP4 ? 1024 : 4096;
+  constexpr int CT = GATEUP ? EW * NTW / 2 : EW * NTW;  // row tiles per chunk and tensor half
+  constexpr int tile_bytes = WDT == SCR_W_NVFP4 ? 1024 : 4096;
+  bf16* const bufs[kWideBufs] = {As0, As1, As2, As3};
 
-  // staging addresses of this thread (fixed for the pass)
-  const bf16* asrc[kPerThread];
-  bool avalid[kPerThread];
-  int adst[kPerThread];
+  // activations through a buffer resource over x (gate/up) or h (down)
+  const __amdgpu_buffer_rsrc_t arsrc =
+      GATEUP ? __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, a.T * a.H * 2, 0x00020000)
+             : __builtin_amdgcn_make_buffer_rsrc((void*)a.h, (short)0, a.h_rows * a.I * 2, 0x00020000);
+  // direct-load sources of this lane: the 4 * MTC wave instructions of a K
+  // block (each fills 64 16-byte chunks = 4 rows) are dealt round-robin to the
+  // EW waves; every wave issues the same count NA (a wave past the end repeats
+  // the last instruction: the same bytes to the same place), so that the
+  // waits below can count them.  Instruction j fills LDS chunk q = 64 j +
+  // lane of a buffer, i.e. row q / 16, physical chunk q % 16, which holds
+  // logical chunk (q % 16) ^ (row % 16).
+  constexpr int NA = (4 * MTC + EW - 1) / EW;
+  int aoff[NA];  // byte offsets
+  int adst[NA];  // LDS element offsets of the wave's 1 KB destinations
 #pragma unroll
-  for (int u = 0; u < kPerThread; ++u) {
-    const int ci = u * kExpThreads + tid;
-    const bool in = ci < kChunks;
-    const int r = in ? ci / kRowChunks : 0, ch = ci % kRowChunks;
-    const int off = sm.src_row[r];
-    avalid[u] = in && off >= 0;
-    asrc[u] = abase + (off >= 0 ? off : 0) + ch * 8;
-    adst[u] = (in ? r : MT * 16) * kAStride + ch * 8;
+  for (int u = 0; u < NA; ++u) {
+    const int j = min(u * EW + wave, 4 * MTC - 1);
+    const int q = j * 64 + lane;
+    const int r = q >> 4, c = (q & 15) ^ (r & 15);
+    const int off = src_row[r];
+    aoff[u] = 2 * (off >= 0 ? off : 0) + 16 * c;  // padding rows read row 0 (their outputs are dropped)
+    adst[u] = j * 512;
   }
-  struct AStage {
-    u32x4 v[kPerThread];
-  };
-  auto load_a = [&](AStage& st, int kb) {
+  auto load_a = [&](bf16* buf, int kb) {
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) st.v[u] = ldg<u32x4>(asrc[u] + kb * kKB);
-  };
-  auto store_a = [&](const AStage& st, int buf) {
-    bf16* base = &sm.As[buf][0][0];
-#pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(base + adst[u]) = avalid[u] ? st.v[u] : z;
-    }
+    for (int u = 0; u < NA; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (__attribute__((address_space(3))) void*)(buf + adst[u]), 16,
+                                               aoff[u], kb * (2 * kKB), 0, 0);
   };
   // weights of flat step s = chunk * nkb + kb
-  auto load_b = [&](BFrag<WDT, kNTW>& f, int s) {
+  auto load_b = [&](BFrag<WDT, NTW>& f, int s) {
     const int ch = s / nkb, kb = s - ch * nkb;
-    const size_t blk = (size_t)ch * CT * nkb + kb;
-    const uint8_t* tp[kNTW];
-    const uint8_t* sp[kNTW];
+    const int blk = ch * CT * nkb + kb;
+    int tp[NTW], sp[NTW];
 #pragma unroll
-    for (int t = 0; t < kNTW; ++t) {
-      tp[t] = tile0[t] + blk * tile_bytes;
-      sp[t] = stile0[t] + blk * 128;
+    for (int t = 0; t < NTW; ++t) {
+      tp[t] = toff0[t] + blk * tile_bytes;
+      sp[t] = soff0[t] + blk * 128;
     }
-    f.load(tp, sp, 0, lane);
+    f.load_buf(wrsrc, tp, sp, lane);
   };
-
-  f32x4 acc[MTC][kNTW];
-  auto zero_acc = [&]() {  // (defined before use below)
+  // L2 prefetch of the weights of flat step s: one dword per lane per 64 B of
+  // each tile-block (so every cache line of it is touched), landing in a
+  // per-wave LDS scratch area that is never read, which costs no registers
+  // and no wait (later waits only need the prefetch done within two blocks)
+  auto prefetch_b = [&](int s) {
+    const int ch = s / nkb, kb = s - ch * nkb;
+    const int blk = ch * CT * nkb + kb;
+    auto* dst = (__attribute__((address_space(3))) void*)(pfbuf + wave * 64);
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst, 4, lane * (tile_bytes / 64), toff0[t] + blk * tile_bytes, 0,
+                                               0);
+      if (WDT == SCR_W_NVFP4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst, 4, lane * 2, soff0[t] + blk * 128, 0, 0);
+    }
+  };
+  auto read_a = [&](bf16x8 (&af)[MTC], const bf16* buf, int st) {
+    const int c = kcol<WDT>(grp, st) >> 3;
 #pragma unroll
     for (int mt = 0; mt < MTC; ++mt)
-#pragma unroll
-      for (int t = 0; t < kNTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      af[mt] = *reinterpret_cast<const bf16x8*>(buf + (mt * 16 + col) * kKB + ((c ^ col) << 3));
   };
-  auto compute = [&](const BFrag<WDT, kNTW>& bc, int buf) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      bf16x8 bf[kNTW];
-#pragma unroll
-      for (int t = 0; t < kNTW; ++t) bf[t] = bc.get(t, st);
-#pragma unroll
-      for (int mt = 0; mt < MTC; ++mt) {
-        const bf16x8 av =
-            *reinterpret_cast<const bf16x8*>(&sm.As[buf][mt * 16 + col][kcol<WDT>(grp, st)]);
-#pragma unroll
-        for (int t = 0; t < kNTW; ++t) acc[mt][t] = mfma16(av, bf[t], acc[mt][t]);
-      }
-    }
-  };
+
+
+  f32x4 acc[MTC][NTW];
+
   auto epilogue = [&](int ch) {
 #pragma unroll
     for (int mt = 0; mt < MTC; ++mt) {
@@ -493,11 +526,11 @@ __device__ __forceinline__ void expert_pass(const GemmArgs& a, ExpSmem<WDT, MT, 
       for (int i = 0; i < 4; ++i) {
         const int pos = m0 + mt * 16 + grp * 4 + i;
         if (GATEUP) {
-          constexpr int HW = 8 * kNTW;  // h columns per wave
+          constexpr int HW = 8 * NTW;  // h columns per wave
 #pragma unroll
-          for (int t = 0; t < kNTW / 2; ++t) {
-            const int hc = ch * (HW * kExpWaves) + wave * HW + 16 * t + col;
-            const float hv = silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + kNTW / 2][i]);
+          for (int t = 0; t < NTW / 2; ++t) {
+            const int hc = ch * (HW * EW) + wave * HW + 16 * t + col;
+            const float hv = silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]);
             a.h[(size_t)pos * a.I + hc] = static_cast<bf16>(hv);
           }
         } else {
@@ -505,9 +538,9 @@ __device__ __forceinline__ void expert_pass(const GemmArgs& a, ExpSmem<WDT, MT, 
           if (r >= 0 && r < a.R) {
             const float w = a.topk_w[r];
             typedef typename RowT<WDT>::type OT;
-            OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + ch * (16 * kNTW * kExpWaves) + wave * 16 * kNTW + col;
+            OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + ch * (16 * NTW * EW) + wave * 16 * NTW + col;
 #pragma unroll
-            for (int t = 0; t < kNTW; ++t) orow[16 * t] = static_cast<OT>(w * (gs * acc[mt][t][i]));
+            for (int t = 0; t < NTW; ++t) orow[16 * t] = static_cast<OT>(w * (gs * acc[mt][t][i]));
             if (ch == 0 && wave == 0 && col == 0) a.flags[r] = 1;
           }
         }
@@ -515,77 +548,116 @@ __device__ __forceinline__ void expert_pass(const GemmArgs& a, ExpSmem<WDT, MT, 
     }
   };
 
-  const int S = nchunks * nkb;  // flat steps s = chunk * nkb + kb
-  constexpr int D = WDT == SCR_W_NVFP4 ? 4 : 2;  // the launcher guarantees nkb % D == 0
-  BFrag<WDT, kNTW> ring[D];
+  // weight ring depth (blocks): HBM latency under load is about two blocks
+  // of compute, so the weights of block s are requested at block s - D + 1
+  constexpr int D = WDT == SCR_W_NVFP4 ? kWideRing : 2;
+  constexpr int U = D > kWideBufs ? D : kWideBufs;  // unroll: ring and buffers indexed statically
+  constexpr int PD = 0;  // weight blocks prefetched ahead into L2 (measured no gain: off)
+  constexpr int NB = BLoads<WDT, NTW>::value;
+  constexpr int NPF = PD > 0 ? (WDT == SCR_W_NVFP4 ? 2 * NTW : NTW) : 0;
+  const int s0 = c_begin * nkb, s1 = c_end * nkb;  // flat steps s = chunk * nkb + kb
+  constexpr int LA = kWideBufs - 1;  // activation blocks loaded ahead
+  BFrag<WDT, NTW> ring[D];
+  // blocks s0 .. s0+LA-1 of the activations, then the weights of blocks
+  // s0 .. s0+D-2
 #pragma unroll
-  for (int i = 0; i < D - 1; ++i) load_b(ring[i], min(i, S - 1));
-  AStage A0;
-  if (ARES) {
-    // the whole K of the bucket's rows, once for all chunks (two blocks in flight)
-    AStage A1;
-    for (int b = 0; b < nkb; b += 2) {
-      load_a(A0, b);
-      if (b + 1 < nkb) load_a(A1, b + 1);
-      store_a(A0, b);
-      if (b + 1 < nkb) store_a(A1, b + 1);
-    }
-  } else {
-    load_a(A0, 0);
-    store_a(A0, 0);
-  }
-  __syncthreads();
-  auto step = [&](int s, int kb, const BFrag<WDT, kNTW>& bc, BFrag<WDT, kNTW>& bl) {
-    if (!ARES) load_a(A0, (s + 1) % nkb);  // next step's activation block
-    load_b(bl, min(s + D - 1, S - 1));
-    compute(bc, ARES ? kb : (s & 1));
-    if (!ARES) {
-      store_a(A0, (s + 1) & 1);
-      __syncthreads();
-    }
-  };
-  for (int ch = 0; ch < nchunks; ++ch) {
-    zero_acc();
-    for (int kb0 = 0; kb0 < nkb; kb0 += D) {
+  for (int i = 0; i < LA; ++i) load_a(bufs[i], i % nkb);
 #pragma unroll
-      for (int i = 0; i < D; ++i) step(ch * nkb + kb0 + i, kb0 + i, ring[i], ring[(i + D - 1) % D]);
+  for (int i = 0; i < D - 1; ++i) load_b(ring[i], min(s0 + i, s1 - 1));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((LA - 1) * NA + (D - 1) * NB));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  bf16x8 af[MTC];
+  for (int ch = c_begin; ch < c_end; ++ch) {
+#pragma unroll
+    for (int mt = 0; mt < MTC; ++mt)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb0 = 0; kb0 < nkb; kb0 += U) {
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int kb = kb0 + i, s = ch * nkb + kb;
+        const BFrag<WDT, NTW>& bc = ring[i % D];
+        const bf16* buf = bufs[i % kWideBufs];
+        // the activations of block kb + LA into the buffer block kb - 1 used
+        // (every wave has finished it), then the weights of block s + D - 1
+        // into the ring slot block s - 1 used
+        load_a(bufs[(i + LA) % kWideBufs], (kb + LA) % nkb);
+        load_b(ring[(i + D - 1) % D], min(s + D - 1, s1 - 1));
+        if (PD > 0) prefetch_b(min(s + PD, s1 - 1));
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          read_a(af, buf, st);
+          // one weight tile at a time: its decode, then its MTC products
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) {
+            const bf16x8 bt = bc.get_hw(t, st);
+#pragma unroll
+            for (int mt = 0; mt < MTC; ++mt) acc[mt][t] = mfma16(af[mt], bt, acc[mt][t]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the next block's activations (issued LA - 1 blocks ago) are in LDS
+        // once at most the loads issued after them are pending: in steady
+        // state weights (+ prefetch) of LA blocks and activations of LA - 1;
+        // right after the prologue (which issued D - 1 weight blocks behind
+        // the activations) possibly fewer weights, so the smaller count
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((LA - 1) * NA + (D < LA ? D : LA) * NB + NPF));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     epilogue(ch);
   }
+  // no direct load may still target the buffers when the next pass refills them
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
 }
 
-template <int WDT, int MT, bool GATEUP, bool ARES>
-__global__ __launch_bounds__(kExpThreads) void moe_expert_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) ExpSmem<WDT, MT, GATEUP, ARES> sm;
-  // XCD-aware order: bucket j runs on XCD j mod 8
-  const int bid = blockIdx.x, j = 8 * (bid >> 3) + (bid & 7);
+template <int WDT, int MT, bool GATEUP, int EW, int NTW>
+__global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int groups) {
+  __shared__ __attribute__((aligned(1024))) bf16 As0[MT * 16 * kKB];
+  __shared__ __attribute__((aligned(1024))) bf16 As1[MT * 16 * kKB];
+  __shared__ __attribute__((aligned(1024))) bf16 As2[MT * 16 * kKB];
+  __shared__ __attribute__((aligned(1024))) bf16 As3[MT * 16 * kKB];
+  __shared__ int src_row[MT * 16];
+  __shared__ __attribute__((aligned(256))) uint32_t pfbuf[EW * 64];  // prefetch landing area, never read
+  // XCD-aware order: all groups of bucket j run on XCD j mod 8
+  const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
+  const int j = 8 * (q / groups) + xcd, g = q % groups;
   if (j >= *a.n_active) return;
   const int b = a.active_buckets[j];
   const int p0 = a.active_block_begin[j] * a.B, p1 = a.active_block_begin[j + 1] * a.B;
   if (p1 > a.h_rows || p0 >= p1) return;
+  constexpr int kThreads = 64 * EW;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int K = GATEUP ? a.H : a.I;
   const int nkb = K / kKB;
-  const int nchunks = GATEUP ? a.I / (8 * kNTW * kExpWaves) : a.H / (16 * kNTW * kExpWaves);
+  const int nchunks = GATEUP ? a.I / (8 * NTW * EW) : a.H / (16 * NTW * EW);
+  const int c_begin = g * nchunks / groups, c_end = (g + 1) * nchunks / groups;
+  if (c_begin >= c_end) return;
   const uint8_t* rec = static_cast<const uint8_t*>(a.bucket_rows[b]);
-  constexpr size_t tile_bytes = WDT == SCR_W_NVFP4 ? 1024 : 4096;
-  // tile-block (t, 0) of this wave's tiles in chunk 0
-  const uint8_t* tile0[kNTW];
-  const uint8_t* stile0[kNTW];
+  // the record as a buffer (every weight load is range-checked against it)
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, (int)a.lay.record_bytes, 0x00020000);
+  constexpr int tile_bytes = WDT == SCR_W_NVFP4 ? 1024 : 4096;
+  // byte offsets of tile-block (t, 0) of this wave's tiles in chunk 0 (wave-uniform)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  int toff0[NTW], soff0[NTW];
 #pragma unroll
-  for (int t = 0; t < kNTW; ++t) {
-    const int row0 = GATEUP ? (t < kNTW / 2 ? 0 : a.I) + wave * 8 * kNTW + 16 * (t % (kNTW / 2))
-                            : wave * 16 * kNTW + 16 * t;
-    const size_t tb = (size_t)(row0 / 16) * nkb;
-    tile0[t] = rec + (GATEUP ? a.lay.w13_off : a.lay.w2_off) + tb * tile_bytes;
-    stile0[t] = rec + (GATEUP ? a.lay.w13_scale_off : a.lay.w2_scale_off) + tb * 128;
+  for (int t = 0; t < NTW; ++t) {
+    const int row0 = GATEUP ? (t < NTW / 2 ? 0 : a.I) + wv * 8 * NTW + 16 * (t % (NTW / 2)) : wv * 16 * NTW + 16 * t;
+    const int tb = (row0 / 16) * nkb;
+    toff0[t] = (int)(GATEUP ? a.lay.w13_off : a.lay.w2_off) + tb * tile_bytes;
+    soff0[t] = (int)(GATEUP ? a.lay.w13_scale_off : a.lay.w2_scale_off) + tb * 128;
   }
   const float gs = WDT == SCR_W_NVFP4
                        ? *reinterpret_cast<const float*>(rec + (GATEUP ? a.lay.g13_off : a.lay.g2_off))
                        : 1.0f;
   for (int m0 = p0; m0 < p1; m0 += MT * 16) {
     const int rows = min(MT * 16, p1 - m0);
-    for (int i = tid; i < MT * 16; i += kExpThreads) {
+    for (int i = tid; i < MT * 16; i += kThreads) {
       int off = -1;
       if (i < rows) {
         if (GATEUP) {
@@ -595,19 +667,28 @@ __global__ __launch_bounds__(kExpThreads) void moe_expert_kernel(GemmArgs a) {
           off = (m0 + i) * K;
         }
       }
-      sm.src_row[i] = off;
+      src_row[i] = off;
     }
     __syncthreads();
+#define SCR_WIDE_PASS(n)                                                                                   \
+  case n:                                                                                                  \
+    if constexpr (MT >= n)                                                                                 \
+      wide_pass<WDT, MT, GATEUP, EW, NTW, n>(a, src_row, As0, As1, As2, As3, pfbuf, m0, wrsrc, toff0, soff0, \
+                                             gs, nkb, c_begin, c_end);                                          \
+    break;
     switch (rows / 16) {
-      case 1: expert_pass<WDT, MT, GATEUP, ARES, 1>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
-      case 2: if constexpr (MT >= 2) expert_pass<WDT, MT, GATEUP, ARES, 2>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
-      case 3: if constexpr (MT >= 3) expert_pass<WDT, MT, GATEUP, ARES, 3>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
-      case 4: if constexpr (MT >= 4) expert_pass<WDT, MT, GATEUP, ARES, 4>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
-      case 5: if constexpr (MT >= 5) expert_pass<WDT, MT, GATEUP, ARES, 5>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
-      case 6: if constexpr (MT >= 6) expert_pass<WDT, MT, GATEUP, ARES, 6>(a, sm, m0, tile0, stile0, gs, nkb, nchunks); break;
+      SCR_WIDE_PASS(1)
+      SCR_WIDE_PASS(2)
+      SCR_WIDE_PASS(3)
+      SCR_WIDE_PASS(4)
+      SCR_WIDE_PASS(5)
+      SCR_WIDE_PASS(6)
+      SCR_WIDE_PASS(7)
+      SCR_WIDE_PASS(8)
       default: break;
     }
-    __syncthreads();  // src_row and As are reused by the next pass
+#undef SCR_WIDE_PASS
+    __syncthreads();  // src_row is reused by the next pass
   }
 }
 
@@ -704,27 +785,37 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
   return w;
 }
 
-template <int WDT, int MT>
-static bool expert_gemms_fit(const GemmArgs& a) {
-  constexpr int D = WDT == SCR_W_NVFP4 ? 4 : 2;
-  return (a.H / kKB) % D == 0 && (a.I / kKB) % D == 0 && a.I % (8 * kNTW * kExpWaves) == 0 &&
-         a.H % (16 * kNTW * kExpWaves) == 0;
+constexpr int kWideWaves = 8;  // two waves per SIMD in one workgroup per CU
+template <int WDT>
+struct WideNT {  // row tiles per wave: the bf16 weight ring holds four times the registers
+  static constexpr int value = WDT == SCR_W_NVFP4 ? 4 : 2;
+};
+
+template <int WDT>
+static bool wide_gemms_fit(const GemmArgs& a) {
+  constexpr int NTW = WideNT<WDT>::value;
+  // K blocks cycle through the LDS buffers and the weight ring in steps of U
+  constexpr int U = WDT == SCR_W_NVFP4 ? (kWideRing > kWideBufs ? kWideRing : kWideBufs) : kWideBufs;
+  return (a.H / kKB) % U == 0 && (a.I / kKB) % U == 0 && a.I % (8 * NTW * kWideWaves) == 0 &&
+         a.H % (16 * NTW * kWideWaves) == 0;
 }
 
-// many rows per expert: gate/up as (bucket, N tile) workgroups (measured
-// faster for the long K = H loop), down as one expert-persistent workgroup per
-// bucket with its h rows resident in LDS
+// many rows per expert: both GEMMs as wide-tile workgroups, each walking a
+// contiguous range of one bucket's N chunks (gate/up: one chunk of 128 h
+// columns; down: two chunks of 256 output columns)
 template <int WDT, int MT>
-static int launch_expert_gemms(const GemmArgs& a, int max_active, hipEvent_t* marks, hipStream_t s) {
-  const int grid = 8 * ((max_active + 7) / 8);
-  const int ntx_gu = (a.I + 4 * 8 * 2 - 1) / (4 * 8 * 2);
-  hipLaunchKernelGGL((moe_gemm_kernel<WDT, MT, 2, true>), dim3(grid * ntx_gu), dim3(kGemmThreads), 0, s, a, ntx_gu);
+static int launch_wide_gemms(const GemmArgs& a, int max_active, hipEvent_t* marks, hipStream_t s) {
+  constexpr int NTW = WideNT<WDT>::value;
+  const int rows8 = (max_active + 7) / 8;  // buckets per XCD (rounded up)
+  const int g_gu = a.I / (8 * NTW * kWideWaves);
+  const int nch_dn = a.H / (16 * NTW * kWideWaves);
+  const int g_dn = nch_dn >= 2 ? nch_dn / 2 : 1;  // two chunks per workgroup
+  hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, true, kWideWaves, NTW>), dim3(8 * rows8 * g_gu), dim3(64 * kWideWaves),
+                     0, s, a, g_gu);
   SCR_CHECK_LAUNCH();
   if (marks && marks[2]) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
-  if (a.I / kKB <= kResMaxKB)
-    hipLaunchKernelGGL((moe_expert_kernel<WDT, MT, false, true>), dim3(grid), dim3(kExpThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((moe_expert_kernel<WDT, MT, false, false>), dim3(grid), dim3(kExpThreads), 0, s, a);
+  hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, false, kWideWaves, NTW>), dim3(8 * rows8 * g_dn), dim3(64 * kWideWaves),
+                     0, s, a, g_dn);
   SCR_CHECK_LAUNCH();
   if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
   return SCR_OK;
@@ -758,7 +849,9 @@ extern "C" int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_c
   // few rows per expert: small M passes and narrow N tiles (more workgroups to
   // stream weights); many rows: 128-row passes and wide N tiles (MFMA reuse)
   const bool small = per_expert <= 16;
-  cfg->m_chunk = small ? 32 : 96;
+  // NVFP4 passes hold 96 rows (the deeper weight ring of its wide kernel
+  // takes the registers of a seventh row tile), bf16 passes 112
+  cfg->m_chunk = small ? 32 : 112;
   cfg->n_tile_gu = 4 * 8 * 2;    // h columns per workgroup
   cfg->n_tile_dn = 4 * 16 * 2;   // output columns per workgroup
   cfg->wdtype = wdtype;
@@ -836,12 +929,12 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   const int max_active = R < E ? R : E;
   if (view->wdtype == SCR_W_BF16) {
     rc = cfg.m_chunk == 32                              ? scr::launch_gemms<SCR_W_BF16, 2, 2>(a, max_active, marks, stream)
-         : scr::expert_gemms_fit<SCR_W_BF16, 6>(a) ? scr::launch_expert_gemms<SCR_W_BF16, 6>(a, max_active, marks, stream)
-                                                    : scr::launch_gemms<SCR_W_BF16, 6, 2>(a, max_active, marks, stream);
+         : scr::wide_gemms_fit<SCR_W_BF16>(a)      ? scr::launch_wide_gemms<SCR_W_BF16, 7>(a, max_active, marks, stream)
+                                                    : scr::launch_gemms<SCR_W_BF16, 7, 2>(a, max_active, marks, stream);
   } else {
     rc = cfg.m_chunk == 32                               ? scr::launch_gemms<SCR_W_NVFP4, 2, 2>(a, max_active, marks, stream)
-         : scr::expert_gemms_fit<SCR_W_NVFP4, 6>(a) ? scr::launch_expert_gemms<SCR_W_NVFP4, 6>(a, max_active, marks, stream)
-                                                     : scr::launch_gemms<SCR_W_NVFP4, 6, 2>(a, max_active, marks, stream);
+         : scr::wide_gemms_fit<SCR_W_NVFP4>(a)      ? scr::launch_wide_gemms<SCR_W_NVFP4, 7>(a, max_active, marks, stream)
+                                                     : scr::launch_gemms<SCR_W_NVFP4, 7, 2>(a, max_active, marks, stream);
   }
   if (rc) return rc;
 

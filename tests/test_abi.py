@@ -43,7 +43,7 @@ def test_tile_config_depends_on_the_layer_only(lib):
     a = L.tile_config(600, 2, 8, L.SCR_W_BF16).as_tuple()
     assert a == L.tile_config(600, 2, 8, L.SCR_W_BF16).as_tuple()
     assert L.tile_config(96, 10, 512, L.SCR_W_BF16).m_chunk == 32      # ~2 rows per expert
-    assert L.tile_config(4096, 10, 512, L.SCR_W_NVFP4).m_chunk == 96   # ~80 rows per expert
+    assert L.tile_config(4096, 10, 512, L.SCR_W_NVFP4).m_chunk == 112  # ~80 rows per expert
 
 
 def test_record_layouts(lib):

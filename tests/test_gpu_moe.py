@@ -162,7 +162,10 @@ def test_layer_view_one_layer_cache_three_per_query():
     assert torch.equal(d["y"], st["y"])
 
 
-@pytest.mark.parametrize("T,E,k,H,I", [(64, 16, 4, 256, 128), (200, 32, 6, 512, 256), (37, 8, 3, 256, 128)])
+# the last two take the wide-tile kernels (I = 512, many rows per expert; at
+# 1500 routes over 12 experts some buckets need a second M pass)
+@pytest.mark.parametrize("T,E,k,H,I", [(64, 16, 4, 256, 128), (200, 32, 6, 512, 256), (37, 8, 3, 256, 128),
+                                       (384, 16, 4, 512, 512), (500, 12, 3, 1024, 512)])
 def test_nvfp4_layer_vs_oracle_and_stream(T, E, k, H, I):
     s = _setup(f"fp4_{T}_{E}", S=2 * E, W_=8, wdtype="nvfp4", T=T, E=E, k=k, H=H, I=I, NL=2)
     bank = _bank_for(s)
@@ -185,6 +188,21 @@ def test_bf16_ragged_shapes_vs_oracle():
     d = _run_demand(s, bank, sc)
     y_ref, _, _ = _oracle(s)
     assert rel_max_err(_y(d), y_ref) <= TOL_BF16
+    st = _run_stream(s, sc)
+    assert torch.equal(d["y"], st["y"])
+
+
+def test_bf16_wide_tiles_vs_oracle():
+    # about 96 rows per expert with I = 512: the wide-tile kernels in bf16
+    s = _setup("wide_bf16", S=40, W_=16, wdtype="bf16", T=384, E=16, k=4, H=512, I=512, NL=2)
+    bank = _bank_for(s)
+    sc = np.ones(s["E"], np.float32)
+    d = _run_demand(s, bank, sc)
+    assert d.cfg_used.m_chunk == 112
+    y_ref, _, _ = _oracle(s)
+    err = rel_max_err(_y(d), y_ref)
+    flush(f"bf16 wide 384x16: rel max err = {err:.3e}")
+    assert err <= TOL_BF16
     st = _run_stream(s, sc)
     assert torch.equal(d["y"], st["y"])
 
