@@ -36,6 +36,20 @@ template <typename T>
 __device__ __forceinline__ T ldg(const void* p) {
   return *(const __attribute__((address_space(1))) T*)(p);
 }
+// the same as a nontemporal (streaming) load
+template <typename T>
+__device__ __forceinline__ T ldg_nt(const void* p) {
+  return __builtin_nontemporal_load((const __attribute__((address_space(1))) T*)(p));
+}
+template <bool NT, typename T>
+__device__ __forceinline__ T ldg_w(const void* p) {
+  if constexpr (NT) return ldg_nt<T>(p);
+  else return ldg<T>(p);
+}
+
+// cache policy of the buffer loads of weights: nontemporal (each weight byte
+// is read once per pass; keeping it out of the caches' way measured faster)
+constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -141,12 +155,13 @@ struct BFrag;
 template <int NT>
 struct BFrag<SCR_W_BF16, NT> {
   u32x4 raw[NT][4];
+  template <bool STREAM = false>
   __device__ __forceinline__ void load(const uint8_t* const* tile, const uint8_t* const*, int kb, int lane) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int st = 0; st < 4; ++st)
-        raw[t][st] = ldg<u32x4>(tile[t] + (size_t)kb * 4096 + st * 1024 + lane * 16);
+        raw[t][st] = ldg_w<STREAM, u32x4>(tile[t] + (size_t)kb * 4096 + st * 1024 + lane * 16);
   }
   // through a buffer resource: the wave-uniform tile offsets go in scalar
   // registers, the per-lane part is the constant lane * 16
@@ -154,7 +169,8 @@ struct BFrag<SCR_W_BF16, NT> {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int st = 0; st < 4; ++st) raw[t][st] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, toff[t] + st * 1024, 0);
+      for (int st = 0; st < 4; ++st)
+        raw[t][st] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, toff[t] + st * 1024, kNonTemporal);
   }
   __device__ __forceinline__ bf16x8 get(int t, int st) const { return __builtin_bit_cast(bf16x8, raw[t][st]); }
   __device__ __forceinline__ bf16x8 get_hw(int t, int st) const { return get(t, st); }
@@ -164,18 +180,19 @@ template <int NT>
 struct BFrag<SCR_W_NVFP4, NT> {
   u32x4 codes[NT];  // 32 codes: step s uses dword s
   unsigned sc[NT];  // two scale codes: low byte for codes 0..15, next for 16..31
+  template <bool STREAM = false>
   __device__ __forceinline__ void load(const uint8_t* const* tile, const uint8_t* const* stile, int kb, int lane) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      codes[t] = ldg<u32x4>(tile[t] + (size_t)kb * 1024 + lane * 16);
-      sc[t] = ldg<unsigned short>(stile[t] + (size_t)kb * 128 + lane * 2);
+      codes[t] = ldg_w<STREAM, u32x4>(tile[t] + (size_t)kb * 1024 + lane * 16);
+      sc[t] = ldg_w<STREAM, unsigned short>(stile[t] + (size_t)kb * 128 + lane * 2);
     }
   }
   __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, const int* toff, const int* soff, int lane) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      codes[t] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, toff[t], 0);
-      sc[t] = __builtin_amdgcn_raw_buffer_load_b16(r, lane * 2, soff[t], 0);
+      codes[t] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, toff[t], kNonTemporal);
+      sc[t] = __builtin_amdgcn_raw_buffer_load_b16(r, lane * 2, soff[t], kNonTemporal);
     }
   }
   __device__ __forceinline__ bf16x8 get(int t, int st) const {
@@ -238,7 +255,9 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
       *reinterpret_cast<u32x4*>(base + adst[u]) = avalid[u] ? st.v[u] : z;
     }
   };
-  auto load_b = [&](BFrag<WDT, NT>& f, int kb) { f.load(rowp, scp, kb, c.lane); };
+  // gate/up streams its weights with nontemporal loads (measured faster);
+  // down, with fewer rows per weight byte, measured slower that way
+  auto load_b = [&](BFrag<WDT, NT>& f, int kb) { f.template load<GATEUP>(rowp, scp, kb, c.lane); };
 
   f32x4 acc[MTC][NT];
 #pragma unroll
@@ -428,6 +447,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
 // from the direct loads still in flight into the other.
 constexpr int kWideBufs = 4;  // activation K-block buffers in LDS (loaded kWideBufs - 1 blocks ahead)
 constexpr int kWideRing = 2;  // NVFP4 weight ring depth in K blocks (deeper measured slower)
+constexpr int kWideStage = 4096;  // bytes of LDS per wave for the epilogue tile (16 rows x 64 fp32)
 
 // s_waitcnt immediate that waits until at most n vector memory operations are
 // outstanding (gfx9 encoding; the LDS and export counters are left alone)
@@ -442,7 +462,7 @@ struct BLoads {  // vector memory instructions per wave for one K block of weigh
 
 template <int WDT, int MT, bool GATEUP, int EW, int NTW, int MTC>
 __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row, bf16* As0, bf16* As1, bf16* As2,
-                                          bf16* As3, uint32_t* pfbuf, int m0, __amdgpu_buffer_rsrc_t wrsrc,
+                                          bf16* As3, uint32_t* stg, int m0, __amdgpu_buffer_rsrc_t wrsrc,
                                           const int* toff0, const int* soff0, float gs, int nkb, int c_begin,
                                           int c_end) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -493,22 +513,6 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
     }
     f.load_buf(wrsrc, tp, sp, lane);
   };
-  // L2 prefetch of the weights of flat step s: one dword per lane per 64 B of
-  // each tile-block (so every cache line of it is touched), landing in a
-  // per-wave LDS scratch area that is never read, which costs no registers
-  // and no wait (later waits only need the prefetch done within two blocks)
-  auto prefetch_b = [&](int s) {
-    const int ch = s / nkb, kb = s - ch * nkb;
-    const int blk = ch * CT * nkb + kb;
-    auto* dst = (__attribute__((address_space(3))) void*)(pfbuf + wave * 64);
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst, 4, lane * (tile_bytes / 64), toff0[t] + blk * tile_bytes, 0,
-                                               0);
-      if (WDT == SCR_W_NVFP4)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, dst, 4, lane * 2, soff0[t] + blk * 128, 0, 0);
-    }
-  };
   auto read_a = [&](bf16x8 (&af)[MTC], const bf16* buf, int st) {
     const int c = kcol<WDT>(grp, st) >> 3;
 #pragma unroll
@@ -519,29 +523,62 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
 
   f32x4 acc[MTC][NTW];
 
+  // Epilogue through a per-wave LDS tile: the outputs of one 16-row tile are
+  // written to LDS in the MFMA layout and read back as 16-byte row pieces,
+  // so that each global store writes whole row segments (gate/up: 64 bytes
+  // of h per row and wave; down: a row's 64 output columns, one or two cache
+  // lines) instead of scattered 2- and 4-byte values.
+  uint32_t* const wst = stg + wave * (kWideStage / 4);
   auto epilogue = [&](int ch) {
+    if (GATEUP) {
+      constexpr int HC = 8 * NTW;                  // h columns per wave
+      constexpr int PPR = HC / 8;                  // 16-byte pieces per row
+      constexpr int ROUNDS = (16 * PPR + 63) / 64;  // store rounds for 16 rows
+      bf16* sh = reinterpret_cast<bf16*>(wst);
 #pragma unroll
-    for (int mt = 0; mt < MTC; ++mt) {
+      for (int mt = 0; mt < MTC; ++mt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int pos = m0 + mt * 16 + grp * 4 + i;
-        if (GATEUP) {
-          constexpr int HW = 8 * NTW;  // h columns per wave
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int t = 0; t < NTW / 2; ++t) {
-            const int hc = ch * (HW * EW) + wave * HW + 16 * t + col;
-            const float hv = silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]);
-            a.h[(size_t)pos * a.I + hc] = static_cast<bf16>(hv);
+          for (int t = 0; t < NTW / 2; ++t)
+            sh[(grp * 4 + i) * HC + 16 * t + col] =
+                static_cast<bf16>(silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]));
+#pragma unroll
+        for (int rd = 0; rd < ROUNDS; ++rd) {
+          const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
+          if (q < 16 * PPR) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(sh + rr * HC + pc * 8);
+            const int pos = m0 + mt * 16 + rr;
+            const int hc = ch * (HC * EW) + wave * HC + pc * 8;
+            *reinterpret_cast<u32x4*>(a.h + (size_t)pos * a.I + hc) = v;
           }
-        } else {
-          const int r = a.sorted_routes[pos];
-          if (r >= 0 && r < a.R) {
-            const float w = a.topk_w[r];
-            typedef typename RowT<WDT>::type OT;
-            OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + ch * (16 * NTW * EW) + wave * 16 * NTW + col;
+        }
+      }
+    } else {
+      typedef typename RowT<WDT>::type OT;
+      constexpr int OC = 16 * NTW;                  // output columns per wave
+      constexpr int EPP = 16 / (int)sizeof(OT);     // elements per 16-byte piece
+      constexpr int PPR = OC / EPP;                 // pieces per row
+      constexpr int ROUNDS = (16 * PPR + 63) / 64;  // store rounds for 16 rows
+      OT* so = reinterpret_cast<OT*>(wst);
 #pragma unroll
-            for (int t = 0; t < NTW; ++t) orow[16 * t] = static_cast<OT>(w * (gs * acc[mt][t][i]));
-            if (ch == 0 && wave == 0 && col == 0) a.flags[r] = 1;
+      for (int mt = 0; mt < MTC; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = a.sorted_routes[m0 + mt * 16 + grp * 4 + i];
+          const float w = (r >= 0 && r < a.R) ? a.topk_w[r] : 0.0f;
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) so[(grp * 4 + i) * OC + 16 * t + col] = static_cast<OT>(w * (gs * acc[mt][t][i]));
+        }
+#pragma unroll
+        for (int rd = 0; rd < ROUNDS; ++rd) {
+          const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(so + (q < 16 * PPR ? rr : 0) * OC + pc * EPP);
+          const int r = q < 16 * PPR ? a.sorted_routes[m0 + mt * 16 + rr] : -1;
+          if (r >= 0 && r < a.R) {
+            OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + ch * (OC * EW) + wave * OC + pc * EPP;
+            *reinterpret_cast<u32x4*>(orow) = v;
+            if (ch == 0 && wave == 0 && pc == 0) a.flags[r] = 1;
           }
         }
       }
@@ -552,19 +589,25 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
   // of compute, so the weights of block s are requested at block s - D + 1
   constexpr int D = WDT == SCR_W_NVFP4 ? kWideRing : 2;
   constexpr int U = D > kWideBufs ? D : kWideBufs;  // unroll: ring and buffers indexed statically
-  constexpr int PD = 0;  // weight blocks prefetched ahead into L2 (measured no gain: off)
   constexpr int NB = BLoads<WDT, NTW>::value;
-  constexpr int NPF = PD > 0 ? (WDT == SCR_W_NVFP4 ? 2 * NTW : NTW) : 0;
   const int s0 = c_begin * nkb, s1 = c_end * nkb;  // flat steps s = chunk * nkb + kb
   constexpr int LA = kWideBufs - 1;  // activation blocks loaded ahead
   BFrag<WDT, NTW> ring[D];
-  // blocks s0 .. s0+LA-1 of the activations, then the weights of blocks
-  // s0 .. s0+D-2
+  // Down (K = I = kWideBufs blocks) keeps the bucket's whole h block resident
+  // for all of its chunks: loaded once, no further activation loads or
+  // barriers.  Gate/up streams x blocks LA ahead through the buffers.
+  const bool resident = !GATEUP && nkb == kWideBufs;
+  // blocks s0 .. s0+LA-1 of the activations (all of them when resident),
+  // then the weights of blocks s0 .. s0+D-2
 #pragma unroll
   for (int i = 0; i < LA; ++i) load_a(bufs[i], i % nkb);
+  if (resident) load_a(bufs[LA], LA);
 #pragma unroll
   for (int i = 0; i < D - 1; ++i) load_b(ring[i], min(s0 + i, s1 - 1));
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((LA - 1) * NA + (D - 1) * NB));
+  if (resident)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * NB));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((LA - 1) * NA + (D - 1) * NB));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
@@ -583,9 +626,8 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
         // the activations of block kb + LA into the buffer block kb - 1 used
         // (every wave has finished it), then the weights of block s + D - 1
         // into the ring slot block s - 1 used
-        load_a(bufs[(i + LA) % kWideBufs], (kb + LA) % nkb);
+        if (!resident) load_a(bufs[(i + LA) % kWideBufs], (kb + LA) % nkb);
         load_b(ring[(i + D - 1) % D], min(s + D - 1, s1 - 1));
-        if (PD > 0) prefetch_b(min(s + PD, s1 - 1));
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
           read_a(af, buf, st);
@@ -598,14 +640,16 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // the next block's activations (issued LA - 1 blocks ago) are in LDS
-        // once at most the loads issued after them are pending: in steady
-        // state weights (+ prefetch) of LA blocks and activations of LA - 1;
-        // right after the prologue (which issued D - 1 weight blocks behind
-        // the activations) possibly fewer weights, so the smaller count
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((LA - 1) * NA + (D < LA ? D : LA) * NB + NPF));
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        if (!resident) {
+          // the next block's activations (issued LA - 1 blocks ago) are in
+          // LDS once at most the loads issued after them are pending: in
+          // steady state weights of LA blocks and activations of LA - 1;
+          // right after the prologue (which issued D - 1 weight blocks behind
+          // the activations) possibly fewer weights, so the smaller count
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm((LA - 1) * NA + (D < LA ? D : LA) * NB));
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     epilogue(ch);
@@ -622,7 +666,7 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
   __shared__ __attribute__((aligned(1024))) bf16 As2[MT * 16 * kKB];
   __shared__ __attribute__((aligned(1024))) bf16 As3[MT * 16 * kKB];
   __shared__ int src_row[MT * 16];
-  __shared__ __attribute__((aligned(256))) uint32_t pfbuf[EW * 64];  // prefetch landing area, never read
+  __shared__ __attribute__((aligned(256))) uint32_t stg[EW * kWideStage / 4];  // per-wave epilogue tiles
   // XCD-aware order: all groups of bucket j run on XCD j mod 8
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
   const int j = 8 * (q / groups) + xcd, g = q % groups;
@@ -673,7 +717,7 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
 #define SCR_WIDE_PASS(n)                                                                                   \
   case n:                                                                                                  \
     if constexpr (MT >= n)                                                                                 \
-      wide_pass<WDT, MT, GATEUP, EW, NTW, n>(a, src_row, As0, As1, As2, As3, pfbuf, m0, wrsrc, toff0, soff0, \
+      wide_pass<WDT, MT, GATEUP, EW, NTW, n>(a, src_row, As0, As1, As2, As3, stg, m0, wrsrc, toff0, soff0,   \
                                              gs, nkb, c_begin, c_end);                                          \
     break;
     switch (rows / 16) {
