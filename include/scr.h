@@ -290,9 +290,11 @@ int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cf
  *   a_scale_out device f32 [1], nullable: max of the layer's input scales
  *               (what an activation-quantising GEMM would quantise under)
  *   marks       host array of 5 events or NULL: recorded on `stream` before
- *               the prologue and after the prologue, gate/up, down and
- *               combine kernels (per-kernel timing on the launching stream);
- *               NULL entries are skipped
+ *               the launches, again before gate/up (which also clears the
+ *               per-route flags and reports a_scale, so marks 0 and 1 bracket
+ *               nothing), and after the gate/up, down and combine kernels
+ *               (per-kernel timing on the launching stream); NULL entries
+ *               are skipped
  * H % 128 == 0, I % 128 == 0, 128 <= H, I <= 16384 (the GEMM's K block is 128). */
 int scr_grouped_moe_forward(const scr_routed_experts* view, const void* x, int T,
                             const float* topk_w, const int32_t* sorted_routes,

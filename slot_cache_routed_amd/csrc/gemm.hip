@@ -89,8 +89,26 @@ struct GemmArgs {
   bf16* h;              // [h_rows][I]
   void* o;              // [R][H] per-route weighted expert outputs (RowT<WDT>)
   int32_t* flags;       // [R]
-  int T, k, R, H, I, B, h_rows;
+  const float* input_scale;  // [E] the layer's activation scales
+  float* a_scale_out;        // nullable, device
+  int T, k, R, H, I, B, h_rows, E;
 };
+
+// Work that must precede the down GEMM, done by the gate/up workgroups before
+// anything else (so that it costs no launch of its own): clear the per-route
+// written flags that down sets, and report the layer's activation scale
+// (the max of its input scales) from the first wave of workgroup 0.
+__device__ __forceinline__ void gateup_prologue(const GemmArgs& a) {
+  const int nthreads = gridDim.x * blockDim.x;
+  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < a.R; r += nthreads) a.flags[r] = 0;
+  if (a.a_scale_out && blockIdx.x == 0 && threadIdx.x < 64) {
+    float m = -INFINITY;
+    for (int e = threadIdx.x; e < a.E; e += 64) m = fmaxf(m, a.input_scale[e]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (threadIdx.x == 0) *a.a_scale_out = m;
+  }
+}
 
 // silu(g) * u with the hardware exp2 and reciprocal (about 1 ulp each)
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -347,6 +365,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
 
   // XCD-aware order: consecutive workgroups go to different XCDs, so bucket j
   // and all its N tiles land on XCD (j mod 8) and share its L2
+  if (GATEUP) gateup_prologue(a);
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
   const int j = 8 * (q / ntx) + xcd;
   const int tx = q % ntx;
@@ -667,6 +686,7 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
   __shared__ __attribute__((aligned(1024))) bf16 As3[MT * 16 * kKB];
   __shared__ int src_row[MT * 16];
   __shared__ __attribute__((aligned(256))) uint32_t stg[EW * kWideStage / 4];  // per-wave epilogue tiles
+  if (GATEUP) gateup_prologue(a);
   // XCD-aware order: all groups of bucket j run on XCD j mod 8
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
   const int j = 8 * (q / groups) + xcd, g = q % groups;
@@ -736,26 +756,6 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
   }
 }
 
-// clears the per-route written flags and reports the layer's activation scale
-__global__ __launch_bounds__(256) void prologue_kernel(int32_t* __restrict__ flags, int R,
-                                                       const float* __restrict__ input_scale, int E,
-                                                       float* __restrict__ a_scale_out) {
-  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < R; r += gridDim.x * blockDim.x) flags[r] = 0;
-  if (a_scale_out && blockIdx.x == 0) {
-    __shared__ float red[256];
-    float m = -INFINITY;
-    for (int e = threadIdx.x; e < E; e += blockDim.x) m = fmaxf(m, input_scale[e]);
-    red[threadIdx.x] = m;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-      if ((int)threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) *a_scale_out = red[0];
-  }
-}
-
-// y[t][c] = sum_j o[t*k + j][c] in rank order (unwritten routes count as zero)
 // y[t][c] = sum_j o[t*k + j][c] in rank order j, in fp32 (unwritten routes
 // count as zero); 8 columns per thread
 __device__ __forceinline__ void load_row8(const float* p, float* v) {
@@ -961,12 +961,12 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   a.B = cfg.block_m;
   a.h_rows = wl.h_rows;
 
+  a.input_scale = view->input_scale;
+  a.a_scale_out = a_scale_out;
+  a.E = E;
+  // marks[0] and marks[1] bracket the (now empty) prologue: the gate/up
+  // kernel clears the flags and reports the activation scale itself
   if (marks && marks[0]) SCR_CHECK_HIP(hipEventRecord(marks[0], stream));
-  int pgrid = (R + 255) / 256;
-  if (pgrid > 256) pgrid = 256;
-  hipLaunchKernelGGL(scr::prologue_kernel, dim3(pgrid), dim3(256), 0, stream, a.flags, R, view->input_scale, E,
-                     a_scale_out);
-  SCR_CHECK_LAUNCH();
   if (marks && marks[1]) SCR_CHECK_HIP(hipEventRecord(marks[1], stream));
 
   // the grid covers at most min(R, E_layer) active buckets: a layer size

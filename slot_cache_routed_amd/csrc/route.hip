@@ -10,10 +10,22 @@
 
 namespace scr {
 
-// Lane l holds logits l, l+64, l+128, ... (VPL of them, E <= 64*VPL).  Each of
-// the k rounds takes every lane's best untaken value, then a butterfly over
-// the wave keeps the larger value (lower id on ties); the owning lane marks
-// it taken.  Lane j keeps the j-th selection.
+// float -> u32 with the same order (non-NaN inputs; -0 is first made +0, so
+// that equal logits compare equal) and back
+__device__ __forceinline__ unsigned ordered_key(float f) {
+  const unsigned u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Lane l holds logits l, l+64, l+128, ... (VPL of them, E <= 64*VPL) as
+// ordered keys (every finite or infinite key is above 0, the "taken" mark).
+// Each of the k rounds takes every lane's best untaken key (lowest id on
+// ties), the wave's largest key, then among the lanes holding it the lowest
+// id, both as DPP reductions; the owning lane marks it taken.  Lane j keeps
+// the j-th selection.
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                     int k, int32_t* __restrict__ ids,
@@ -22,47 +34,46 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
-  float v[VPL];
+  unsigned key[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + kWave * i;
-    v[i] = e < E ? row[e] : 0.0f;
+    key[i] = e < E ? ordered_key(row[e]) : 0u;
   }
-  uint64_t taken = 0;
-  float my_val = 0.0f;
+  unsigned my_key = 0u;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    unsigned lk = 0u;
+    unsigned li = 0xffffffffu;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-      const int e = lane + kWave * i;
-      const bool ok = e < E && !((taken >> i) & 1ull);
-      if (ok && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
+      const bool better = key[i] > lk;  // strict: the lower id stays on ties
+      li = better ? (unsigned)(lane + kWave * i) : li;
+      lk = better ? key[i] : lk;
     }
+    const unsigned gk = __reduce_max_sync(~0ull, lk);
+    const unsigned gi = __reduce_min_sync(~0ull, lk == gk ? li : 0xffffffffu);
+    if ((int)(gi & (kWave - 1)) == lane) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oi = __shfl_xor(bi, off, kWave);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
+      for (int i = 0; i < VPL; ++i)
+        if ((int)(gi / kWave) == i) key[i] = 0u;
     }
-    if ((bi & (kWave - 1)) == lane) taken |= 1ull << (bi / kWave);
     if (lane == j) {
-      my_val = bv;
-      my_id = bi;
+      my_key = gk;
+      my_id = (int)gi;
     }
   }
   // softmax over the selection, in fp64, summed in rank order
-  const double top = (double)__shfl(my_val, 0, kWave);
+  const float my_val = key_value(my_key);
+  const double top = (double)key_value((unsigned)__builtin_amdgcn_readlane((int)my_key, 0));
   const double ex = lane < k ? exp((double)my_val - top) : 0.0;
+  const unsigned long long exb = __double_as_longlong(ex);
   double s = 0.0;
-  for (int j = 0; j < k; ++j) s += __shfl(ex, j, kWave);
+  for (int j = 0; j < k; ++j) {
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)exb, j);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(exb >> 32), j);
+    s += __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+  }
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     w[(size_t)t * k + lane] = (float)(ex / s);
