@@ -45,6 +45,8 @@ def _args():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle's CPU sample")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-long", action="store_true", help="skip the 4096-token staged NVFP4 measurement")
+    p.add_argument("--separate-plan", action="store_true",
+                   help="plan the 96-token chunk with separate dedup / LRU / align launches instead of one")
     p.add_argument("--long-layers", type=int, default=8)
     p.add_argument("--long-reps", type=int, default=3)
     p.add_argument("--no-decode", action="store_true", help="skip the decode-stream measurement")
@@ -123,16 +125,31 @@ def main():
     view = LY.make_view(0, E, k, H, I, L.SCR_W_BF16, S, bank.row_table, scales)
     stream = torch.cuda.current_stream()
 
+    s = stream.cuda_stream
+
     def step(marks=None, phase_events=None):
+        """route -> plan (dedup, the four LRU queries, align: one launch) -> copy
+        of the final misses -> grouped GEMMs and combine.  With --separate-plan
+        the planning runs as its three separate launches instead."""
         if phase_events:
             LY.record_timer(phase_events[0])
-        LY.route_dedup(buf, logits)
+        L.route(logits, T, E, k, buf["topk_ids"], buf["topk_w"], s)
+        if args.separate_plan:
+            L.dedup(buf["topk_ids"], buf.R, E, buf["distinct"], buf["n_distinct"], buf["inverse"], s)
+            L.ensure_slots_batched(bank.desc, 0, buf["distinct"], buf.lmax, Wd, False, buf["miss_slot"],
+                                   buf["miss_key"], buf["n_miss"], buf["n_total"], s)
+            LY.align(buf, id_map, E)
+        else:
+            ok = L.plan_chunk(bank.desc, 0, buf["topk_ids"], buf.R, buf["distinct"], buf["n_distinct"], Wd, False,
+                              buf["miss_slot"], buf["miss_key"], buf["n_miss"], buf["n_total"], buf.cfg.block_m,
+                              buf["sorted_routes"], buf["block_bucket"], buf["n_post_pad"], buf["active_buckets"],
+                              buf["active_block_begin"], buf["n_active"], s)
+            assert ok
         if phase_events:
             LY.record_timer(phase_events[1])
-        LY.admit(buf, bank, pool, 0, record_stats=False, batched=True)
+        L.copy_misses(bank.desc, pool.desc, buf["miss_slot"], buf["miss_key"], buf["n_total"], buf.lmax, s)
         if phase_events:
             LY.record_timer(phase_events[2])
-        LY.align(buf, id_map, E)
         LY.forward(buf, view, x, marks=marks)
         if phase_events:
             LY.record_timer(phase_events[3])

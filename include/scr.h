@@ -231,6 +231,27 @@ int scr_ensure_slots_batched(const scr_bank_desc* bank, int layer, const int32_t
                              int width, int record_stats, int32_t* miss_slot, int32_t* miss_key,
                              int32_t* n_miss, int32_t* n_total, hipStream_t stream);
 
+/* plan_chunk [P1 Solution bullets 2-3: the distinct list, then the LRU
+ * queries of fixed width; P3 What: a device-side planner; P1 Tests: align of
+ * the routes by their slots].  The chunk's whole planning in one launch (one
+ * workgroup): exactly scr_dedup(ids, n, E, distinct, n_distinct, NULL), then
+ * scr_ensure_slots_batched(bank, layer, distinct, min(n, E), width, ...), then
+ * scr_align_blocks(ids, n, key_to_slot + layer * E, E, S, block_size, ...),
+ * with the same outputs, bank updates and error bit.  The caller then copies
+ * the final misses with one scr_copy_misses over n_total.
+ *   ids         device i32 [n] routed expert ids of the layer (route r = t*k+j)
+ *   distinct    device i32 [min(n, E)], n_distinct device i32 [1]
+ *   miss_slot, miss_key device i32 [min(n, E)]; n_miss device i32
+ *               [ceil(min(n, E) / width)]; n_total device i32 [1]
+ *   sorted_routes .. n_active: as scr_align_blocks with num_buckets = S
+ * Returns SCR_ENOTSUP (nothing launched) when n > 4096, E > 8192 or S > 8192,
+ * where the separate calls apply. */
+int scr_plan_chunk(const scr_bank_desc* bank, int layer, const int32_t* ids, int n, int32_t* distinct,
+                   int32_t* n_distinct, int width, int record_stats, int32_t* miss_slot, int32_t* miss_key,
+                   int32_t* n_miss, int32_t* n_total, int block_size, int32_t* sorted_routes,
+                   int32_t* block_bucket, int32_t* n_post_pad, int32_t* active_buckets,
+                   int32_t* active_block_begin, int32_t* n_active, hipStream_t stream);
+
 /* copy_misses [P1 Solution second bullet; P3 What: fixed-grid row copies from
  * the host source's device-mapped view].  For i < *n_miss (read on the
  * device) copies the record of key miss_key[i] from the pool into bank slot

@@ -26,7 +26,7 @@ SCR_MAX_BUCKETS = 16384
 
 EXPORTS = (
     "scr_record_layout_of", "scr_route", "scr_dedup", "scr_ensure_slots", "scr_ensure_slots_batched",
-    "scr_copy_misses",
+    "scr_copy_misses", "scr_plan_chunk",
     "scr_align_capacity", "scr_align_workspace", "scr_align_blocks", "scr_tile_config",
     "scr_moe_workspace", "scr_grouped_moe_forward", "scr_stream_layer_async", "scr_stage_plan",
     "scr_stage_rows_async", "scr_fill_row_table", "scr_fill_staged_rows", "scr_bank_rebuild_map",
@@ -88,6 +88,8 @@ _SIGS = {
     "scr_ensure_slots": (_I, [C.POINTER(BankDesc), _I, _P, _I, _I, _I, _P, _P, _P, _P]),
     "scr_ensure_slots_batched": (_I, [C.POINTER(BankDesc), _I, _P, _I, _I, _I, _P, _P, _P, _P, _P]),
     "scr_copy_misses": (_I, [C.POINTER(BankDesc), C.POINTER(HostPoolDesc), _P, _P, _P, _I, _P]),
+    "scr_plan_chunk": (_I, [C.POINTER(BankDesc), _I, _P, _I, _P, _P, _I, _I, _P, _P, _P, _P, _I, _P, _P, _P, _P,
+                            _P, _P, _P]),
     "scr_align_capacity": (_SZ, [_I, _I, _I]),
     "scr_align_workspace": (_I, [_I, _I, C.POINTER(_SZ)]),
     "scr_align_blocks": (_I, [_P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -167,6 +169,20 @@ def ensure_slots(bank: BankDesc, layer, distinct, q_begin, width, record_stats, 
     _check("scr_ensure_slots", load().scr_ensure_slots(C.byref(bank), layer, _p(distinct), q_begin, width,
                                                        int(record_stats), _p(miss_slot), _p(miss_key),
                                                        _p(n_miss), stream))
+
+
+def plan_chunk(bank: BankDesc, layer, ids, n, distinct, n_distinct, width, record_stats, miss_slot, miss_key,
+               n_miss, n_total, block_size, sorted_routes, block_bucket, n_post_pad, active_buckets,
+               active_block_begin, n_active, stream) -> bool:
+    """True when planned; False when the shape is beyond one workgroup (SCR_ENOTSUP)."""
+    rc = load().scr_plan_chunk(C.byref(bank), layer, _p(ids), n, _p(distinct), _p(n_distinct), width,
+                               int(record_stats), _p(miss_slot), _p(miss_key), _p(n_miss), _p(n_total), block_size,
+                               _p(sorted_routes), _p(block_bucket), _p(n_post_pad), _p(active_buckets),
+                               _p(active_block_begin), _p(n_active), stream)
+    if rc == SCR_ENOTSUP:
+        return False
+    _check("scr_plan_chunk", rc)
+    return True
 
 
 def ensure_slots_batched(bank: BankDesc, layer, distinct, n, width, record_stats, miss_slot, miss_key, n_miss,

@@ -8,7 +8,7 @@
 // workgroup lays the buckets out, and a stable scatter places every route in
 // ascending route order inside its bucket (wave ballots give the rank among
 // equal buckets of one 64-route batch).
-#include "common.h"
+#include "small_blocks.h"
 
 namespace scr {
 
@@ -32,12 +32,6 @@ static AlignPlan align_plan(int n, int nb) {
   return p;
 }
 
-__device__ __forceinline__ int bucket_of(const int32_t* __restrict__ ids, const int32_t* __restrict__ map,
-                                         int num_ids, int nb, int r) {
-  int b = ids[r];
-  if (map) b = (b >= 0 && b < num_ids) ? map[b] : -1;
-  return (b >= 0 && b < nb) ? b : -1;
-}
 
 // one wave per chunk: per-bucket counts of the chunk, written bucket-major
 __global__ __launch_bounds__(64) void align_count_kernel(const int32_t* __restrict__ ids, int n,
@@ -213,110 +207,20 @@ __global__ __launch_bounds__(256) void align_fill_kernel(int n, int B, int nbloc
   }
 }
 
-// Small inputs (n <= kSmallRoutes, nb <= kSmallBuckets): the whole align in
-// one workgroup and one launch.  All waves count and lay the buckets out; one
-// wave scatters the routes in ascending order (64 at a time, ballot ranks)
-// while the other waves write the padding and block ids.
-constexpr int kSmallRoutes = 4096;
-constexpr int kSmallBuckets = 8192;
-
-__global__ __launch_bounds__(1024) void align_small_kernel(const int32_t* __restrict__ ids, int n,
-                                                           const int32_t* __restrict__ map, int num_ids, int nb,
-                                                           int B, int cap, int32_t* __restrict__ sorted_routes,
-                                                           int32_t* __restrict__ block_bucket,
-                                                           int32_t* __restrict__ n_post_pad,
-                                                           int32_t* __restrict__ active_buckets,
-                                                           int32_t* __restrict__ active_block_begin,
-                                                           int32_t* __restrict__ n_active) {
-  __shared__ int cnt[kSmallBuckets];      // counts, then running scatter positions
-  __shared__ int rb[kSmallRoutes];        // bucket of each route (-1 dropped)
-  __shared__ int wave_tot[2][kWave];
-  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave, nw = blockDim.x / kWave;
-  for (int b = tid; b < nb; b += blockDim.x) cnt[b] = 0;
-  __syncthreads();
-  for (int r = tid; r < n; r += blockDim.x) {
-    const int b = bucket_of(ids, map, num_ids, nb, r);
-    rb[r] = b;
-    if (b >= 0) atomicAdd(&cnt[b], 1);
-  }
-  __syncthreads();
-  // exclusive scans of padded counts and of the active flags; thread owns a
-  // contiguous run of buckets
-  const int per = (nb + blockDim.x - 1) / blockDim.x;
-  const int b0 = min(nb, tid * per), b1 = min(nb, b0 + per);
-  int pad_sum = 0, act_sum = 0;
-  for (int b = b0; b < b1; ++b) {
-    const int c = cnt[b];
-    pad_sum += (c + B - 1) / B * B;
-    act_sum += c > 0;
-  }
-  int s0 = pad_sum, s1 = act_sum;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o0 = __shfl_up(s0, off, kWave), o1 = __shfl_up(s1, off, kWave);
-    if (lane >= off) {
-      s0 += o0;
-      s1 += o1;
-    }
-  }
-  if (lane == kWave - 1) {
-    wave_tot[0][wv] = s0;
-    wave_tot[1][wv] = s1;
-  }
-  __syncthreads();
-  int before0 = 0, before1 = 0, total0 = 0, total1 = 0;
-  for (int w = 0; w < nw; ++w) {
-    if (w < wv) {
-      before0 += wave_tot[0][w];
-      before1 += wave_tot[1][w];
-    }
-    total0 += wave_tot[0][w];
-    total1 += wave_tot[1][w];
-  }
-  int off = before0 + s0 - pad_sum, idx = before1 + s1 - act_sum;
-  for (int b = b0; b < b1; ++b) {
-    const int c = cnt[b];
-    const int padded = (c + B - 1) / B * B;
-    if (c > 0) {
-      active_buckets[idx] = b;
-      active_block_begin[idx] = off / B;
-      ++idx;
-      for (int q = off + c; q < off + padded; ++q) sorted_routes[q] = n;
-      for (int j = off / B; j < (off + padded) / B; ++j) block_bucket[j] = b;
-    }
-    cnt[b] = off;  // scatter position of the bucket's first route
-    off += padded;
-  }
-  if (tid == 0) {
-    *n_post_pad = total0;
-    *n_active = total1;
-    active_block_begin[total1] = total0 / B;
-  }
-  for (int q = total0 + tid; q < cap; q += blockDim.x) sorted_routes[q] = n;
-  for (int j = total0 / B + tid; j < cap / B; j += blockDim.x) block_bucket[j] = -1;
-  __syncthreads();
-  if (wv == 0) {
-    int nbits = 0;
-    while ((1 << nbits) < nb) ++nbits;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int rb0 = 0; rb0 < n; rb0 += kWave) {
-      const int r = rb0 + lane;
-      const int b = r < n ? rb[r] : -1;
-      uint64_t peers = __ballot(b >= 0);
-      for (int bit = 0; bit < nbits; ++bit) {
-        const uint64_t ones = __ballot(b >= 0 && ((b >> bit) & 1));
-        peers &= ((b >> bit) & 1) ? ones : ~ones;
-      }
-      int pos = 0;
-      if (b >= 0) pos = cnt[b] + __popcll(peers & lt_mask);
-      __builtin_amdgcn_wave_barrier();
-      if (b >= 0) {
-        sorted_routes[pos] = r;
-        if ((peers & lt_mask) == 0) cnt[b] += __popcll(peers);
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
+__global__ __launch_bounds__(kPlanThreads) void align_small_kernel(const int32_t* __restrict__ ids, int n,
+                                                                   const int32_t* __restrict__ map, int num_ids,
+                                                                   int nb, int B, int cap,
+                                                                   int32_t* __restrict__ sorted_routes,
+                                                                   int32_t* __restrict__ block_bucket,
+                                                                   int32_t* __restrict__ n_post_pad,
+                                                                   int32_t* __restrict__ active_buckets,
+                                                                   int32_t* __restrict__ active_block_begin,
+                                                                   int32_t* __restrict__ n_active) {
+  __shared__ int cnt[kSmallBuckets];  // counts, then running scatter positions
+  __shared__ int rb[kSmallRoutes];    // bucket of each route (-1 dropped)
+  __shared__ int wave_tot[2 * kWave];
+  align_small_block(ids, n, map, num_ids, nb, B, cap, sorted_routes, block_bucket, n_post_pad, active_buckets,
+                    active_block_begin, n_active, cnt, rb, wave_tot);
 }
 
 }  // namespace scr
@@ -356,7 +260,7 @@ extern "C" int scr_align_blocks(const int32_t* ids, int n, const int32_t* id_to_
   SCR_CHECK_ARG(ws_bytes >= need, "align: workspace of %zu bytes, %zu needed", ws_bytes, need);
   if (n <= scr::kSmallRoutes && num_buckets <= scr::kSmallBuckets) {
     const int cap = (int)scr_align_capacity(n, num_buckets, block_size);
-    hipLaunchKernelGGL(scr::align_small_kernel, dim3(1), dim3(1024), 0, stream, ids, n, id_to_bucket, num_ids,
+    hipLaunchKernelGGL(scr::align_small_kernel, dim3(1), dim3(scr::kPlanThreads), 0, stream, ids, n, id_to_bucket, num_ids,
                        num_buckets, block_size, cap, sorted_routes, block_bucket, n_post_pad, active_buckets,
                        active_block_begin, n_active);
     SCR_CHECK_LAUNCH();

@@ -6,11 +6,11 @@
 // bank shared by all layers).  Recency is one stamp per query; candidates for
 // eviction are ordered by the 64-bit key (stamp << 20 | slot), found by an
 // 8-bit radix select in LDS instead of sorting the bank.
-#include "common.h"
+#include "small_blocks.h"
 
 namespace scr {
 
-constexpr int kLruThreads = 1024;
+constexpr int kLruThreads = kPlanThreads;
 constexpr int kSlotBits = 20;  // SCR_MAX_SLOTS <= 2^18 < 2^20
 
 __device__ __forceinline__ uint64_t cand_key(uint64_t stamp, int slot) {
@@ -210,11 +210,11 @@ __global__ __launch_bounds__(kLruThreads) void ensure_slots_kernel(BankRefs bk, 
 // Their admitted misses are appended to one list; an entry whose slot was
 // taken again by a later query of the same call is marked superseded (slot -1)
 // so that one copy over the list moves only each slot's final record.
-__global__ __launch_bounds__(kLruThreads) void ensure_slots_batched_kernel(
-    BankRefs bk, uint64_t* __restrict__ clock, const int32_t* __restrict__ distinct, int width, int n_queries,
-    int last_width, int record_stats, int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_key,
-    int32_t* __restrict__ n_miss, int32_t* __restrict__ n_total) {
-  __shared__ EnsureShared sh;
+__device__ __forceinline__ void ensure_batched_block(EnsureShared& sh, const BankRefs& bk, uint64_t* __restrict__ clock,
+                                                     const int32_t* __restrict__ distinct, int width, int n_queries,
+                                                     int last_width, int record_stats, int32_t* __restrict__ miss_slot,
+                                                     int32_t* __restrict__ miss_key, int32_t* __restrict__ n_miss,
+                                                     int32_t* __restrict__ n_total) {
   uint64_t now = *clock;
   int total = 0;
   for (int q = 0; q < n_queries; ++q) {
@@ -233,6 +233,50 @@ __global__ __launch_bounds__(kLruThreads) void ensure_slots_batched_kernel(
     *clock = now;
     *n_total = total;
   }
+}
+
+__global__ __launch_bounds__(kLruThreads) void ensure_slots_batched_kernel(
+    BankRefs bk, uint64_t* __restrict__ clock, const int32_t* __restrict__ distinct, int width, int n_queries,
+    int last_width, int record_stats, int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_key,
+    int32_t* __restrict__ n_miss, int32_t* __restrict__ n_total) {
+  __shared__ EnsureShared sh;
+  ensure_batched_block(sh, bk, clock, distinct, width, n_queries, last_width, record_stats, miss_slot, miss_key,
+                       n_miss, n_total);
+}
+
+// The chunk's planning in one workgroup and one launch: dedup of the routed
+// ids, the LRU queries over the distinct list, then the align of the routes by
+// their (new) slots.  The phases share one LDS area; each phase's global
+// writes are visible to the next after the barrier between them.
+union PlanShared {
+  EnsureShared ens;
+  struct {
+    int pos[kDedupMaxE];
+    int wave_tot[kWave + 1];
+  } dd;
+  struct {
+    int cnt[kSmallBuckets];
+    int rb[kSmallRoutes];
+    int wave_tot[2 * kWave];
+  } al;
+};
+
+__global__ __launch_bounds__(kPlanThreads) void plan_chunk_kernel(
+    BankRefs bk, uint64_t* __restrict__ clock, const int32_t* __restrict__ ids, int n, int lmax,
+    int32_t* __restrict__ distinct, int32_t* __restrict__ n_distinct, int width, int n_queries, int last_width,
+    int record_stats, int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_key, int32_t* __restrict__ n_miss,
+    int32_t* __restrict__ n_total, int B, int cap, int32_t* __restrict__ sorted_routes,
+    int32_t* __restrict__ block_bucket, int32_t* __restrict__ n_post_pad, int32_t* __restrict__ active_buckets,
+    int32_t* __restrict__ active_block_begin, int32_t* __restrict__ n_active) {
+  __shared__ PlanShared sh;
+  dedup_block(ids, n, bk.E, lmax, distinct, n_distinct, nullptr, sh.dd.pos, sh.dd.wave_tot);
+  __syncthreads();
+  ensure_batched_block(sh.ens, bk, clock, distinct, width, n_queries, last_width, record_stats, miss_slot, miss_key,
+                       n_miss, n_total);
+  __syncthreads();
+  align_small_block(ids, n, bk.key_to_slot + (size_t)bk.layer * bk.E, bk.E, bk.S, B, cap, sorted_routes,
+                    block_bucket, n_post_pad, active_buckets, active_block_begin, n_active, sh.al.cnt, sh.al.rb,
+                    sh.al.wave_tot);
 }
 
 __global__ void rebuild_map_clear(int32_t* __restrict__ key_to_slot, int n) {
@@ -306,6 +350,40 @@ extern "C" int scr_ensure_slots_batched(const scr_bank_desc* bank, int layer, co
   hipLaunchKernelGGL(scr::ensure_slots_batched_kernel, dim3(1), dim3(scr::kLruThreads), 0, stream,
                      scr::bank_refs(bank, layer), bank->clock, distinct, width, n_queries, last_width,
                      record_stats ? 1 : 0, miss_slot, miss_key, n_miss, n_total);
+  SCR_CHECK_LAUNCH();
+  return SCR_OK;
+}
+
+extern "C" int scr_plan_chunk(const scr_bank_desc* bank, int layer, const int32_t* ids, int n, int32_t* distinct,
+                              int32_t* n_distinct, int width, int record_stats, int32_t* miss_slot,
+                              int32_t* miss_key, int32_t* n_miss, int32_t* n_total, int block_size,
+                              int32_t* sorted_routes, int32_t* block_bucket, int32_t* n_post_pad,
+                              int32_t* active_buckets, int32_t* active_block_begin, int32_t* n_active,
+                              hipStream_t stream) {
+  int rc = scr::check_bank(bank);
+  if (rc) return rc;
+  SCR_CHECK_ARG(layer >= 0 && layer < bank->L, "plan_chunk: layer %d out of [0, %d)", layer, bank->L);
+  SCR_CHECK_ARG(width >= 1 && width <= SCR_MAX_QUERY_WIDTH, "plan_chunk: width must be in [1, %d]",
+                SCR_MAX_QUERY_WIDTH);
+  SCR_CHECK_ARG(n >= 1, "plan_chunk: n must be >= 1");
+  SCR_CHECK_ARG(block_size == 16 || block_size == 32 || block_size == 64,
+                "plan_chunk: block_size must be 16, 32 or 64");
+  SCR_CHECK_ARG(ids && distinct && n_distinct && miss_slot && miss_key && n_miss && n_total && sorted_routes &&
+                    block_bucket && n_post_pad && active_buckets && active_block_begin && n_active,
+                "plan_chunk: null pointer");
+  if (n > scr::kSmallRoutes || bank->E > scr::kDedupMaxE || bank->S > scr::kSmallBuckets) {
+    scr::set_error("plan_chunk: n %d, E %d or S %d beyond one workgroup (%d, %d, %d)", n, bank->E, bank->S,
+                   scr::kSmallRoutes, scr::kDedupMaxE, scr::kSmallBuckets);
+    return SCR_ENOTSUP;
+  }
+  const int lmax = n < bank->E ? n : bank->E;
+  const int n_queries = (lmax + width - 1) / width;
+  const int last_width = lmax - (n_queries - 1) * width;
+  const int cap = (int)scr_align_capacity(n, bank->S, block_size);
+  hipLaunchKernelGGL(scr::plan_chunk_kernel, dim3(1), dim3(scr::kPlanThreads), 0, stream, scr::bank_refs(bank, layer),
+                     bank->clock, ids, n, lmax, distinct, n_distinct, width, n_queries, last_width,
+                     record_stats ? 1 : 0, miss_slot, miss_key, n_miss, n_total, block_size, cap, sorted_routes,
+                     block_bucket, n_post_pad, active_buckets, active_block_begin, n_active);
   SCR_CHECK_LAUNCH();
   return SCR_OK;
 }

@@ -1,0 +1,189 @@
+// Single-workgroup bodies shared by the stand-alone kernels (dedup, the small
+// align) and the fused chunk planner: each is called by all threads of one
+// workgroup of kPlanThreads threads with its LDS passed in.
+#pragma once
+#include "common.h"
+
+namespace scr {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kDedupMaxE = 8192;
+constexpr int kSmallRoutes = 4096;   // routes the one-workgroup align takes
+constexpr int kSmallBuckets = 8192;  // buckets the one-workgroup align takes
+
+// inclusive scan of one int per thread across the block; returns the block total
+__device__ __forceinline__ int block_inclusive_scan(int v, int* wave_tot) {
+  const int lane = lane_id();
+  const int wv = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(v, off, kWave);
+    if (lane >= off) v += o;
+  }
+  if (lane == kWave - 1) wave_tot[wv] = v;
+  __syncthreads();
+  if (wv == 0) {
+    int t = lane < nw ? wave_tot[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(t, off, kWave);
+      if (lane >= off) t += o;
+    }
+    if (lane < nw) wave_tot[lane] = t;
+  }
+  __syncthreads();
+  const int before = wv > 0 ? wave_tot[wv - 1] : 0;
+  const int total = wave_tot[nw - 1];
+  __syncthreads();
+  wave_tot[kWave] = total;
+  return v + before;
+}
+
+
+__device__ __forceinline__ int bucket_of(const int32_t* __restrict__ ids, const int32_t* __restrict__ map,
+                                         int num_ids, int nb, int r) {
+  int b = ids[r];
+  if (map) b = (b >= 0 && b < num_ids) ? map[b] : -1;
+  return (b >= 0 && b < nb) ? b : -1;
+}
+
+// Distinct ids as a sorted fixed-length list: marks in LDS, a scan, a
+// scatter (a counting sort over ids).  pos: LDS [kDedupMaxE]; wave_tot: LDS
+// [kWave + 1].
+__device__ __forceinline__ void dedup_block(const int32_t* __restrict__ ids, int n, int E, int lmax,
+                                            int32_t* __restrict__ distinct, int32_t* __restrict__ n_distinct,
+                                            int32_t* __restrict__ inverse, int* pos, int* wave_tot) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) pos[e] = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int e = ids[i];
+    if (e >= 0 && e < E) pos[e] = 1;
+  }
+  __syncthreads();
+  // each thread owns a contiguous run of ids [e0, e1)
+  const int per = (E + blockDim.x - 1) / blockDim.x;
+  const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
+  int cnt = 0;
+  for (int e = e0; e < e1; ++e) cnt += pos[e];
+  const int incl = block_inclusive_scan(cnt, wave_tot);
+  const int total = wave_tot[kWave];
+  int p = incl - cnt;
+  for (int e = e0; e < e1; ++e) {
+    const int present = pos[e];
+    if (present) distinct[p] = e;
+    pos[e] = present ? p : -1;
+    p += present;
+  }
+  for (int i = total + threadIdx.x; i < lmax; i += blockDim.x) distinct[i] = E;
+  if (threadIdx.x == 0) *n_distinct = total;
+  if (inverse) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const int e = ids[i];
+      inverse[i] = (e >= 0 && e < E) ? pos[e] : -1;
+    }
+  }
+}
+
+// Small inputs (n <= kSmallRoutes, nb <= kSmallBuckets): the whole align in
+// one workgroup.  All waves count and lay the buckets out; one wave scatters
+// the routes in ascending order (64 at a time, ballot ranks) while the other
+// waves write the padding and block ids.  cnt: LDS [kSmallBuckets]; rb: LDS
+// [kSmallRoutes]; wave_tot: LDS [2 * kWave].
+__device__ __forceinline__ void align_small_block(const int32_t* __restrict__ ids, int n,
+                                                  const int32_t* __restrict__ map, int num_ids, int nb, int B,
+                                                  int cap, int32_t* __restrict__ sorted_routes,
+                                                  int32_t* __restrict__ block_bucket, int32_t* __restrict__ n_post_pad,
+                                                  int32_t* __restrict__ active_buckets,
+                                                  int32_t* __restrict__ active_block_begin,
+                                                  int32_t* __restrict__ n_active, int* cnt, int* rb, int* wave_tot) {
+  const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave, nw = blockDim.x / kWave;
+  for (int b = tid; b < nb; b += blockDim.x) cnt[b] = 0;
+  __syncthreads();
+  for (int r = tid; r < n; r += blockDim.x) {
+    const int b = bucket_of(ids, map, num_ids, nb, r);
+    rb[r] = b;
+    if (b >= 0) atomicAdd(&cnt[b], 1);
+  }
+  __syncthreads();
+  // exclusive scans of padded counts and of the active flags; thread owns a
+  // contiguous run of buckets
+  const int per = (nb + blockDim.x - 1) / blockDim.x;
+  const int b0 = min(nb, tid * per), b1 = min(nb, b0 + per);
+  int pad_sum = 0, act_sum = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int c = cnt[b];
+    pad_sum += (c + B - 1) / B * B;
+    act_sum += c > 0;
+  }
+  int s0 = pad_sum, s1 = act_sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o0 = __shfl_up(s0, off, kWave), o1 = __shfl_up(s1, off, kWave);
+    if (lane >= off) {
+      s0 += o0;
+      s1 += o1;
+    }
+  }
+  if (lane == kWave - 1) {
+    wave_tot[wv] = s0;
+    wave_tot[kWave + wv] = s1;
+  }
+  __syncthreads();
+  int before0 = 0, before1 = 0, total0 = 0, total1 = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wv) {
+      before0 += wave_tot[w];
+      before1 += wave_tot[kWave + w];
+    }
+    total0 += wave_tot[w];
+    total1 += wave_tot[kWave + w];
+  }
+  int off = before0 + s0 - pad_sum, idx = before1 + s1 - act_sum;
+  for (int b = b0; b < b1; ++b) {
+    const int c = cnt[b];
+    const int padded = (c + B - 1) / B * B;
+    if (c > 0) {
+      active_buckets[idx] = b;
+      active_block_begin[idx] = off / B;
+      ++idx;
+      for (int q = off + c; q < off + padded; ++q) sorted_routes[q] = n;
+      for (int j = off / B; j < (off + padded) / B; ++j) block_bucket[j] = b;
+    }
+    cnt[b] = off;  // scatter position of the bucket's first route
+    off += padded;
+  }
+  if (tid == 0) {
+    *n_post_pad = total0;
+    *n_active = total1;
+    active_block_begin[total1] = total0 / B;
+  }
+  for (int q = total0 + tid; q < cap; q += blockDim.x) sorted_routes[q] = n;
+  for (int j = total0 / B + tid; j < cap / B; j += blockDim.x) block_bucket[j] = -1;
+  __syncthreads();
+  if (wv == 0) {
+    int nbits = 0;
+    while ((1 << nbits) < nb) ++nbits;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int rb0 = 0; rb0 < n; rb0 += kWave) {
+      const int r = rb0 + lane;
+      const int b = r < n ? rb[r] : -1;
+      uint64_t peers = __ballot(b >= 0);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const uint64_t ones = __ballot(b >= 0 && ((b >> bit) & 1));
+        peers &= ((b >> bit) & 1) ? ones : ~ones;
+      }
+      int pos = 0;
+      if (b >= 0) pos = cnt[b] + __popcll(peers & lt_mask);
+      __builtin_amdgcn_wave_barrier();
+      if (b >= 0) {
+        sorted_routes[pos] = r;
+        if ((peers & lt_mask) == 0) cnt[b] += __popcll(peers);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+}
+
+}  // namespace scr

@@ -246,6 +246,20 @@ def admit(buf: LayerBuffers, bank: Bank, pool: HostPool, layer: int, record_stat
         L.copy_misses(bank.desc, pool.desc, ms, mk, nm, w, s)
 
 
+def plan(buf: LayerBuffers, bank: Bank, pool: HostPool, layer: int, record_stats: bool, stream=None) -> bool:
+    """Dedup, all LRU queries and the align of one chunk in one launch, then one
+    copy of the final misses.  Needs the routed ids in buf (route first).
+    False (nothing enqueued) when the shape is beyond the one-workgroup planner."""
+    s = _stream(stream)
+    ok = L.plan_chunk(bank.desc, layer, buf["topk_ids"], buf.R, buf["distinct"], buf["n_distinct"], buf.width,
+                      record_stats, buf["miss_slot"], buf["miss_key"], buf["n_miss"], buf["n_total"],
+                      buf.cfg.block_m, buf["sorted_routes"], buf["block_bucket"], buf["n_post_pad"],
+                      buf["active_buckets"], buf["active_block_begin"], buf["n_active"], s)
+    if ok:
+        L.copy_misses(bank.desc, pool.desc, buf["miss_slot"], buf["miss_key"], buf["n_total"], buf.lmax, s)
+    return ok
+
+
 def align(buf: LayerBuffers, id_to_bucket, num_ids, stream=None):
     s = _stream(stream)
     L.align_blocks(buf["topk_ids"], buf.R, id_to_bucket, num_ids, buf.num_buckets, buf.cfg.block_m,
@@ -261,17 +275,26 @@ def forward(buf: LayerBuffers, view: L.RoutedExperts, x: torch.Tensor, stream=No
 
 
 def demand_layer(bank: Bank, pool: HostPool, layer: int, logits, x, input_scale, width=128, record_stats=False,
-                 y_dtype=L.SCR_Y_F32, buf: LayerBuffers | None = None, stream=None, shape=None, batched=False):
+                 y_dtype=L.SCR_Y_F32, buf: LayerBuffers | None = None, stream=None, shape=None, batched=False,
+                 fused=False):
     """Demand (slot) path of one layer: route, dedup, per-query ensure + miss copy,
-    align over the bank's slots through key_to_slot, grouped GEMM at the slots."""
+    align over the bank's slots through key_to_slot, grouped GEMM at the slots.
+    fused=True plans the chunk (dedup, queries, align) in one launch when it fits."""
     T, E = logits.shape
     k, H, I = shape
     if buf is None:
         buf = LayerBuffers(T, E, k, H, I, bank.S, bank.wdtype, width=width, y_dtype=y_dtype)
-    route_dedup(buf, logits, stream)
-    admit(buf, bank, pool, layer, record_stats, stream, batched=batched)
-    id_map = bank.key_to_slot.data_ptr() + layer * E * 4
-    align(buf, id_map, E, stream)
+    s = _stream(stream)
+    if fused:
+        L.route(logits, buf.T, buf.E, buf.k, buf["topk_ids"], buf["topk_w"], s)
+        if not plan(buf, bank, pool, layer, record_stats, stream):
+            L.dedup(buf["topk_ids"], buf.R, buf.E, buf["distinct"], buf["n_distinct"], buf["inverse"], s)
+            admit(buf, bank, pool, layer, record_stats, stream, batched=True)
+            align(buf, bank.key_to_slot.data_ptr() + layer * E * 4, E, stream)
+    else:
+        route_dedup(buf, logits, stream)
+        admit(buf, bank, pool, layer, record_stats, stream, batched=batched)
+        align(buf, bank.key_to_slot.data_ptr() + layer * E * 4, E, stream)
     view = make_view(layer, E, k, H, I, bank.wdtype, bank.S, bank.row_table, input_scale)
     buf.cfg_used = forward(buf, view, x, stream)
     return buf

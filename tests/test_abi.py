@@ -99,3 +99,26 @@ def test_bank_and_view_validation(lib):
     view = L.RoutedExperts(0, 8, 2, 256, 128, 0, 8, 1, 1)
     with pytest.raises(L.ScrError):                                  # workspace too small
         L.grouped_moe_forward(view, 1, 4, 1, 1, 1, 1, 1, 1, 0, 1, 16, None, None)
+
+
+def test_plan_chunk_validation(lib):
+    bank = L.BankDesc(16, 2, 8, 0, 1, 1, 1, 1, 1, 1, 1, 1, 16)
+    args = dict(ids=1, n=10, distinct=1, n_distinct=1, width=4, record_stats=0, miss_slot=1, miss_key=1,
+                n_miss=1, n_total=1, block_size=16, sorted_routes=1, block_bucket=1, n_post_pad=1,
+                active_buckets=1, active_block_begin=1, n_active=1, stream=None)
+
+    def call(b, layer, **kw):
+        a = dict(args, **kw)
+        return L.plan_chunk(b, layer, a["ids"], a["n"], a["distinct"], a["n_distinct"], a["width"],
+                            a["record_stats"], a["miss_slot"], a["miss_key"], a["n_miss"], a["n_total"],
+                            a["block_size"], a["sorted_routes"], a["block_bucket"], a["n_post_pad"],
+                            a["active_buckets"], a["active_block_begin"], a["n_active"], a["stream"])
+    for kw in (dict(width=0), dict(width=2000), dict(n=0), dict(block_size=24), dict(ids=None)):
+        with pytest.raises(L.ScrError):
+            call(bank, 0, **kw)
+    with pytest.raises(L.ScrError):
+        call(bank, 2)                                                  # layer out of range
+    # beyond one workgroup: reported as unsupported before any launch
+    assert call(bank, 0, n=5000) is False
+    big = L.BankDesc(9000, 2, 8, 0, 1, 1, 1, 1, 1, 1, 1, 1, 16)
+    assert call(big, 0) is False

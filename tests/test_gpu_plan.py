@@ -1,0 +1,118 @@
+"""GPU parity of the one-launch chunk planner: dedup + all LRU queries + align
+in one workgroup gives exactly the outputs, bank state and copied rows of the
+separate calls, and (through them) of the oracle's LRU."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from helpers import ExpertSource, fill_pool, flush
+from oracle import SlotBankState, ensure_slots
+
+pytestmark = pytest.mark.gpu
+
+# outputs written in full; active_buckets / active_block_begin are defined up
+# to n_active / n_active + 1 entries (the rest of those buffers is not written)
+OUT_KEYS = ("distinct", "n_distinct", "n_miss", "n_total", "sorted_routes", "block_bucket", "n_post_pad",
+            "n_active")
+STATE_KEYS = ("slot_key", "slot_stamp", "key_to_slot", "clock", "stats", "decode_freq", "err")
+
+
+def _plan_both(S, NL, E, k, T, logits, fill, width, record_stats, layer=0, rec=4096, seed=11):
+    """Runs the separate calls and the fused planner from the same bank state;
+    returns both (buffers, bank) pairs."""
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    pool = LY.HostPool(NL, E, rec, E, payload_of=lambda key: key % E)
+    g = np.random.default_rng(seed)
+    for p in range(E):
+        pool.write_payload(p, g.integers(0, 256, size=rec, dtype=np.uint8))
+    dev = torch.from_numpy(np.ascontiguousarray(logits)).cuda()
+    s = torch.cuda.current_stream().cuda_stream
+    out = []
+    for fused in (False, True):
+        bank = LY.Bank(S, NL, E, 0, rec)
+        if fill is not None:
+            bank.load_fill(fill)
+        buf = LY.LayerBuffers(T, E, k, 128, 128, S, 0, width=width)
+        L.route(dev, T, E, k, buf["topk_ids"], buf["topk_w"], s)
+        if fused:
+            assert LY.plan(buf, bank, pool, layer, record_stats)
+        else:
+            L.dedup(buf["topk_ids"], buf.R, E, buf["distinct"], buf["n_distinct"], buf["inverse"], s)
+            LY.admit(buf, bank, pool, layer, record_stats, batched=True)
+            LY.align(buf, bank.key_to_slot.data_ptr() + layer * E * 4, E)
+        torch.cuda.synchronize()
+        out.append((buf, bank))
+    return out
+
+
+def _compare(out, where):
+    (b0, k0), (b1, k1) = out
+    for key in OUT_KEYS:
+        assert torch.equal(b0[key], b1[key]), (where, key)
+    na = int(b0["n_active"].item())
+    assert torch.equal(b0["active_buckets"][:na], b1["active_buckets"][:na]), where
+    assert torch.equal(b0["active_block_begin"][:na + 1], b1["active_block_begin"][:na + 1]), where
+    nt = int(b0["n_total"].item())
+    assert torch.equal(b0["miss_slot"][:nt], b1["miss_slot"][:nt]) and torch.equal(b0["miss_key"][:nt],
+                                                                                   b1["miss_key"][:nt]), where
+    s0, s1 = k0.snapshot(), k1.snapshot()
+    for key in STATE_KEYS:
+        assert np.array_equal(np.asarray(s0[key]), np.asarray(s1[key])), (where, key)
+    assert torch.equal(k0.rows, k1.rows), (where, "bank rows")
+    return s1
+
+
+def test_plan_short_prefill_96_equals_separate_calls():
+    cfg = W.C2
+    E, k, S, NL, T = cfg.shape.E, cfg.shape.k, cfg.S, cfg.L, cfg.T
+    lg, _ = W.logits_with_chosen(cfg.seed, T, E, k, 160)
+    fill = W.bank_prefilled(cfg.seed, S, NL, E, 600, exclude_layer=0)
+    out = _plan_both(S, NL, E, k, T, lg, fill, 128, False, rec=1024)
+    _compare(out, "short prefill")
+    assert out[1][0]["n_miss"].cpu().numpy().tolist() == [128, 32, 0, 0]
+    flush("plan: 96-token chunk equals the separate calls")
+
+
+def test_plan_one_layer_cache_three_per_query():
+    cfg = W.C3B
+    E, k, T = cfg.shape.E, cfg.shape.k, cfg.T
+    lg = W.logits_normal(cfg.seed, 0, T, E)
+    fill = W.bank_prefilled(cfg.seed, 8, cfg.L, E, 8, exclude_layer=0)
+    out = _plan_both(8, cfg.L, E, k, T, lg, fill, 3, False, rec=512)
+    _compare(out, "S=8 W=3")
+    assert out[1][0]["n_miss"].cpu().numpy().tolist() == [3, 3, 2]
+
+
+@pytest.mark.parametrize("S,E,k,T,width,stats", [(6, 16, 3, 40, 4, 0), (30, 64, 4, 50, 16, 1), (700, 512, 10, 12, 32, 1)])
+def test_plan_small_banks_overflow_and_decode(S, E, k, T, width, stats):
+    # S=6 with up to 16 distinct: later queries take earlier slots again (superseded
+    # entries) and overflow the bank (error bit); the others are decode-like chunks
+    g = np.random.default_rng(S + E)
+    lg = g.standard_normal((T, E)).astype(np.float32)
+    out = _plan_both(S, 2, E, k, T, lg, None, width, stats, layer=1, rec=512)
+    snap = _compare(out, f"S={S} E={E}")
+    # the bank state also equals the oracle's LRU run query by query
+    from oracle import route_topk_softmax, dedup_sorted
+    ids, _ = route_topk_softmax(lg, k)
+    distinct, _, _ = dedup_sorted(ids.reshape(-1), E)
+    st = SlotBankState(S, 2, E)
+    for q0 in range(0, len(distinct), width):
+        ensure_slots(st, 1, distinct[q0:q0 + width], bool(stats))
+    for key in ("slot_key", "slot_stamp", "key_to_slot", "clock", "stats", "decode_freq", "err"):
+        assert np.array_equal(np.asarray(snap[key]), np.asarray(getattr(st, key))), key
+
+
+def test_plan_reports_unsupported_shapes_without_launching():
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    S, E, k, T = 9000, 16, 2, 4     # more slots than the one-workgroup align takes
+    bank = LY.Bank(S, 1, E, 0, 256)
+    buf = LY.LayerBuffers(T, E, k, 128, 128, S, 0, width=8)
+    pool = LY.HostPool(1, E, 256, E)
+    before = bank.snapshot()
+    assert not LY.plan(buf, bank, pool, 0, False)
+    torch.cuda.synchronize()
+    after = bank.snapshot()
+    assert after["clock"] == before["clock"]
