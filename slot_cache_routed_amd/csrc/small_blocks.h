@@ -162,25 +162,36 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
   for (int q = total0 + tid; q < cap; q += blockDim.x) sorted_routes[q] = n;
   for (int j = total0 / B + tid; j < cap / B; j += blockDim.x) block_bucket[j] = -1;
   __syncthreads();
+  // Stable scatter in two steps.  First every wave takes 64-route chunks and
+  // finds, by ballots over the bucket bits, each route's rank among the routes
+  // of its bucket in the chunk and (at the first of them) their count, packed
+  // into rb as bucket | rank << 14 | count << 20 (buckets < 2^13).  Then one
+  // wave walks the chunks in order: position = the bucket's running offset +
+  // rank, and the first route of each bucket advances the offset.
+  int nbits = 0;
+  while ((1 << nbits) < nb) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int nchunks = (n + kWave - 1) / kWave;
+  for (int c = wv; c < nchunks; c += nw) {
+    const int r = c * kWave + lane;
+    const int b = r < n ? rb[r] : -1;
+    uint64_t peers = __ballot(b >= 0);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t ones = __ballot(b >= 0 && ((b >> bit) & 1));
+      peers &= ((b >> bit) & 1) ? ones : ~ones;
+    }
+    const int rank = __popcll(peers & lt_mask);
+    if (b >= 0) rb[r] = b | (rank << 14) | ((rank == 0 ? __popcll(peers) : 0) << 20);
+  }
+  __syncthreads();
   if (wv == 0) {
-    int nbits = 0;
-    while ((1 << nbits) < nb) ++nbits;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int rb0 = 0; rb0 < n; rb0 += kWave) {
-      const int r = rb0 + lane;
-      const int b = r < n ? rb[r] : -1;
-      uint64_t peers = __ballot(b >= 0);
-      for (int bit = 0; bit < nbits; ++bit) {
-        const uint64_t ones = __ballot(b >= 0 && ((b >> bit) & 1));
-        peers &= ((b >> bit) & 1) ? ones : ~ones;
-      }
-      int pos = 0;
-      if (b >= 0) pos = cnt[b] + __popcll(peers & lt_mask);
-      __builtin_amdgcn_wave_barrier();
-      if (b >= 0) {
-        sorted_routes[pos] = r;
-        if ((peers & lt_mask) == 0) cnt[b] += __popcll(peers);
-      }
+    for (int c = 0; c < nchunks; ++c) {
+      const int r = c * kWave + lane;
+      const int v = r < n ? rb[r] : -1;
+      const int b = v & 0x3fff, rank = (v >> 14) & 63;
+      if (v >= 0) sorted_routes[cnt[b] + rank] = r;
+      __builtin_amdgcn_wave_barrier();  // every lane has read the offsets before the leaders move them
+      if (v >= 0 && rank == 0) cnt[b] += v >> 20;
       __builtin_amdgcn_wave_barrier();
     }
   }
