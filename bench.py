@@ -460,7 +460,9 @@ def align_bench() -> dict:
     s = torch.cuda.current_stream().cuda_stream
     out = {}
     for name, n, nb, B in (("short_prefill_96", 960, 1100, 16), ("long_prefill_4096", 40960, 512, 16),
-                           ("decode_step", 40, 1650, 16), ("uniform_2100", 960, 2100, 16),
+                           ("decode_step", 40, 1650, 16), ("uniform_1023", 960, 1023, 16),
+                           ("uniform_2100", 960, 2100, 16), ("uniform_1023_block64", 960, 1023, 64),
+                           ("uniform_2100_40960_block64", 40960, 2100, 64),
                            ("bandwidth_655360x2100", 655360, 2100, 16)):
         ids = torch.from_numpy(W.uniform_ids(4, n, nb)).cuda()
         cap = L.align_capacity(n, nb, B)
@@ -479,7 +481,8 @@ def align_bench() -> dict:
         t_b.record(s)
         us = t_a.elapsed_ms(t_b) * 1e3 / reps
         moved = 4 * n + 4 * cap + 4 * (cap // B)     # ids in, sorted routes and block ids out
-        out[name] = {"routes": n, "buckets": nb, "us": round(us, 2), "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
+        out[name] = {"routes": n, "buckets": nb, "block": B, "us": round(us, 2),
+                     "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
     return out
 
 

@@ -245,3 +245,57 @@ def test_rows_past_32_gib_of_bank():
     assert not np.array_equal(outs[0], outs[2])
     del bank
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("H,I", [(256, 128), (512, 512)])
+def test_nvfp4_every_scale_code_and_every_e2m1_code(H, I):
+    """Block scales cycling over every finite E4M3 code (subnormals, 448, both
+    signs) and uniformly random e2m1 codes (both zeros included): the GEMM's
+    in-register decode against the oracle's table decode.  40 tokens over 4
+    experts give 20 rows per expert (the 112-row passes); 256 x 128 takes the
+    narrow-tile kernel, 512 x 512 the wide one (hardware scale conversion)."""
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    from oracle import dequant_nvfp4
+    T, E, k = 40, 4, 2
+    g = np.random.default_rng(448 + H)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+    def raw(e):
+        def sc(rows, cols):
+            n = rows * (cols // 16)
+            return np.resize(np.roll(finite, 37 * e), n).reshape(rows, cols // 16).astype(np.uint8)
+        return {"w13_q": g.integers(0, 256, size=(2 * I, H // 2), dtype=np.uint8), "w13_s": sc(2 * I, H),
+                "w2_q": g.integers(0, 256, size=(H, I // 2), dtype=np.uint8), "w2_s": sc(H, I),
+                "g13": np.float32(2.0 ** -7), "g2": np.float32(2.0 ** -9)}
+    raws = [raw(e) for e in range(E)]
+    lay = LY.record_layout(L.SCR_W_NVFP4, H, I)
+    pool = LY.HostPool(1, E, lay.record_bytes, E)
+    for e in range(E):
+        pool.write_payload(e, LY.pack_record_nvfp4(lay, raws[e]))
+    lg = W.logits_normal(31, 0, T, E)
+    xb = W.f32_to_bf16_bits(W.activations_normal(31, T, H))
+    bank = LY.Bank(E, 1, E, L.SCR_W_NVFP4, lay.record_bytes)
+    d = LY.demand_layer(bank, pool, 0, _dev(lg), _dev(xb.view(np.int16)), _dev(np.ones(E, np.float32)), width=4,
+                        shape=(k, H, I), fused=True)
+    y = _y(d)
+    ids, w = route_topk_softmax(lg, k)
+    f64 = {e: (dequant_nvfp4(raws[e]["w13_q"], raws[e]["w13_s"], raws[e]["g13"]),
+               dequant_nvfp4(raws[e]["w2_q"], raws[e]["w2_s"], raws[e]["g2"])) for e in range(E)}
+    y_ref = moe_layer(bf16_bits_to_f64(xb), ids, w, lambda e: f64[e])
+    err = rel_max_err(y, y_ref)
+    flush(f"nvfp4 every scale code, H={H} I={I}: rel max err = {err:.3e}")
+    assert err <= TOL_FP4
+
+
+def test_forward_with_no_tokens_launches_nothing():
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    rows = torch.zeros(4, dtype=torch.int64, device="cuda")
+    sc = torch.ones(4, dtype=torch.float32, device="cuda")
+    view = LY.make_view(0, 4, 2, 256, 128, L.SCR_W_BF16, 4, rows, sc)
+    y = torch.full((1, 256), 7.0, device="cuda")
+    cfg = L.grouped_moe_forward(view, 0, 0, 0, 0, 0, 0, 0, y, L.SCR_Y_F32, 0, 0, None,
+                                torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)

@@ -18,16 +18,17 @@ OUT_KEYS = ("distinct", "n_distinct", "n_miss", "n_total", "sorted_routes", "blo
 STATE_KEYS = ("slot_key", "slot_stamp", "key_to_slot", "clock", "stats", "decode_freq", "err")
 
 
-def _plan_both(S, NL, E, k, T, logits, fill, width, record_stats, layer=0, rec=4096, seed=11):
+def _plan_both(S, NL, E, k, T, logits, fill, width, record_stats, layer=0, rec=4096, seed=11, ids=None):
     """Runs the separate calls and the fused planner from the same bank state;
-    returns both (buffers, bank) pairs."""
+    returns both (buffers, bank) pairs.  ``ids`` (T, k) replaces routing the
+    logits (for expert counts beyond the router's limit)."""
     import slot_cache_routed_amd.layer as LY
     import slot_cache_routed_amd._lib as L
     pool = LY.HostPool(NL, E, rec, E, payload_of=lambda key: key % E)
     g = np.random.default_rng(seed)
     for p in range(E):
         pool.write_payload(p, g.integers(0, 256, size=rec, dtype=np.uint8))
-    dev = torch.from_numpy(np.ascontiguousarray(logits)).cuda()
+    dev = None if ids is not None else torch.from_numpy(np.ascontiguousarray(logits)).cuda()
     s = torch.cuda.current_stream().cuda_stream
     out = []
     for fused in (False, True):
@@ -35,7 +36,10 @@ def _plan_both(S, NL, E, k, T, logits, fill, width, record_stats, layer=0, rec=4
         if fill is not None:
             bank.load_fill(fill)
         buf = LY.LayerBuffers(T, E, k, 128, 128, S, 0, width=width)
-        L.route(dev, T, E, k, buf["topk_ids"], buf["topk_w"], s)
+        if ids is None:
+            L.route(dev, T, E, k, buf["topk_ids"], buf["topk_w"], s)
+        else:
+            buf["topk_ids"].copy_(torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).reshape(-1))
         if fused:
             assert LY.plan(buf, bank, pool, layer, record_stats)
         else:
@@ -116,3 +120,22 @@ def test_plan_reports_unsupported_shapes_without_launching():
     torch.cuda.synchronize()
     after = bank.snapshot()
     assert after["clock"] == before["clock"]
+
+
+def test_plan_at_its_largest_shape_against_the_oracle():
+    # 4096 routes, 8192 experts, 8192 slots, queries of 1024: the one-workgroup
+    # limits of the planner, with evictions (more distinct experts than free slots)
+    S, E, k, T, width = 8192, 8192, 8, 512, 1024
+    g = np.random.default_rng(8192)
+    ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    fill = W.bank_prefilled(3, S, 2, E, 6000, exclude_layer=1)
+    out = _plan_both(S, 2, E, k, T, None, fill, width, 1, layer=1, rec=256, ids=ids)
+    snap = _compare(out, "largest")
+    from oracle import dedup_sorted
+    distinct, nd, _ = dedup_sorted(ids.reshape(-1), E)
+    st = SlotBankState.from_fill(fill)
+    for q0 in range(0, len(distinct), width):
+        ensure_slots(st, 1, distinct[q0:q0 + width], True)
+    for key in ("slot_key", "slot_stamp", "key_to_slot", "clock", "stats", "decode_freq", "err"):
+        assert np.array_equal(np.asarray(snap[key]), np.asarray(getattr(st, key))), key
+    flush(f"plan at 4096 routes / 8192 experts / 8192 slots: {nd} distinct")

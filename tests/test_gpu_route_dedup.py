@@ -86,3 +86,15 @@ def test_dedup_short_prefill_has_160_and_ignores_invalid():
     ids = np.array([3, -1, 9, 3, 12, 0], np.int32)
     dist, cnt, inv = _dedup_gpu(ids, 10)
     assert cnt == 3 and dist.tolist() == [0, 3, 9, 10, 10, 10] and inv.tolist() == [1, -1, 2, 1, -1, 0]
+
+
+def test_route_signed_zeros_tie_and_minus_infinity():
+    # -0.0 and +0.0 are equal logits (ties go to the lower id); -inf logits are
+    # never chosen while finite ones remain
+    lg = np.array([[0.0, -0.0, -np.inf, 0.0, -1.0, -np.inf, -0.0, 2.0]] * 4, dtype=np.float32)
+    lg[1] = lg[1][::-1]
+    ids, w = _route_gpu(lg, 5)
+    rid, rw = route_topk_softmax(lg, 5)
+    assert np.array_equal(ids, rid)
+    assert ids[0].tolist() == [7, 0, 1, 3, 6]
+    assert np.array_equal(w.view(np.int32), rw.view(np.int32))
