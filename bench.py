@@ -241,16 +241,8 @@ def main():
     w13_bytes = 2 * I * H * 2
     gu_bytes = n_active * w13_bytes + R * H * 2 + R * I * 2
     achieved = gu_bytes / (gu * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            tr = json.load(f)
-        # counters describe the kernel as it was built when they were taken
-        src = os.path.join(ROOT, "slot_cache_routed_amd", "csrc", "gemm.hip")
-        with open(src, "rb") as f:
-            digest = hashlib.sha256(f.read()).hexdigest()[:16]
-        if tr.get("gemm_source_sha256_16") == digest:
-            traffic = tr.get("bytes_per_launch")
+    tr = _traffic_profile(args.traffic)
+    traffic = tr.get("bytes_per_launch") if tr is not None else None
 
     out = {
         "metric": METRIC,
@@ -297,6 +289,20 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out))
+
+
+def _traffic_profile(path: str):
+    """HBM bytes per launch from rocprofv3 counters (a JSON under profiles/),
+    or None when absent or taken on a different build of the GEMM source
+    (counters describe the kernel as it was built when they were taken)."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    src = os.path.join(ROOT, "slot_cache_routed_amd", "csrc", "gemm.hip")
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    return tr if tr.get("gemm_source_sha256_16") == digest else None
 
 
 def long_prefill(args) -> dict:
@@ -376,6 +382,20 @@ def long_prefill(args) -> dict:
     flops = 6.0 * R * H * I
     tflops = flops / ((gu + dn) * 1e-3) / 1e12
     wbytes = E * (rec - 256)
+    # algorithmic bytes per launch: every weight byte once, x read once and h
+    # written once (gate/up); h read once and the per-route bf16 rows written
+    # once (down)
+    w13 = E * (lay.w13_scale_off + (2 * I) * (H // 16) - lay.w13_off)
+    w2 = E * (lay.w2_scale_off + H * (I // 16) - lay.w2_off)
+    alg = {"gate_up": w13 + T * H * 2 + R * I * 2, "down": w2 + R * I * 2 + R * H * 2}
+    hbm = None
+    tr = _traffic_profile(os.path.join(ROOT, "profiles", "traffic_wide_long_prefill_4096.json"))
+    if tr is not None:
+        hbm = {}
+        for kname in ("gate_up", "down"):
+            b_meas = tr[kname]["bytes_per_launch"]
+            hbm[kname] = {"bytes_per_launch": b_meas, "algorithmic_bytes": alg[kname],
+                          "ratio": round(b_meas / alg[kname], 3)}
     return {
         "workload": f"long_prefill_4096: 4096 tokens, 512 experts, top-10, hidden 2048, intermediate 512, NVFP4 "
                     f"(e2m1 + e4m3/16 + fp32 global), {n_res} resident rows per layer, {NL} layers staged with "
@@ -389,6 +409,7 @@ def long_prefill(args) -> dict:
         "gemm_us_in_pipeline": {"gate_up": round(statistics.mean(x for r in reps for x in r[1]) * 1e3, 1),
                                 "down": round(statistics.mean(x for r in reps for x in r[2]) * 1e3, 1)},
         "weight_bytes_per_layer": wbytes,
+        "hbm_traffic": hbm,
     }
 
 

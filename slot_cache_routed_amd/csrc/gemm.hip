@@ -309,9 +309,29 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
   constexpr int D = WDT == SCR_W_NVFP4 ? 4 : 2;
   BFrag<WDT, NT> ring[D];
   AStage A0;
+  // down: the route and top-k weight of each output row of this lane, read
+  // before the K loop (their latency overlaps the first weight loads instead
+  // of following the last MFMA); clamped indices keep the loads unconditional
+  int out_route[GATEUP ? 1 : MTC][4];
+  float out_w[GATEUP ? 1 : MTC][4];
+  if (!GATEUP) {
+#pragma unroll
+    for (int mt = 0; mt < MTC; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out_route[mt][i] = a.sorted_routes[c.m0 + mt * 16 + grp * 4 + i];
+  }
 #pragma unroll
   for (int i = 0; i < D - 1; ++i) load_b(ring[i], min(i, nkb - 1));
   load_a(A0, 0);
+  if (!GATEUP) {
+#pragma unroll
+    for (int mt = 0; mt < MTC; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = out_route[mt][i];
+        out_w[mt][i] = a.topk_w[(r >= 0 && r < a.R) ? r : 0];
+      }
+  }
   store_a(A0, 0);
   __syncthreads();
   auto step = [&](int kb, const BFrag<WDT, NT>& bc, BFrag<WDT, NT>& bl) {
@@ -344,9 +364,9 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
           a.h[(size_t)pos * a.I + hc] = static_cast<bf16>(hv);
         }
       } else {
-        const int r = a.sorted_routes[pos];
+        const int r = out_route[mt][i];
         if (r >= 0 && r < a.R) {
-          const float w = a.topk_w[r];
+          const float w = out_w[mt][i];
           typedef typename RowT<WDT>::type OT;
           OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + c.ncol0 + col;
 #pragma unroll
@@ -480,7 +500,8 @@ struct BLoads {  // vector memory instructions per wave for one K block of weigh
 };
 
 template <int WDT, int MT, bool GATEUP, int EW, int NTW, int MTC>
-__device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row, bf16* As0, bf16* As1, bf16* As2,
+__device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row, const int* row_route,
+                                          const float* row_w, bf16* As0, bf16* As1, bf16* As2,
                                           bf16* As3, uint32_t* stg, int m0, __amdgpu_buffer_rsrc_t wrsrc,
                                           const int* toff0, const int* soff0, float gs, int nkb, int c_begin,
                                           int c_end) {
@@ -584,8 +605,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
       for (int mt = 0; mt < MTC; ++mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = a.sorted_routes[m0 + mt * 16 + grp * 4 + i];
-          const float w = (r >= 0 && r < a.R) ? a.topk_w[r] : 0.0f;
+          const float w = row_w[mt * 16 + grp * 4 + i];
 #pragma unroll
           for (int t = 0; t < NTW; ++t) so[(grp * 4 + i) * OC + 16 * t + col] = static_cast<OT>(w * (gs * acc[mt][t][i]));
         }
@@ -593,8 +613,8 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
         for (int rd = 0; rd < ROUNDS; ++rd) {
           const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
           const u32x4 v = *reinterpret_cast<const u32x4*>(so + (q < 16 * PPR ? rr : 0) * OC + pc * EPP);
-          const int r = q < 16 * PPR ? a.sorted_routes[m0 + mt * 16 + rr] : -1;
-          if (r >= 0 && r < a.R) {
+          const int r = q < 16 * PPR ? row_route[mt * 16 + rr] : -1;
+          if (r >= 0) {
             OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + ch * (OC * EW) + wave * OC + pc * EPP;
             *reinterpret_cast<u32x4*>(orow) = v;
             if (ch == 0 && wave == 0 && pc == 0) a.flags[r] = 1;
@@ -685,6 +705,10 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
   __shared__ __attribute__((aligned(1024))) bf16 As2[MT * 16 * kKB];
   __shared__ __attribute__((aligned(1024))) bf16 As3[MT * 16 * kKB];
   __shared__ int src_row[MT * 16];
+  // down: the route of each pass row (-1 for padding) and its top-k weight,
+  // read once per pass so that the epilogue does no dependent global loads
+  __shared__ int row_route[GATEUP ? 1 : MT * 16];
+  __shared__ float row_w[GATEUP ? 1 : MT * 16];
   __shared__ __attribute__((aligned(256))) uint32_t stg[EW * kWideStage / 4];  // per-wave epilogue tiles
   if (GATEUP) gateup_prologue(a);
   // XCD-aware order: all groups of bucket j run on XCD j mod 8
@@ -732,13 +756,19 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
         }
       }
       src_row[i] = off;
+      if (!GATEUP) {
+        const int r = i < rows ? a.sorted_routes[m0 + i] : -1;
+        const bool valid = r >= 0 && r < a.R;
+        row_route[i] = valid ? r : -1;
+        row_w[i] = valid ? a.topk_w[r] : 0.0f;
+      }
     }
     __syncthreads();
 #define SCR_WIDE_PASS(n)                                                                                   \
   case n:                                                                                                  \
     if constexpr (MT >= n)                                                                                 \
-      wide_pass<WDT, MT, GATEUP, EW, NTW, n>(a, src_row, As0, As1, As2, As3, stg, m0, wrsrc, toff0, soff0,   \
-                                             gs, nkb, c_begin, c_end);                                          \
+      wide_pass<WDT, MT, GATEUP, EW, NTW, n>(a, src_row, row_route, row_w, As0, As1, As2, As3, stg, m0, wrsrc, \
+                                             toff0, soff0, gs, nkb, c_begin, c_end);                            \
     break;
     switch (rows / 16) {
       SCR_WIDE_PASS(1)
