@@ -458,6 +458,25 @@ def decode_stream(args) -> dict:
     total = t_a.elapsed_ms(t_b)
     snap = bank.snapshot()
     hits, misses, evictions, queries = [int(v) for v in snap["stats"]]
+    del bank, buf
+    torch.cuda.empty_cache()
+    # the same steps from an empty bank, each step one replay of a graph holding
+    # every layer (inputs copied into the graph's static tensors first)
+    bank_g = LY.Bank(S, NL, E, L.SCR_W_BF16, rec)
+    step = LY.DecodeStepGraph(bank_g, pool, range(NL), T, E, (k, H, I), sc, width=128, record_stats=True,
+                              y_dtype=L.SCR_Y_BF16)
+    torch.cuda.synchronize()
+    t_a.record(s)
+    for st in range(steps):
+        for l in range(NL):
+            step.logits[l].copy_(logits[st][l])
+            step.x[l].copy_(xs[st][l])
+        step.replay()
+    t_b.record(s)
+    total_g = t_a.elapsed_ms(t_b)
+    snap_g = bank_g.snapshot()
+    same = all(np.array_equal(np.asarray(snap[key]), np.asarray(snap_g[key]))
+               for key in ("slot_key", "key_to_slot", "slot_stamp", "stats", "decode_freq", "clock"))
     return {
         "workload": f"decode_stream: {NL} layers x {E} experts, top-{k}, bf16, {S}-slot bank, {steps} steps of {T} "
                     f"tokens, Zipf(1.1) routing, from an empty bank",
@@ -466,7 +485,10 @@ def decode_stream(args) -> dict:
         "hit_rate": round(hits / max(1, hits + misses), 4),
         "misses": misses, "evictions": evictions, "queries": queries,
         "miss_copy_GBps_effective": round(misses * rec / (total * 1e-3) / 1e9, 2),
-        "note": "wall time of all layer-steps on the compute stream, PCIe-inclusive",
+        "step_ms_hip_graph": round(total_g / steps, 3),
+        "hip_graph_bank_identical": bool(same),
+        "note": "wall time of all layer-steps on the compute stream, PCIe-inclusive; step_ms_hip_graph replays "
+                "one graph per step holding every layer, from an empty bank, inputs copied in before each replay",
     }
 
 

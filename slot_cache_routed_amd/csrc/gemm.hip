@@ -152,6 +152,17 @@ __device__ __forceinline__ unsigned dq_pair(f32x2 v, float scale) {
   return __builtin_bit_cast(unsigned, r);
 }
 
+// two floats as a bf16 pair (round to nearest even), a in the low half.  The
+// empty asm keeps the compiler from splitting the pair back into two single
+// conversions when the halves are stored separately.
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+  unsigned p = __builtin_bit_cast(unsigned, r);
+  asm("" : "+v"(p));
+  return p;
+}
+
 // 8 e2m1 codes (one dword, low nibble first) times a block scale, as bf16
 __device__ __forceinline__ bf16x8 dequant8_hw(unsigned packed, float scale) {
   u32x4 out;
@@ -577,12 +588,17 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
       bf16* sh = reinterpret_cast<bf16*>(wst);
 #pragma unroll
       for (int mt = 0; mt < MTC; ++mt) {
+        // rows i and i + 1 of a lane converted as one bf16 pair, stored as halves
+        uint16_t* sh16 = reinterpret_cast<uint16_t*>(sh);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; i += 2)
 #pragma unroll
-          for (int t = 0; t < NTW / 2; ++t)
-            sh[(grp * 4 + i) * HC + 16 * t + col] =
-                static_cast<bf16>(silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]));
+          for (int t = 0; t < NTW / 2; ++t) {
+            const unsigned p = pack_bf16(silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]),
+                                         silu_mul(gs * acc[mt][t][i + 1], gs * acc[mt][t + NTW / 2][i + 1]));
+            sh16[(grp * 4 + i) * HC + 16 * t + col] = (uint16_t)p;
+            sh16[(grp * 4 + i + 1) * HC + 16 * t + col] = (uint16_t)(p >> 16);
+          }
 #pragma unroll
         for (int rd = 0; rd < ROUNDS; ++rd) {
           const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
@@ -603,11 +619,23 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
       OT* so = reinterpret_cast<OT*>(wst);
 #pragma unroll
       for (int mt = 0; mt < MTC; ++mt) {
+        // row weights carry the global scale; for bf16 rows, rows i and i + 1
+        // of a lane are converted as one pair and stored as halves
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float w = row_w[mt * 16 + grp * 4 + i];
+        for (int i = 0; i < 4; i += 2) {
+          const float w0 = row_w[mt * 16 + grp * 4 + i], w1 = row_w[mt * 16 + grp * 4 + i + 1];
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) so[(grp * 4 + i) * OC + 16 * t + col] = static_cast<OT>(w * (gs * acc[mt][t][i]));
+          for (int t = 0; t < NTW; ++t) {
+            const int o0 = (grp * 4 + i) * OC + 16 * t + col;
+            if constexpr (sizeof(OT) == 2) {
+              const unsigned p = pack_bf16(w0 * acc[mt][t][i], w1 * acc[mt][t][i + 1]);
+              reinterpret_cast<uint16_t*>(so)[o0] = (uint16_t)p;
+              reinterpret_cast<uint16_t*>(so)[o0 + OC] = (uint16_t)(p >> 16);
+            } else {
+              so[o0] = static_cast<OT>(w0 * acc[mt][t][i]);
+              so[o0 + OC] = static_cast<OT>(w1 * acc[mt][t][i + 1]);
+            }
+          }
         }
 #pragma unroll
         for (int rd = 0; rd < ROUNDS; ++rd) {
@@ -760,7 +788,7 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
         const int r = i < rows ? a.sorted_routes[m0 + i] : -1;
         const bool valid = r >= 0 && r < a.R;
         row_route[i] = valid ? r : -1;
-        row_w[i] = valid ? a.topk_w[r] : 0.0f;
+        row_w[i] = valid ? a.topk_w[r] * gs : 0.0f;  // the expert's global scale folded in
       }
     }
     __syncthreads();

@@ -300,6 +300,43 @@ def demand_layer(bank: Bank, pool: HostPool, layer: int, logits, x, input_scale,
     return buf
 
 
+class DecodeStepGraph:
+    """One decode step (the demand path of every listed layer) captured once
+    as a HIP graph and replayed.
+
+    The demand path holds no host sync (miss counts are read and the misses
+    copied on the device, grids are fixed by the layer's shape), so capture
+    enqueues nothing and every replay runs route, planning, miss copies and
+    the grouped GEMM of each layer against the bank's current state.  Inputs
+    are read from static tensors (``logits[i]`` f32 [T, E] and ``x[i]`` bf16
+    bits [T, H] of the i-th listed layer) that the caller fills before each
+    replay; layer i writes ``bufs[i]["y"]``."""
+
+    def __init__(self, bank: Bank, pool: HostPool, layers, T: int, E: int, shape, input_scale: torch.Tensor,
+                 width: int = 128, record_stats: bool = True, y_dtype: int = L.SCR_Y_BF16, fused: bool = False):
+        k, H, I = shape
+        self.layers = list(layers)
+        n = len(self.layers)
+        self.logits = torch.zeros((n, T, E), dtype=torch.float32, device=_DEV)
+        self.x = torch.zeros((n, T, H), dtype=torch.int16, device=_DEV)
+        self.bufs = [LayerBuffers(T, E, k, H, I, bank.S, bank.wdtype, width=width, y_dtype=y_dtype)
+                     for _ in self.layers]
+        self.graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(self.graph, stream=side):
+                for i, layer in enumerate(self.layers):
+                    demand_layer(bank, pool, layer, self.logits[i], self.x[i], input_scale, width=width,
+                                 record_stats=record_stats, buf=self.bufs[i], shape=shape, batched=True,
+                                 fused=fused)
+        torch.cuda.current_stream().wait_stream(side)
+
+    def replay(self):
+        """Runs the captured step on the current stream."""
+        self.graph.replay()
+
+
 class LayerStreamBuffer:
     """A device buffer holding every expert record of one layer, plus its row table."""
 

@@ -64,3 +64,55 @@ def test_captured_demand_step_replays_bitwise():
     se, sg = bank_e.snapshot(), bank_g.snapshot()
     for key in ("slot_key", "key_to_slot", "slot_stamp", "stats", "decode_freq", "clock"):
         assert np.array_equal(np.asarray(se[key]), np.asarray(sg[key])), key
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_captured_decode_step_of_all_layers_replays_bitwise(fused):
+    """A whole decode step (every layer's route, planning, miss copies and
+    GEMMs) in one graph, replayed over several steps with new inputs written
+    into its static tensors: the same outputs and bank as eager steps, with
+    hits and evictions (a bank smaller than the layers' experts)."""
+    import slot_cache_routed_amd._lib as L
+    import slot_cache_routed_amd.layer as LY
+    T, E, k, H, I, S, NL, steps = 4, 64, 6, 256, 128, 96, 5, 5
+    lay = LY.record_layout(L.SCR_W_BF16, H, I)
+    src = ExpertSource(57, H, I, "bf16")
+    pool = LY.HostPool(NL, E, lay.record_bytes, E, payload_of=lambda key: key % E)
+    fill_pool(pool, src, lay, range(E))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    sc = dev(np.ones(E, np.float32))
+    logits = [[dev(W.zipf_gumbel_logits(57, l, st, T, E)) for l in range(NL)] for st in range(steps)]
+    xs = [[dev(W.f32_to_bf16_bits(W.decode_activations(57, l, st, T, H)).view(np.int16)) for l in range(NL)]
+          for st in range(steps)]
+
+    bank_e = LY.Bank(S, NL, E, L.SCR_W_BF16, lay.record_bytes)
+    bufs_e = [LY.LayerBuffers(T, E, k, H, I, S, L.SCR_W_BF16, width=16, y_dtype=L.SCR_Y_BF16) for _ in range(NL)]
+    ref = []
+    for st in range(steps):
+        for l in range(NL):
+            LY.demand_layer(bank_e, pool, l, logits[st][l], xs[st][l], sc, width=16, record_stats=True,
+                            buf=bufs_e[l], shape=(k, H, I), batched=True, fused=fused)
+            ref.append(bufs_e[l]["y"].clone())
+    torch.cuda.synchronize()
+
+    bank_g = LY.Bank(S, NL, E, L.SCR_W_BF16, lay.record_bytes)
+    step = LY.DecodeStepGraph(bank_g, pool, range(NL), T, E, (k, H, I), sc, width=16, record_stats=True,
+                              y_dtype=L.SCR_Y_BF16, fused=fused)
+    torch.cuda.synchronize()
+    assert int(bank_g.clock.item()) == 0            # capture enqueued nothing
+    out = []
+    for st in range(steps):
+        for l in range(NL):
+            step.logits[l].copy_(logits[st][l])
+            step.x[l].copy_(xs[st][l])
+        step.replay()
+        torch.cuda.synchronize()
+        out.extend(step.bufs[l]["y"].clone() for l in range(NL))
+        _ = (xs[st][0].float() * 3).sum().item()    # eager work between replays
+    for i, (a, b) in enumerate(zip(ref, out)):
+        assert torch.equal(a, b), f"step {i // NL} layer {i % NL}"
+    se, sg = bank_e.snapshot(), bank_g.snapshot()
+    for key in ("slot_key", "key_to_slot", "slot_stamp", "stats", "decode_freq", "clock", "err"):
+        assert np.array_equal(np.asarray(se[key]), np.asarray(sg[key])), key
+    hits, misses, evictions, queries = [int(v) for v in sg["stats"]]
+    assert evictions > 0 and hits > 0 and queries == steps * NL * step.bufs[0].n_queries
