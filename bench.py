@@ -55,6 +55,8 @@ def _args():
     p.add_argument("--no-decode", action="store_true", help="skip the decode-stream measurement")
     p.add_argument("--decode-steps", type=int, default=48)
     p.add_argument("--no-align", action="store_true", help="skip the align measurements")
+    p.add_argument("--no-formats", action="store_true",
+                   help="skip the 4096-token grouped GEMM in every weight format (bf16, NVFP4, FP8, MXFP4)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gateup_short_prefill_96.json"),
                    help="HBM traffic of the dominant kernel from rocprofv3 counters (JSON), if present")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -284,6 +286,9 @@ def main():
     if not args.no_decode:
         out["decode_stream"] = decode_stream(args)
         torch.cuda.empty_cache()
+    if not args.no_formats:
+        out["formats_4096"] = formats_4096()
+        torch.cuda.empty_cache()
     if not args.no_align:
         out["align"] = align_bench()
     if not args.no_cpu:
@@ -411,6 +416,67 @@ def long_prefill(args) -> dict:
         "weight_bytes_per_layer": wbytes,
         "hbm_traffic": hbm,
     }
+
+
+def formats_4096() -> dict:
+    """The grouped GEMM of one 4096-token layer (512 experts, top-10, hidden
+    2048, intermediate 512, every expert resident in HBM) in each weight
+    format.  512 expert records alias 64 generated ones (the kernels read
+    every record's own bytes; aliasing only bounds the host set-up time)."""
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    import workloads as W
+    import slot_cache_routed_amd._lib as L
+    import slot_cache_routed_amd.layer as LY
+
+    cfg = W.C5
+    T, E, k, H, I = cfg.T, cfg.shape.E, cfg.shape.k, cfg.shape.H, cfg.shape.I
+    R, P = T * k, 64
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    lg = dev(W.logits_normal(cfg.seed, 0, T, E))
+    x = dev(W.f32_to_bf16_bits(W.activations_normal(cfg.seed, T, H)).view(np.int16))
+    sc = dev(np.ones(E, np.float32))
+    s = torch.cuda.current_stream().cuda_stream
+    fmts = (("bf16", L.SCR_W_BF16, lambda lay, p: LY.pack_record_bf16(lay, *W.expert_bf16(cfg.seed, p, H, I))),
+            ("nvfp4", L.SCR_W_NVFP4, lambda lay, p: LY.pack_record_nvfp4(lay, W.expert_nvfp4(cfg.seed, p, H, I))),
+            ("fp8", L.SCR_W_FP8, lambda lay, p: LY.pack_record_fp8(lay, W.expert_fp8(cfg.seed, p, H, I))),
+            ("mxfp4", L.SCR_W_MXFP4, lambda lay, p: LY.pack_record_mxfp4(lay, W.expert_mxfp4(cfg.seed, p, H, I))))
+    out = {"workload": "4096 tokens, 512 experts resident, top-10, hidden 2048, intermediate 512; "
+                       "TFLOP/s = 6*R*H*I / (gate/up + down)"}
+    flops = 6.0 * R * H * I
+    for name, code, pack in fmts:
+        lay = LY.record_layout(code, H, I)
+        rec = int(lay.record_bytes)
+        with ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+            recs = list(ex.map(lambda p: pack(lay, p), range(P)))
+        lb = LY.LayerStreamBuffer(E, rec)
+        host = torch.from_numpy(np.concatenate(recs))
+        for e0 in range(0, E, P):
+            lb.data[e0 * rec:(e0 + P) * rec].copy_(host)
+        b = LY.LayerBuffers(T, E, k, H, I, E, code, y_dtype=L.SCR_Y_BF16)
+        L.route(lg, T, E, k, b["topk_ids"], b["topk_w"], s)
+        LY.align(b, None, 0)
+        view = LY.make_view(0, E, k, H, I, code, E, lb.row_table, sc)
+        gus, dns = [], []
+        for i in range(12):
+            tm = [L.Timer() for _ in range(5)]
+            LY.forward(b, view, x, marks=[t.handle for t in tm])
+            torch.cuda.synchronize()
+            if i >= 2:
+                gus.append(tm[1].elapsed_ms(tm[2]))
+                dns.append(tm[2].elapsed_ms(tm[3]))
+        gu, dn = statistics.mean(gus), statistics.mean(dns)
+        wbytes = E * rec
+        out[name] = {"gate_up_us": round(gu * 1e3, 1), "down_us": round(dn * 1e3, 1),
+                     "gemm_tflops": round(flops / ((gu + dn) * 1e-3) / 1e12, 1),
+                     "frac_bf16_mfma_peak": round(flops / ((gu + dn) * 1e-3) / 1e12 / 2500.0, 4),
+                     "weight_bytes": wbytes, "weight_GBps": round(wbytes / ((gu + dn) * 1e-3) / 1e9, 1)}
+        _log(f"formats: {name} gate/up {gu * 1e3:.1f} us, down {dn * 1e3:.1f} us")
+        del lb, b, host, recs
+        torch.cuda.empty_cache()
+    return out
 
 
 def decode_stream(args) -> dict:

@@ -61,6 +61,8 @@ extern "C" {
 /* weight formats */
 #define SCR_W_BF16 0  /* bf16 rows                                          */
 #define SCR_W_NVFP4 1 /* e2m1 codes + e4m3 per-16 block scales + fp32 global */
+#define SCR_W_FP8 2   /* e4m3 codes + one fp32 scale per tensor               */
+#define SCR_W_MXFP4 3 /* e2m1 codes + e8m0 per-32 block scales (OCP MX)       */
 
 /* output dtypes of the layer */
 #define SCR_Y_F32 0
@@ -83,7 +85,18 @@ extern "C" {
  *                (one per 16 consecutive input columns of a row), w2 codes [H][I],
  *                w2 scales [H][I/16], then g13 f32, g2 f32 (global scales);
  *                record padded to 256 bytes.
- * Decoded weight = e2m1(code) * e4m3(scale) * global.
+ *                Decoded weight = e2m1(code) * e4m3(scale) * global.
+ *   SCR_W_FP8  : w13 e4m3 (OCP E4M3FN) codes [2I][H], w2 codes [H][I], then g13
+ *                f32, g2 f32 (one scale per tensor); padded to 256 bytes.
+ *                Decoded weight = e4m3(code) * scale.
+ *   SCR_W_MXFP4: w13 e2m1 codes [2I][H], w13 e8m0 scales [2I][H/32] (one per
+ *                32 consecutive input columns of a row), w2 codes [H][I], w2
+ *                scales [H][I/32]; no global scale; padded to 256 bytes.
+ *                Decoded weight = e2m1(code) * 2^(scale - 127) (scale codes
+ *                2..252: the products are exact bf16 values; 255 is NaN).
+ * The FP8 and MXFP4 formats follow the OCP Microscaling Formats specification
+ * (FreeToken PR #676, Known limits, names both for the prefill over the
+ * slots without describing them; the per-tensor FP8 scale is a reading).
  * Storage is tile-major so each load of the GEMM is one contiguous range: a
  * tensor of N rows and K columns is a sequence of tile-blocks (t, kb), t over
  * the N/16 row tiles, kb over the K/128 column blocks (t-major).  Inside a
@@ -92,6 +105,8 @@ extern "C" {
  *   codes  1024 B: code (r, 32 g + j) in byte 16 (16 g + r) + j / 2, low nibble = even j
  *   scales  128 B: scale (r, 2 g + h) (the 16-column block 8 kb + 2 g + h) at byte
  *                  2 (16 g + r) + h
+ *   fp8    2048 B: code (r, 32 g + j) at byte 1024 (j / 16) + 16 (16 g + r) + j % 16
+ *   mx scales 64 B: scale (r, g) (the 32-column block 4 kb + g) at byte 16 g + r
  * H and I must be multiples of 128.
  */
 typedef struct scr_record_layout {

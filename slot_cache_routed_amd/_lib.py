@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libscr.so")
 
 SCR_OK, SCR_EINVAL, SCR_ENOTSUP, SCR_ECAPACITY, SCR_EHIP = 0, -1, -2, -3, -4
 SCR_ERR_CAPACITY = 1
-SCR_W_BF16, SCR_W_NVFP4 = 0, 1
+SCR_W_BF16, SCR_W_NVFP4, SCR_W_FP8, SCR_W_MXFP4 = 0, 1, 2, 3
 SCR_Y_F32, SCR_Y_BF16 = 0, 1
 SCR_MAX_TOPK = 32
 SCR_MAX_EXPERTS = 4096

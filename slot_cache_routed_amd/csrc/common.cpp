@@ -51,6 +51,24 @@ extern "C" int scr_record_layout_of(int wdtype, int H, int I, scr_record_layout*
     out->record_bytes = (out->g2_off + 4 + 255) / 256 * 256;
     return SCR_OK;
   }
+  if (wdtype == SCR_W_FP8) {
+    out->w13_off = 0;
+    out->w2_off = 2 * i * h;
+    out->g13_off = out->w2_off + h * i;
+    out->g2_off = out->g13_off + 4;
+    out->w13_scale_off = out->w2_scale_off = 0;
+    out->record_bytes = (out->g2_off + 4 + 255) / 256 * 256;
+    return SCR_OK;
+  }
+  if (wdtype == SCR_W_MXFP4) {
+    out->w13_off = 0;
+    out->w13_scale_off = out->w13_off + 2 * i * h / 2;
+    out->w2_off = out->w13_scale_off + 2 * i * h / 32;
+    out->w2_scale_off = out->w2_off + h * i / 2;
+    out->g13_off = out->g2_off = 0;  // no global scales
+    out->record_bytes = (out->w2_scale_off + h * i / 32 + 255) / 256 * 256;
+    return SCR_OK;
+  }
   scr::set_error("record_layout: unknown wdtype %d", wdtype);
   return SCR_ENOTSUP;
 }

@@ -66,15 +66,40 @@ __device__ __forceinline__ float e4m3_to_f32(unsigned c) {
   return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
 }
 
-// per-route rows: fp32 for bf16 weights (their output tolerance is tighter),
-// bf16 for NVFP4 weights (half the bytes at the large-chunk shapes)
+// Weight formats: bytes of one tile-block (16 rows x 128 columns) of codes
+// and of its block scales, whether the record carries a per-tensor scale,
+// and the per-route row type: fp32 for bf16 weights (their output tolerance
+// is tighter), bf16 for the narrow formats (half the bytes at the
+// large-chunk shapes).
 template <int WDT>
-struct RowT {
-  typedef float type;
+struct WFmt;
+template <>
+struct WFmt<SCR_W_BF16> {
+  static constexpr int tile = 4096, stile = 0;
+  static constexpr bool gscale = false;
+  typedef float row_t;
 };
 template <>
-struct RowT<SCR_W_NVFP4> {
-  typedef __bf16 type;
+struct WFmt<SCR_W_NVFP4> {
+  static constexpr int tile = 1024, stile = 128;
+  static constexpr bool gscale = true;
+  typedef __bf16 row_t;
+};
+template <>
+struct WFmt<SCR_W_FP8> {
+  static constexpr int tile = 2048, stile = 0;
+  static constexpr bool gscale = true;
+  typedef __bf16 row_t;
+};
+template <>
+struct WFmt<SCR_W_MXFP4> {
+  static constexpr int tile = 1024, stile = 64;
+  static constexpr bool gscale = false;
+  typedef __bf16 row_t;
+};
+template <int WDT>
+struct RowT {
+  typedef typename WFmt<WDT>::row_t type;
 };
 
 struct GemmArgs {
@@ -131,13 +156,15 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // same bits).  MFMA step s (0..3) gives lane group g = lane / 16 eight columns:
 //   bf16 : 32 s + 8 g   (the natural layout: one load = 64 B of a row)
 //   NVFP4: 32 g + 8 s   (lane group g owns 32 consecutive codes = 16 B and
-//                        their two e4m3 scales, so one load covers them)
+//                        their two e4m3 scales, so one load covers them;
+//                        MXFP4 and FP8 the same: 16 B of codes and one e8m0
+//                        scale, or 32 B of fp8 codes in two loads)
 constexpr int kKB = 128;               // K block
 constexpr int kAStride = kKB + 8;      // LDS row stride (bf16): conflict-free b128 reads
 
 template <int WDT>
 __device__ __forceinline__ int kcol(int g, int s) {
-  return WDT == SCR_W_NVFP4 ? 32 * g + 8 * s : 32 * s + 8 * g;
+  return WDT == SCR_W_BF16 ? 32 * s + 8 * g : 32 * g + 8 * s;
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -234,6 +261,73 @@ struct BFrag<SCR_W_NVFP4, NT> {
   }
 };
 
+template <int NT>
+struct BFrag<SCR_W_FP8, NT> {
+  u32x4 raw[NT][2];  // 32 codes: columns 0..15 of the lane's group, then 16..31
+  template <bool STREAM = false>
+  __device__ __forceinline__ void load(const uint8_t* const* tile, const uint8_t* const*, int kb, int lane) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      raw[t][0] = ldg_w<STREAM, u32x4>(tile[t] + (size_t)kb * 2048 + lane * 16);
+      raw[t][1] = ldg_w<STREAM, u32x4>(tile[t] + (size_t)kb * 2048 + 1024 + lane * 16);
+    }
+  }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, const int* toff, const int*, int lane) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      raw[t][0] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, toff[t], kNonTemporal);
+      raw[t][1] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, toff[t] + 1024, kNonTemporal);
+    }
+  }
+  // step s: codes 8 s .. 8 s + 7, exact in bf16 (the tensor scale is applied
+  // to the accumulator)
+  __device__ __forceinline__ bf16x8 get(int t, int st) const {
+    const unsigned d0 = raw[t][st >> 1][2 * (st & 1)], d1 = raw[t][st >> 1][2 * (st & 1) + 1];
+    u32x4 out;
+    out[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, false));
+    out[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, 1.0f, true));
+    out[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, false));
+    out[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, 1.0f, true));
+    return __builtin_bit_cast(bf16x8, out);
+  }
+  __device__ __forceinline__ bf16x8 get_hw(int t, int st) const { return get(t, st); }
+};
+
+template <int NT>
+struct BFrag<SCR_W_MXFP4, NT> {
+  u32x4 codes[NT];  // 32 codes: step s uses dword s
+  unsigned sc[NT];  // the group's e8m0 scale code
+  template <bool STREAM = false>
+  __device__ __forceinline__ void load(const uint8_t* const* tile, const uint8_t* const* stile, int kb, int lane) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      codes[t] = ldg_w<STREAM, u32x4>(tile[t] + (size_t)kb * 1024 + lane * 16);
+      sc[t] = ldg_w<STREAM, uint8_t>(stile[t] + (size_t)kb * 64 + lane);
+    }
+  }
+  __device__ __forceinline__ void load_buf(__amdgpu_buffer_rsrc_t r, const int* toff, const int* soff, int lane) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      codes[t] = __builtin_amdgcn_raw_buffer_load_b128(r, lane * 16, toff[t], kNonTemporal);
+      sc[t] = __builtin_amdgcn_raw_buffer_load_b8(r, lane, soff[t], kNonTemporal);
+    }
+  }
+  // the conversion's scale operand contributes its exponent field only, which
+  // is exactly the e8m0 code: value = e2m1 * 2^(code - 127), rounded to bf16
+  // (exact for scale codes 2..252)
+  __device__ __forceinline__ bf16x8 get(int t, int st) const {
+    const float scale = __builtin_bit_cast(float, (sc[t] & 0xFFu) << 23);
+    const unsigned c = codes[t][st];
+    u32x4 out;
+    out[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 0));
+    out[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 1));
+    out[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 2));
+    out[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3));
+    return __builtin_bit_cast(bf16x8, out);
+  }
+  __device__ __forceinline__ bf16x8 get_hw(int t, int st) const { return get(t, st); }
+};
+
 struct PassCtx {
   int tid, lane, wave, col, grp, rows, m0, nkb, ncol0, tx;
   bool active;
@@ -317,7 +411,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
   // LDS store does not wait behind the weight loads (the load counter is in
   // order).  Past the last block the loads are clamped to it (redundant, in
   // bounds).  The ring is indexed by compile-time constants.
-  constexpr int D = WDT == SCR_W_NVFP4 ? 4 : 2;
+  constexpr int D = WDT == SCR_W_BF16 ? 2 : 4;
   BFrag<WDT, NT> ring[D];
   AStage A0;
   // down: the route and top-k weight of each output row of this lane, read
@@ -420,7 +514,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
   const uint8_t* rowp[NT];
   const uint8_t* scp[NT];
   const int K_blocks = K / kKB;
-  const size_t tile_bytes = WDT == SCR_W_NVFP4 ? 1024 : 4096;  // per tile-block
+  const size_t tile_bytes = WFmt<WDT>::tile;   // per tile-block
+  const size_t stile_bytes = WFmt<WDT>::stile;
   if (GATEUP) {
     // tiles 0..NT/2-1: gate rows; NT/2..NT-1: the matching up rows
     c.ncol0 = tx * (4 * 8 * NT) + c.wave * (8 * NT);
@@ -430,7 +525,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
       const int row0 = (t < NT / 2 ? 0 : a.I) + (c.active ? c.ncol0 + 16 * (t % (NT / 2)) : 0);
       const size_t tb = (size_t)(row0 / 16) * K_blocks;
       rowp[t] = rec + a.lay.w13_off + tb * tile_bytes;
-      scp[t] = rec + a.lay.w13_scale_off + tb * 128;
+      scp[t] = rec + a.lay.w13_scale_off + tb * stile_bytes;
     }
   } else {
     c.ncol0 = tx * (4 * 16 * NT) + c.wave * (16 * NT);
@@ -440,11 +535,11 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
       const int row0 = c.active ? c.ncol0 + 16 * t : 0;
       const size_t tb = (size_t)(row0 / 16) * K_blocks;
       rowp[t] = rec + a.lay.w2_off + tb * tile_bytes;
-      scp[t] = rec + a.lay.w2_scale_off + tb * 128;
+      scp[t] = rec + a.lay.w2_scale_off + tb * stile_bytes;
     }
   }
-  c.gs = WDT == SCR_W_NVFP4 ? *reinterpret_cast<const float*>(rec + (GATEUP ? a.lay.g13_off : a.lay.g2_off))
-                            : 1.0f;
+  c.gs = WFmt<WDT>::gscale ? *reinterpret_cast<const float*>(rec + (GATEUP ? a.lay.g13_off : a.lay.g2_off))
+                           : 1.0f;
   const int arow_len = K;  // elements per activation row
 
   for (int m0 = p0; m0 < p1; m0 += MT * 16) {
@@ -507,7 +602,7 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
 
 template <int WDT, int NTW>
 struct BLoads {  // vector memory instructions per wave for one K block of weights
-  static constexpr int value = WDT == SCR_W_NVFP4 ? 2 * NTW : 4 * NTW;
+  static constexpr int value = WDT == SCR_W_BF16 ? 4 * NTW : 2 * NTW;  // fp8: two code loads; fp4: codes + scales
 };
 
 template <int WDT, int MT, bool GATEUP, int EW, int NTW, int MTC>
@@ -520,7 +615,8 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   constexpr int CT = GATEUP ? EW * NTW / 2 : EW * NTW;  // row tiles per chunk and tensor half
-  constexpr int tile_bytes = WDT == SCR_W_NVFP4 ? 1024 : 4096;
+  constexpr int tile_bytes = WFmt<WDT>::tile;
+  constexpr int stile_bytes = WFmt<WDT>::stile;
   bf16* const bufs[kWideBufs] = {As0, As1, As2, As3};
 
   // activations through a buffer resource over x (gate/up) or h (down)
@@ -560,7 +656,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       tp[t] = toff0[t] + blk * tile_bytes;
-      sp[t] = soff0[t] + blk * 128;
+      sp[t] = soff0[t] + blk * stile_bytes;
     }
     f.load_buf(wrsrc, tp, sp, lane);
   };
@@ -654,7 +750,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
 
   // weight ring depth (blocks): HBM latency under load is about two blocks
   // of compute, so the weights of block s are requested at block s - D + 1
-  constexpr int D = WDT == SCR_W_NVFP4 ? kWideRing : 2;
+  constexpr int D = WDT == SCR_W_BF16 ? 2 : kWideRing;
   constexpr int U = D > kWideBufs ? D : kWideBufs;  // unroll: ring and buffers indexed statically
   constexpr int NB = BLoads<WDT, NTW>::value;
   const int s0 = c_begin * nkb, s1 = c_end * nkb;  // flat steps s = chunk * nkb + kb
@@ -757,7 +853,8 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
   // the record as a buffer (every weight load is range-checked against it)
   const __amdgpu_buffer_rsrc_t wrsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, (int)a.lay.record_bytes, 0x00020000);
-  constexpr int tile_bytes = WDT == SCR_W_NVFP4 ? 1024 : 4096;
+  constexpr int tile_bytes = WFmt<WDT>::tile;
+  constexpr int stile_bytes = WFmt<WDT>::stile;
   // byte offsets of tile-block (t, 0) of this wave's tiles in chunk 0 (wave-uniform)
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   int toff0[NTW], soff0[NTW];
@@ -766,9 +863,9 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
     const int row0 = GATEUP ? (t < NTW / 2 ? 0 : a.I) + wv * 8 * NTW + 16 * (t % (NTW / 2)) : wv * 16 * NTW + 16 * t;
     const int tb = (row0 / 16) * nkb;
     toff0[t] = (int)(GATEUP ? a.lay.w13_off : a.lay.w2_off) + tb * tile_bytes;
-    soff0[t] = (int)(GATEUP ? a.lay.w13_scale_off : a.lay.w2_scale_off) + tb * 128;
+    soff0[t] = (int)(GATEUP ? a.lay.w13_scale_off : a.lay.w2_scale_off) + tb * stile_bytes;
   }
-  const float gs = WDT == SCR_W_NVFP4
+  const float gs = WFmt<WDT>::gscale
                        ? *reinterpret_cast<const float*>(rec + (GATEUP ? a.lay.g13_off : a.lay.g2_off))
                        : 1.0f;
   for (int m0 = p0; m0 < p1; m0 += MT * 16) {
@@ -881,7 +978,7 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
   w.h_rows = (int)rows;
   w.h_off = 0;
   w.o_off = align256(w.h_off + (size_t)rows * I * sizeof(uint16_t));
-  const size_t row_bytes = wdtype == SCR_W_NVFP4 ? sizeof(uint16_t) : sizeof(float);
+  const size_t row_bytes = wdtype == SCR_W_BF16 ? sizeof(float) : sizeof(uint16_t);
   w.flags_off = align256(w.o_off + (size_t)R * H * row_bytes);
   w.bytes = align256(w.flags_off + (size_t)R * sizeof(int32_t));
   return w;
@@ -890,14 +987,14 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
 constexpr int kWideWaves = 8;  // two waves per SIMD in one workgroup per CU
 template <int WDT>
 struct WideNT {  // row tiles per wave: the bf16 weight ring holds four times the registers
-  static constexpr int value = WDT == SCR_W_NVFP4 ? 4 : 2;
+  static constexpr int value = WDT == SCR_W_BF16 ? 2 : 4;
 };
 
 template <int WDT>
 static bool wide_gemms_fit(const GemmArgs& a) {
   constexpr int NTW = WideNT<WDT>::value;
   // K blocks cycle through the LDS buffers and the weight ring in steps of U
-  constexpr int U = WDT == SCR_W_NVFP4 ? (kWideRing > kWideBufs ? kWideRing : kWideBufs) : kWideBufs;
+  constexpr int U = WDT == SCR_W_BF16 ? kWideBufs : (kWideRing > kWideBufs ? kWideRing : kWideBufs);
   return (a.H / kKB) % U == 0 && (a.I / kKB) % U == 0 && a.I % (8 * NTW * kWideWaves) == 0 &&
          a.H % (16 * NTW * kWideWaves) == 0;
 }
@@ -939,12 +1036,23 @@ static int launch_gemms(const GemmArgs& a, int max_active, hipEvent_t* marks, hi
   return SCR_OK;
 }
 
+// few rows per expert: the small-M kernels; many: the wide-tile kernels when
+// the shape fits them, else the small-M kernels with 112-row passes
+template <int WDT>
+static int run_gemms(const scr_tile_cfg& cfg, const GemmArgs& a, int max_active, hipEvent_t* marks,
+                     hipStream_t s) {
+  if (cfg.m_chunk == 32) return launch_gemms<WDT, 2, 2>(a, max_active, marks, s);
+  if (wide_gemms_fit<WDT>(a)) return launch_wide_gemms<WDT, 7>(a, max_active, marks, s);
+  return launch_gemms<WDT, 7, 2>(a, max_active, marks, s);
+}
+
 }  // namespace scr
 
 extern "C" int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_cfg* cfg) {
   SCR_CHECK_ARG(cfg != nullptr, "tile_config: cfg is null");
   SCR_CHECK_ARG(T >= 0 && k >= 1 && E_layer >= 1, "tile_config: bad T, k or E");
-  SCR_CHECK_ARG(wdtype == SCR_W_BF16 || wdtype == SCR_W_NVFP4, "tile_config: unknown wdtype");
+  SCR_CHECK_ARG(wdtype == SCR_W_BF16 || wdtype == SCR_W_NVFP4 || wdtype == SCR_W_FP8 || wdtype == SCR_W_MXFP4,
+                "tile_config: unknown wdtype");
   // rows per expert of the routed layer (never of the bank)
   const long long per_expert = ((long long)T * k + E_layer - 1) / E_layer;
   cfg->block_m = 16;
@@ -979,7 +1087,9 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   SCR_CHECK_ARG(H >= 128 && H % 128 == 0 && H <= 16384, "forward: H must be a multiple of 128 in [128, 16384]");
   SCR_CHECK_ARG(I >= 128 && I % 128 == 0 && I <= 16384, "forward: I must be a multiple of 128 in [128, 16384]");
   SCR_CHECK_ARG(view->num_buckets >= 1 && view->bucket_rows && view->input_scale, "forward: bad view");
-  SCR_CHECK_ARG(view->wdtype == SCR_W_BF16 || view->wdtype == SCR_W_NVFP4, "forward: unknown wdtype");
+  SCR_CHECK_ARG(view->wdtype == SCR_W_BF16 || view->wdtype == SCR_W_NVFP4 || view->wdtype == SCR_W_FP8 ||
+                    view->wdtype == SCR_W_MXFP4,
+                "forward: unknown wdtype");
   SCR_CHECK_ARG(y_dtype == SCR_Y_F32 || y_dtype == SCR_Y_BF16, "forward: unknown y dtype");
   SCR_CHECK_ARG(T >= 0 && (long long)T * k < (1ll << 30) && (long long)T * H < (1ll << 31),
                 "forward: T out of range");
@@ -1029,21 +1139,18 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
 
   // the grid covers at most min(R, E_layer) active buckets: a layer size
   const int max_active = R < E ? R : E;
-  if (view->wdtype == SCR_W_BF16) {
-    rc = cfg.m_chunk == 32                              ? scr::launch_gemms<SCR_W_BF16, 2, 2>(a, max_active, marks, stream)
-         : scr::wide_gemms_fit<SCR_W_BF16>(a)      ? scr::launch_wide_gemms<SCR_W_BF16, 7>(a, max_active, marks, stream)
-                                                    : scr::launch_gemms<SCR_W_BF16, 7, 2>(a, max_active, marks, stream);
-  } else {
-    rc = cfg.m_chunk == 32                               ? scr::launch_gemms<SCR_W_NVFP4, 2, 2>(a, max_active, marks, stream)
-         : scr::wide_gemms_fit<SCR_W_NVFP4>(a)      ? scr::launch_wide_gemms<SCR_W_NVFP4, 7>(a, max_active, marks, stream)
-                                                     : scr::launch_gemms<SCR_W_NVFP4, 7, 2>(a, max_active, marks, stream);
+  switch (view->wdtype) {
+    case SCR_W_BF16: rc = scr::run_gemms<SCR_W_BF16>(cfg, a, max_active, marks, stream); break;
+    case SCR_W_NVFP4: rc = scr::run_gemms<SCR_W_NVFP4>(cfg, a, max_active, marks, stream); break;
+    case SCR_W_FP8: rc = scr::run_gemms<SCR_W_FP8>(cfg, a, max_active, marks, stream); break;
+    default: rc = scr::run_gemms<SCR_W_MXFP4>(cfg, a, max_active, marks, stream); break;
   }
   if (rc) return rc;
 
   const size_t total = (size_t)T * (H / 8);
   int cgrid = (int)((total + 255) / 256);
   if (cgrid > 4096) cgrid = 4096;
-  if (view->wdtype == SCR_W_NVFP4) {
+  if (view->wdtype != SCR_W_BF16) {
     const scr::bf16* o = static_cast<const scr::bf16*>(a.o);
     if (y_dtype == SCR_Y_BF16)
       hipLaunchKernelGGL((scr::combine_kernel<scr::bf16, true>), dim3(cgrid), dim3(256), 0, stream, o, a.flags, T, k, H, y);

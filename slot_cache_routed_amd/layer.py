@@ -67,6 +67,20 @@ def tile_fp4_scales(sc: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(w.transpose(0, 2, 3, 1, 4)).reshape(-1)
 
 
+def tile_fp8(q: np.ndarray) -> np.ndarray:
+    """fp8 codes [N][K] -> [t][kb][half h][group g][row r][16 bytes], column 128 kb + 32 g + 16 h + j."""
+    N, K = q.shape
+    w = np.ascontiguousarray(q, np.uint8).reshape(N // 16, 16, K // 128, 4, 2, 16)
+    return np.ascontiguousarray(w.transpose(0, 2, 4, 3, 1, 5)).reshape(-1)
+
+
+def tile_mx_scales(sc: np.ndarray) -> np.ndarray:
+    """e8m0 scales [N][K/32] -> [t][kb][group g][row r], scale 4 kb + g."""
+    N, Ks = sc.shape
+    w = np.ascontiguousarray(sc, np.uint8).reshape(N // 16, 16, Ks // 4, 4)
+    return np.ascontiguousarray(w.transpose(0, 2, 3, 1)).reshape(-1)
+
+
 def pack_record_bf16(lay: L.RecordLayout, w13_bits: np.ndarray, w2_bits: np.ndarray) -> np.ndarray:
     """Lays out one bf16 expert record (uint8 [record_bytes])."""
     rec = np.zeros(lay.record_bytes, np.uint8)
@@ -86,6 +100,27 @@ def pack_record_nvfp4(lay: L.RecordLayout, d: dict) -> np.ndarray:
         rec[off:off + a.size] = a
     rec[lay.g13_off:lay.g13_off + 4] = np.array([d["g13"]], np.float32).view(np.uint8)
     rec[lay.g2_off:lay.g2_off + 4] = np.array([d["g2"]], np.float32).view(np.uint8)
+    return rec
+
+
+def pack_record_fp8(lay: L.RecordLayout, d: dict) -> np.ndarray:
+    """Lays out one FP8 expert record from e4m3 codes and per-tensor scales."""
+    rec = np.zeros(lay.record_bytes, np.uint8)
+    for key, off in (("w13_q", lay.w13_off), ("w2_q", lay.w2_off)):
+        a = tile_fp8(d[key])
+        rec[off:off + a.size] = a
+    rec[lay.g13_off:lay.g13_off + 4] = np.array([d["g13"]], np.float32).view(np.uint8)
+    rec[lay.g2_off:lay.g2_off + 4] = np.array([d["g2"]], np.float32).view(np.uint8)
+    return rec
+
+
+def pack_record_mxfp4(lay: L.RecordLayout, d: dict) -> np.ndarray:
+    """Lays out one MXFP4 expert record from e2m1 codes and e8m0 block scales."""
+    rec = np.zeros(lay.record_bytes, np.uint8)
+    for key, off, fn in (("w13_q", lay.w13_off, tile_fp4_codes), ("w13_s", lay.w13_scale_off, tile_mx_scales),
+                         ("w2_q", lay.w2_off, tile_fp4_codes), ("w2_s", lay.w2_scale_off, tile_mx_scales)):
+        a = fn(d[key])
+        rec[off:off + a.size] = a
     return rec
 
 

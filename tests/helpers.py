@@ -12,6 +12,7 @@ import numpy as np
 import workloads as W
 from oracle.mlp import bf16_bits_to_f64
 from oracle.nvfp4 import dequant_nvfp4
+from oracle.lowbit import dequant_fp8, dequant_mxfp4
 
 N_THREADS = min(16, os.cpu_count() or 4)
 
@@ -35,6 +36,10 @@ class ExpertSource:
     def raw(self, payload):
         if self.wdtype == "nvfp4":
             return W.expert_nvfp4(self.seed, payload, self.H, self.I)
+        if self.wdtype == "fp8":
+            return W.expert_fp8(self.seed, payload, self.H, self.I)
+        if self.wdtype == "mxfp4":
+            return W.expert_mxfp4(self.seed, payload, self.H, self.I)
         if self.wdtype == "fp32":
             w13, w2 = W.expert_f32(self.seed, payload, self.H, self.I)
             return W.f32_to_bf16_bits(w13), W.f32_to_bf16_bits(w2)
@@ -47,6 +52,10 @@ class ExpertSource:
         r = self.raw(payload)
         if self.wdtype == "nvfp4":
             out = (dequant_nvfp4(r["w13_q"], r["w13_s"], r["g13"]), dequant_nvfp4(r["w2_q"], r["w2_s"], r["g2"]))
+        elif self.wdtype == "fp8":
+            out = (dequant_fp8(r["w13_q"], r["g13"]), dequant_fp8(r["w2_q"], r["g2"]))
+        elif self.wdtype == "mxfp4":
+            out = (dequant_mxfp4(r["w13_q"], r["w13_s"]), dequant_mxfp4(r["w2_q"], r["w2_s"]))
         else:
             out = (bf16_bits_to_f64(r[0]), bf16_bits_to_f64(r[1]))
         if len(self._cache) < 64:
@@ -62,11 +71,23 @@ def fill_pool(pool, src: ExpertSource, lay, payloads):
 
     def one(p):
         r = src.raw(p)
-        rec = LY.pack_record_nvfp4(lay, r) if src.wdtype == "nvfp4" else LY.pack_record_bf16(lay, r[0], r[1])
+        if src.wdtype == "nvfp4":
+            rec = LY.pack_record_nvfp4(lay, r)
+        elif src.wdtype == "fp8":
+            rec = LY.pack_record_fp8(lay, r)
+        elif src.wdtype == "mxfp4":
+            rec = LY.pack_record_mxfp4(lay, r)
+        else:
+            rec = LY.pack_record_bf16(lay, r[0], r[1])
         pool.write_payload(p, rec)
 
     with ThreadPoolExecutor(N_THREADS) as ex:
         list(ex.map(one, payloads))
+
+
+def wdtype_code(wd):
+    import slot_cache_routed_amd._lib as L
+    return {"nvfp4": L.SCR_W_NVFP4, "fp8": L.SCR_W_FP8, "mxfp4": L.SCR_W_MXFP4}.get(wd, L.SCR_W_BF16)
 
 
 def rms(a):

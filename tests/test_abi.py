@@ -52,6 +52,11 @@ def test_record_layouts(lib):
     f = L.record_layout_of(L.SCR_W_NVFP4, 2048, 512)
     assert f.w13_scale_off == 1 << 20 and f.w2_off == (1 << 20) + (128 << 10)
     assert f.g13_off == 1769472 and f.record_bytes % 256 == 0 and f.record_bytes >= 1769472 + 8
+    p = L.record_layout_of(L.SCR_W_FP8, 2048, 512)
+    assert p.w2_off == 2 << 20 and p.g13_off == 3 << 20 and p.record_bytes == (3 << 20) + 256
+    m = L.record_layout_of(L.SCR_W_MXFP4, 2048, 512)
+    assert m.w13_scale_off == 1 << 20 and m.w2_off == (1 << 20) + (64 << 10)
+    assert m.w2_scale_off == m.w2_off + (512 << 10) and m.record_bytes == m.w2_scale_off + (32 << 10)
 
 
 def test_align_capacity_formula(lib):
@@ -74,6 +79,7 @@ def test_align_capacity_formula(lib):
     lambda: L.align_blocks(1, 10, None, 0, 8, 16, 1, 1, 1, 1, 1, 1, 1, 4, None),         # tiny workspace
     lambda: L.tile_config(1, 0, 8, 0),
     lambda: L.tile_config(1, 1, 8, 7),
+    lambda: L.tile_config(1, 1, 8, 4),                        # no format 4
 ])
 def test_bad_arguments_are_rejected_before_any_launch(lib, call):
     with pytest.raises(L.ScrError) as ei:

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import workloads as W
-from helpers import ExpertSource, fill_pool, flush, rel_max_err
+from helpers import ExpertSource, fill_pool, flush, rel_max_err, wdtype_code
 from oracle import moe_layer, moe_layer_tokens, route_topk_softmax
 from oracle.mlp import bf16_bits_to_f64
 
@@ -37,7 +37,7 @@ def _setup(name, S=None, W_=None, prefill=None, wdtype=None, T=None, E=None, k=N
     S = S or cfg.S
     NL = NL or cfg.L
     seed = cfg.seed if cfg else 77
-    wcode = L.SCR_W_NVFP4 if wd == "nvfp4" else L.SCR_W_BF16
+    wcode = wdtype_code(wd)
     lay = LY.record_layout(wcode, H, I)
     src = ExpertSource(seed, H, I, wd)
     flush(f"setup {name}: T={T} E={E} k={k} H={H} I={I} {wd} S={S} layers={NL}")
@@ -164,17 +164,21 @@ def test_layer_view_one_layer_cache_three_per_query():
 
 # the last two take the wide-tile kernels (I = 512, many rows per expert; at
 # 1500 routes over 12 experts some buckets need a second M pass)
+# Narrow formats (NVFP4; FP8 with a per-tensor scale; MXFP4 with e8m0 block
+# scales): every shape above for each, decoded in the GEMM against the
+# oracle's table decode
+@pytest.mark.parametrize("wd", ["nvfp4", "fp8", "mxfp4"])
 @pytest.mark.parametrize("T,E,k,H,I", [(64, 16, 4, 256, 128), (200, 32, 6, 512, 256), (37, 8, 3, 256, 128),
                                        (384, 16, 4, 512, 512), (500, 12, 3, 1024, 512)])
-def test_nvfp4_layer_vs_oracle_and_stream(T, E, k, H, I):
-    s = _setup(f"fp4_{T}_{E}", S=2 * E, W_=8, wdtype="nvfp4", T=T, E=E, k=k, H=H, I=I, NL=2)
+def test_narrow_format_layer_vs_oracle_and_stream(wd, T, E, k, H, I):
+    s = _setup(f"{wd}_{T}_{E}", S=2 * E, W_=8, wdtype=wd, T=T, E=E, k=k, H=H, I=I, NL=2)
     bank = _bank_for(s)
     sc = np.ones(E, np.float32)
     d = _run_demand(s, bank, sc)
     y = _y(d)
     y_ref, _, _ = _oracle(s)
     err = rel_max_err(y, y_ref)
-    flush(f"nvfp4 {T}x{E} k={k} H={H} I={I}: rel max err = {err:.3e}")
+    flush(f"{wd} {T}x{E} k={k} H={H} I={I}: rel max err = {err:.3e}")
     assert err <= TOL_FP4
     st = _run_stream(s, sc)
     assert torch.equal(d["y"], st["y"])

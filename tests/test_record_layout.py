@@ -51,3 +51,46 @@ def test_records_are_permutations_of_the_tensors():
     a, b = W.expert_bf16(3, 0, 256, 128)
     rec = LY.pack_record_bf16(lay, a, b)
     assert np.array_equal(np.sort(rec[lay.w2_off:].view(np.uint16)), np.sort(b.reshape(-1)))
+
+
+def test_fp8_tiles_follow_the_documented_formula():
+    g = np.random.default_rng(2)
+    N, K = 32, 384
+    nk = K // 128
+    q = g.integers(0, 256, size=(N, K), dtype=np.uint8)
+    t = LY.tile_fp8(q)
+    n, k = np.meshgrid(np.arange(N), np.arange(K), indexing="ij")
+    tb, r, kb, kk = n // 16, n % 16, k // 128, k % 128
+    gg, j = kk // 32, kk % 32
+    off = (tb * nk + kb) * 2048 + 1024 * (j // 16) + 16 * (16 * gg + r) + j % 16
+    assert np.array_equal(t[off], q)
+
+
+def test_mx_scale_tiles_follow_the_documented_formula():
+    g = np.random.default_rng(3)
+    N, K = 48, 256
+    nk = K // 128
+    sc = g.integers(0, 255, size=(N, K // 32), dtype=np.uint8)
+    t = LY.tile_mx_scales(sc)
+    n, b = np.meshgrid(np.arange(N), np.arange(K // 32), indexing="ij")
+    tb, r, kb, gg = n // 16, n % 16, b // 4, b % 4
+    assert np.array_equal(t[(tb * nk + kb) * 64 + 16 * gg + r], sc)
+
+
+def test_fp8_and_mxfp4_records():
+    import slot_cache_routed_amd._lib as L
+    import workloads as W
+    lay = L.record_layout_of(L.SCR_W_FP8, 256, 128)
+    assert lay.w2_off == 2 * 128 * 256 and lay.g13_off == lay.w2_off + 256 * 128 and lay.g2_off == lay.g13_off + 4
+    assert lay.record_bytes % 256 == 0 and lay.record_bytes >= lay.g2_off + 4
+    d = W.expert_fp8(3, 0, 256, 128)
+    rec = LY.pack_record_fp8(lay, d)
+    assert np.array_equal(np.sort(rec[lay.w2_off:lay.g13_off]), np.sort(d["w2_q"].reshape(-1)))
+    assert rec[lay.g2_off:lay.g2_off + 4].view(np.float32)[0] == d["g2"]
+    lay = L.record_layout_of(L.SCR_W_MXFP4, 256, 128)
+    assert lay.w13_scale_off == 128 * 256 and lay.w2_off == lay.w13_scale_off + 2 * 128 * 256 // 32
+    assert lay.w2_scale_off == lay.w2_off + 256 * 128 // 2 and lay.g13_off == 0
+    d = W.expert_mxfp4(3, 0, 256, 128)
+    rec = LY.pack_record_mxfp4(lay, d)
+    assert rec.size == lay.record_bytes
+    assert np.array_equal(np.sort(rec[lay.w13_scale_off:lay.w2_off]), np.sort(d["w13_s"].reshape(-1)))
