@@ -63,6 +63,7 @@ extern "C" {
 #define SCR_W_NVFP4 1 /* e2m1 codes + e4m3 per-16 block scales + fp32 global */
 #define SCR_W_FP8 2   /* e4m3 codes + one fp32 scale per tensor               */
 #define SCR_W_MXFP4 3 /* e2m1 codes + e8m0 per-32 block scales (OCP MX)       */
+#define SCR_W_MXFP4_A8 4 /* MXFP4 records; activations quantised to MXFP8 (W4A8) */
 
 /* output dtypes of the layer */
 #define SCR_Y_F32 0
@@ -305,7 +306,8 @@ int scr_align_blocks(const int32_t* ids, int n, const int32_t* id_to_bucket, int
  * layer's experts, never by the slot count]. */
 int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_cfg* cfg);
 /* workspace of scr_grouped_moe_forward: h [cap][I] bf16 + per-route rows [T*k][H]
- * (fp32 for bf16 weights, bf16 for NVFP4 weights) + per-route flags */
+ * (fp32 for bf16 weights, bf16 for the narrow formats) + per-route flags; for
+ * SCR_W_MXFP4_A8 the MXFP8 codes and scales of x and of h in place of h */
 int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cfg* cfg,
                       size_t* bytes);
 
@@ -331,13 +333,29 @@ int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cf
  *               nothing), and after the gate/up, down and combine kernels
  *               (per-kernel timing on the launching stream); NULL entries
  *               are skipped
- * H % 128 == 0, I % 128 == 0, 128 <= H, I <= 16384 (the GEMM's K block is 128). */
+ * H % 128 == 0, I % 128 == 0, 128 <= H, I <= 16384 (the GEMM's K block is 128).
+ * SCR_W_MXFP4_A8 (W4A8, FreeToken PR #676 Known limits names activation-
+ * quantising GEMMs; the MX pairing is this library's reading): x is quantised
+ * to MXFP8 per row (scr_quantize_mxfp8, between marks 0 and 1), each route's
+ * h to MXFP8 per 32-column block in the gate/up epilogue, and both GEMMs run
+ * on the block-scaled fp8 x fp4 MFMA; needs H and I multiples of 512, at most
+ * 4096 (SCR_ENOTSUP otherwise, nothing launched). */
 int scr_grouped_moe_forward(const scr_routed_experts* view, const void* x, int T,
                             const float* topk_w, const int32_t* sorted_routes,
                             const int32_t* active_buckets, const int32_t* active_block_begin,
                             const int32_t* n_active, void* y, int y_dtype, void* ws,
                             size_t ws_bytes, scr_tile_cfg* cfg_out, float* a_scale_out,
                             hipEvent_t* marks, hipStream_t stream);
+
+/* quantize_mxfp8 (the W4A8 activations; OCP Microscaling Formats, MXFP8
+ * E4M3): x device bf16 [rows][cols], cols a multiple of 32; per row and block
+ * of 32 consecutive columns, shared = floor(log2(max |x|)) - 8 clamped to
+ * [-127, 127] (-127 for an all-zero block), scales[row][block] = shared + 127
+ * (e8m0), codes[row][col] = e4m3 of x * 2^-shared rounded to nearest even,
+ * saturated to +-448.  codes device [rows][cols], scales device [rows][cols/32].
+ * Inputs must be finite. */
+int scr_quantize_mxfp8(const void* x, long long rows, int cols, uint8_t* codes, uint8_t* scales,
+                       hipStream_t stream);
 
 /* ------------------------------------------------ whole-layer / staging */
 

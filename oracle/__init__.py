@@ -17,6 +17,6 @@ from .dedup import dedup_sorted
 from .lru import SlotBankState, ensure_slots
 from .align import align_blocks, align_capacity
 from .nvfp4 import e2m1_value, e4m3_value, dequant_nvfp4
-from .lowbit import e8m0_value, dequant_fp8, dequant_mxfp4
-from .mlp import expert_mlp, moe_layer, moe_layer_tokens
+from .lowbit import e8m0_value, dequant_fp8, dequant_mxfp4, e4m3_encode, quantize_mxfp8, dequant_mxfp8
+from .mlp import expert_mlp, moe_layer, moe_layer_tokens, moe_layer_w4a8
 from .dispatch import prefill_on_demand, demand_capacity_ok

@@ -11,10 +11,19 @@ W2_e is [H, I] and silu(z) = z / (1 + exp(-z)).  The sum over j runs in rank
 order.  Inputs are the exact values the device receives (bf16 or decoded
 NVFP4), widened to fp64; nothing is rounded on the way.
 
+W4A8 variant (moe_layer_w4a8): the expert input and the SwiGLU output h are
+each quantised to MXFP8 (oracle.lowbit.quantize_mxfp8, per 32 consecutive
+columns of a row) before their product with the weights; everything else as
+above, in fp64.
+
 Parity: pinned (pure-Python scalar loops on tiny shapes, single-expert
-reduction with k = 1, zero up-projection gives zero output).
+reduction with k = 1, zero up-projection gives zero output; the W4A8 variant
+equals the plain layer when every activation and h value is already an MXFP8
+value, and its quantiser is pinned in tests/test_oracle_lowbit.py).
 """
 import numpy as np
+
+from .lowbit import dequant_mxfp8, quantize_mxfp8
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -66,3 +75,38 @@ def moe_layer_tokens(x: np.ndarray, ids: np.ndarray, w: np.ndarray, weights_of, 
 def moe_layer(x, ids, w, weights_of):
     """Routed layer output for every token: fp64 [T, H]."""
     return moe_layer_tokens(x, ids, w, weights_of, range(x.shape[0]))
+
+
+def expert_mlp_w4a8(xq: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """Like expert_mlp on MXFP8 inputs xq [m, H] (already quantised values),
+    with h quantised to MXFP8 before the down projection."""
+    I = w13.shape[0] // 2
+    g = xq @ w13[:I].T
+    u = xq @ w13[I:].T
+    h = (g / (1.0 + np.exp(-g))) * u
+    hq = dequant_mxfp8(*quantize_mxfp8(h))
+    return hq @ w2.T
+
+
+def moe_layer_w4a8(x: np.ndarray, ids: np.ndarray, w: np.ndarray, weights_of) -> np.ndarray:
+    """W4A8 routed layer for every token: x [T, H] fp64 is quantised to MXFP8
+    per token, each route's h to MXFP8 per route; rank-ordered combine."""
+    xq = dequant_mxfp8(*quantize_mxfp8(x))
+    T, k = ids.shape
+    outs = {}
+    by_e = {}
+    for t in range(T):
+        for j in range(k):
+            by_e.setdefault(int(ids[t, j]), []).append((t, j))
+    for e, routes in by_e.items():
+        w13, w2 = weights_of(e)
+        o = expert_mlp_w4a8(np.stack([xq[t] for t, _ in routes]), w13, w2)
+        for (t, j), row in zip(routes, o):
+            outs[(t, j)] = row
+    y = np.zeros_like(x, dtype=np.float64)
+    for t in range(T):
+        acc = np.zeros(x.shape[1], dtype=np.float64)
+        for j in range(k):
+            acc = acc + float(w[t, j]) * outs[(t, j)]
+        y[t] = acc
+    return y

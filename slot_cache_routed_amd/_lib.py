@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libscr.so")
 
 SCR_OK, SCR_EINVAL, SCR_ENOTSUP, SCR_ECAPACITY, SCR_EHIP = 0, -1, -2, -3, -4
 SCR_ERR_CAPACITY = 1
-SCR_W_BF16, SCR_W_NVFP4, SCR_W_FP8, SCR_W_MXFP4 = 0, 1, 2, 3
+SCR_W_BF16, SCR_W_NVFP4, SCR_W_FP8, SCR_W_MXFP4, SCR_W_MXFP4_A8 = 0, 1, 2, 3, 4
 SCR_Y_F32, SCR_Y_BF16 = 0, 1
 SCR_MAX_TOPK = 32
 SCR_MAX_EXPERTS = 4096
@@ -28,7 +28,8 @@ EXPORTS = (
     "scr_record_layout_of", "scr_route", "scr_dedup", "scr_ensure_slots", "scr_ensure_slots_batched",
     "scr_copy_misses", "scr_plan_chunk",
     "scr_align_capacity", "scr_align_workspace", "scr_align_blocks", "scr_tile_config",
-    "scr_moe_workspace", "scr_grouped_moe_forward", "scr_stream_layer_async", "scr_stage_plan",
+    "scr_moe_workspace", "scr_grouped_moe_forward", "scr_quantize_mxfp8", "scr_stream_layer_async",
+    "scr_stage_plan",
     "scr_stage_rows_async", "scr_fill_row_table", "scr_fill_staged_rows", "scr_bank_rebuild_map",
     "scr_host_device_alias", "scr_prefill_on_demand", "scr_demand_capacity_ok", "scr_timer_create",
     "scr_timer_record", "scr_timer_elapsed_ms", "scr_timer_destroy", "scr_last_error", "scr_version",
@@ -97,6 +98,7 @@ _SIGS = {
     "scr_moe_workspace": (_I, [_I, _I, _I, _I, _I, C.POINTER(TileCfg), C.POINTER(_SZ)]),
     "scr_grouped_moe_forward": (_I, [C.POINTER(RoutedExperts), _P, _I, _P, _P, _P, _P, _P, _P, _I, _P,
                                      _SZ, C.POINTER(TileCfg), _P, _P, _P]),
+    "scr_quantize_mxfp8": (_I, [_P, C.c_longlong, _I, _P, _P, _P]),
     "scr_stream_layer_async": (_I, [C.POINTER(HostPoolDesc), _I, _P, _P]),
     "scr_stage_plan": (_I, [C.POINTER(BankDesc), C.POINTER(HostPoolDesc), _I, _I, _P, C.POINTER(Run), _I,
                             C.POINTER(_I), _P]),
@@ -238,6 +240,10 @@ def grouped_moe_forward(view: RoutedExperts, x, T, topk_w, sorted_routes, active
         _p(n_active), _p(y), y_dtype, _p(ws), ws_bytes, C.byref(cfg), _p(a_scale_out),
         None if ev is None else C.cast(ev, C.c_void_p), stream))
     return cfg
+
+
+def quantize_mxfp8(x, rows, cols, codes, scales, stream):
+    _check("scr_quantize_mxfp8", load().scr_quantize_mxfp8(_p(x), rows, cols, _p(codes), _p(scales), stream))
 
 
 def stream_layer_async(pool: HostPoolDesc, layer, dst, stream):

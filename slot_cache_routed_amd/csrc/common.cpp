@@ -60,7 +60,7 @@ extern "C" int scr_record_layout_of(int wdtype, int H, int I, scr_record_layout*
     out->record_bytes = (out->g2_off + 4 + 255) / 256 * 256;
     return SCR_OK;
   }
-  if (wdtype == SCR_W_MXFP4) {
+  if (wdtype == SCR_W_MXFP4 || wdtype == SCR_W_MXFP4_A8) {
     out->w13_off = 0;
     out->w13_scale_off = out->w13_off + 2 * i * h / 2;
     out->w2_off = out->w13_scale_off + 2 * i * h / 32;

@@ -116,6 +116,11 @@ struct GemmArgs {
   int32_t* flags;       // [R]
   const float* input_scale;  // [E] the layer's activation scales
   float* a_scale_out;        // nullable, device
+  // W4A8 only: MXFP8 activations (e4m3 codes, e8m0 scale per 32 columns)
+  const uint8_t* xq;  // [T][H]
+  const uint8_t* xs;  // [T][H/32]
+  uint8_t* hq;        // [h_rows][I]
+  uint8_t* hs;        // [h_rows][I/32]
   int T, k, R, H, I, B, h_rows, E;
 };
 
@@ -962,8 +967,348 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ o,
   }
 }
 
+// ------------------------------------------------ W4A8: MXFP4 x MXFP8
+//
+// Activations quantised to MXFP8 (OCP MX: e4m3 elements, one e8m0 scale per
+// 32 consecutive columns of a row) against MXFP4 weights, multiplied by the
+// gfx950 block-scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4 (A fp8, B fp4):
+// one instruction per 16x16 output tile and 128-wide K block, the scales
+// applied inside the instruction, no dequantisation.  Operand layout per lane
+// l, g = l / 16 (measured on the device with one-hot operands):
+//   A (16 x 128 fp8): row l % 16; bytes 0..15 hold k = 16 g .. 16 g + 15,
+//                     bytes 16..31 hold k = 64 + 16 g .. 64 + 16 g + 15
+//   B (128 x 16 fp4): column l % 16; nibbles 0..31 (low first) hold
+//                     k = 32 g .. 32 g + 31: exactly one MXFP4 tile-block load
+//   scales: lane l gives the e8m0 code of row (A) / column (B) l % 16 for the
+//           32-column block l / 16: the MXFP4 tile-block's scale byte `lane`
+// x is quantised by a separate pass; h is quantised in the gate/up epilogue,
+// per row and 32-column block (one wave's 32 h columns), and read by down the
+// way gate/up reads x.
+
+constexpr int kMxScaleCols = 128;  // e8m0 scales per staged activation row (K <= 4096)
+
+// Shared exponent of an MX block: floor(log2(amax)) - 8 (8 = the largest e4m3
+// exponent), clamped to the e8m0 range; -127 (code 0) for an all-zero block.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  const int e = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// two values as e4m3 codes (low byte = a) under a block's shared exponent:
+// v * 2^-shared is exact, saturated to +-448, then rounded to nearest even
+__device__ __forceinline__ unsigned mx_fp8_pair(float a, float b, int shared) {
+  const float va = fminf(fmaxf(__builtin_amdgcn_ldexpf(a, -shared), -448.0f), 448.0f);
+  const float vb = fminf(fmaxf(__builtin_amdgcn_ldexpf(b, -shared), -448.0f), 448.0f);
+  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(va, vb, 0, false) & 0xFFFFu;
+}
+
+// one thread per 32-element block of a row-major [rows][cols] bf16 array
+__global__ __launch_bounds__(256) void mxfp8_quant_kernel(const bf16* __restrict__ x, long long nblocks,
+                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
+  for (long long b = blockIdx.x * 256ll + threadIdx.x; b < nblocks; b += (long long)gridDim.x * 256) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 32);
+    u32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = ldg<u32x4>(src + i);
+    float f[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const unsigned w = v[i / 4][i % 4];
+      f[2 * i] = __uint_as_float(w << 16);
+      f[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
+      amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
+    }
+    const int shared = mx_shared_exp(amax);
+    u32x4 out[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      out[i / 4][i % 4] = mx_fp8_pair(f[4 * i], f[4 * i + 1], shared) | (mx_fp8_pair(f[4 * i + 2], f[4 * i + 3], shared) << 16);
+    u32x4* dst = reinterpret_cast<u32x4*>(q + b * 32);
+    dst[0] = out[0];
+    dst[1] = out[1];
+    s[b] = (uint8_t)(shared + 127);
+  }
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// RES: down with K = I = kWideBufs blocks keeps the bucket's whole h block
+// resident in LDS (a compile-time choice: the run-time one spills registers)
+template <int MT, bool GATEUP, int EW, int NTW, int MTC, bool RES>
+__device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row, const uint8_t* asc,
+                                          const int* row_route, const float* row_w, uint8_t* As0, uint8_t* As1,
+                                          uint8_t* As2, uint8_t* As3, uint32_t* stg, int m0,
+                                          __amdgpu_buffer_rsrc_t wrsrc, const int* toff0, const int* soff0,
+                                          int nkb, int c_begin, int c_end) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  constexpr int CT = GATEUP ? EW * NTW / 2 : EW * NTW;  // row tiles per chunk and tensor half
+  uint8_t* const bufs[kWideBufs] = {As0, As1, As2, As3};
+
+  // MXFP8 activations through a buffer resource over x's codes (gate/up) or h's (down)
+  const __amdgpu_buffer_rsrc_t arsrc =
+      GATEUP ? __builtin_amdgcn_make_buffer_rsrc((void*)a.xq, (short)0, a.T * a.H, 0x00020000)
+             : __builtin_amdgcn_make_buffer_rsrc((void*)a.hq, (short)0, a.h_rows * a.I, 0x00020000);
+  // direct loads of a K block: rows of 128 bytes = 8 chunks of 16; 2 * MTC
+  // wave instructions dealt round-robin to the waves (a wave past the end
+  // repeats the last one), instruction j filling LDS chunk q = 64 j + lane,
+  // i.e. row q / 8, physical chunk q % 8 = logical chunk (q % 8) ^ (row % 8)
+  constexpr int NA = (2 * MTC + EW - 1) / EW;
+  int aoff[NA];
+  int adst[NA];
+#pragma unroll
+  for (int u = 0; u < NA; ++u) {
+    const int j = min(u * EW + wave, 2 * MTC - 1);
+    const int q = j * 64 + lane;
+    const int r = q >> 3, c = (q & 7) ^ (r & 7);
+    const int off = src_row[r];
+    aoff[u] = (off >= 0 ? off : 0) + 16 * c;  // padding rows read row 0 (their outputs are dropped)
+    adst[u] = j * 1024;
+  }
+  auto load_a = [&](uint8_t* buf, int kb) {
+#pragma unroll
+    for (int u = 0; u < NA; ++u)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (__attribute__((address_space(3))) void*)(buf + adst[u]), 16,
+                                               aoff[u], kb * kKB, 0, 0);
+  };
+  auto load_b = [&](BFrag<SCR_W_MXFP4, NTW>& f, int s) {
+    const int ch = s / nkb, kb = s - ch * nkb;
+    const int blk = ch * CT * nkb + kb;
+    int tp[NTW], sp[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      tp[t] = toff0[t] + blk * 1024;
+      sp[t] = soff0[t] + blk * 64;
+    }
+    f.load_buf(wrsrc, tp, sp, lane);
+  };
+  // A operand of row tile mt: row mt * 16 + col, logical chunks grp and 4 + grp
+  auto read_a = [&](const uint8_t* buf, int mt) {
+    const int row = mt * 16 + col;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(buf + row * 128 + 16 * (grp ^ (row & 7)));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(buf + row * 128 + 16 * ((4 + grp) ^ (row & 7)));
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+
+  f32x4 acc[MTC][NTW];
+
+  uint32_t* const wst = stg + wave * (kWideStage / 4);
+  auto epilogue = [&](int ch) {
+    if (GATEUP) {
+      // h = silu(g) * u for this wave's 32 h columns (one MX block per row),
+      // quantised per row: block max across the 16 lanes of a row group
+      uint8_t* sh = reinterpret_cast<uint8_t*>(wst);
+#pragma unroll
+      for (int mt = 0; mt < MTC; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float h0 = silu_mul(acc[mt][0][i], acc[mt][NTW / 2][i]);
+          const float h1 = silu_mul(acc[mt][1][i], acc[mt][NTW / 2 + 1][i]);
+          float m = fmaxf(fabsf(h0), fabsf(h1));
+#pragma unroll
+          for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+          const int shared = mx_shared_exp(m);
+          const unsigned p = mx_fp8_pair(h0, h1, shared);
+          sh[(grp * 4 + i) * 32 + col] = (uint8_t)(p & 0xFF);
+          sh[(grp * 4 + i) * 32 + 16 + col] = (uint8_t)(p >> 8);
+          if (col == 0) {
+            const int pos = m0 + mt * 16 + grp * 4 + i;
+            a.hs[(size_t)pos * (a.I / 32) + ch * EW + wave] = (uint8_t)(shared + 127);
+          }
+        }
+        // 16 rows x 32 bytes = 32 lanes x 16 bytes
+        if (lane < 32) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sh + (lane >> 1) * 32 + (lane & 1) * 16);
+          const int pos = m0 + mt * 16 + (lane >> 1);
+          *reinterpret_cast<u32x4*>(a.hq + (size_t)pos * a.I + ch * (32 * EW) + wave * 32 + (lane & 1) * 16) = v;
+        }
+      }
+    } else {
+      constexpr int OC = 16 * NTW;   // output columns per wave
+      constexpr int EPP = 8;         // bf16 per 16-byte piece
+      constexpr int PPR = OC / EPP;  // pieces per row
+      constexpr int ROUNDS = (16 * PPR + 63) / 64;
+      bf16* so = reinterpret_cast<bf16*>(wst);
+#pragma unroll
+      for (int mt = 0; mt < MTC; ++mt) {
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+          const float w0 = row_w[mt * 16 + grp * 4 + i], w1 = row_w[mt * 16 + grp * 4 + i + 1];
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) {
+            const int o0 = (grp * 4 + i) * OC + 16 * t + col;
+            const unsigned p = pack_bf16(w0 * acc[mt][t][i], w1 * acc[mt][t][i + 1]);
+            reinterpret_cast<uint16_t*>(so)[o0] = (uint16_t)p;
+            reinterpret_cast<uint16_t*>(so)[o0 + OC] = (uint16_t)(p >> 16);
+          }
+        }
+#pragma unroll
+        for (int rd = 0; rd < ROUNDS; ++rd) {
+          const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(so + (q < 16 * PPR ? rr : 0) * OC + pc * EPP);
+          const int r = q < 16 * PPR ? row_route[mt * 16 + rr] : -1;
+          if (r >= 0) {
+            bf16* orow = static_cast<bf16*>(a.o) + (size_t)r * a.H + ch * (OC * EW) + wave * OC + pc * EPP;
+            *reinterpret_cast<u32x4*>(orow) = v;
+            if (ch == 0 && wave == 0 && pc == 0) a.flags[r] = 1;
+          }
+        }
+      }
+    }
+  };
+
+  constexpr int D = kWideRing;
+  constexpr int U = D > kWideBufs ? D : kWideBufs;
+  constexpr int NB = 2 * NTW;  // codes + scale per tile
+  const int s0 = c_begin * nkb, s1 = c_end * nkb;
+  constexpr int LA = kWideBufs - 1;
+  BFrag<SCR_W_MXFP4, NTW> ring[D];
+  constexpr bool resident = RES;
+#pragma unroll
+  for (int i = 0; i < LA; ++i) load_a(bufs[i], i % nkb);
+  if (resident) load_a(bufs[LA], LA);
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i) load_b(ring[i], min(s0 + i, s1 - 1));
+  if (resident)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((D - 1) * NB));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((LA - 1) * NA + (D - 1) * NB));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int ch = c_begin; ch < c_end; ++ch) {
+#pragma unroll
+    for (int mt = 0; mt < MTC; ++mt)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb0 = 0; kb0 < nkb; kb0 += U) {
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        const int kb = kb0 + i, s = ch * nkb + kb;
+        const BFrag<SCR_W_MXFP4, NTW>& bc = ring[i % D];
+        const uint8_t* buf = bufs[i % kWideBufs];
+        if (!resident) load_a(bufs[(i + LA) % kWideBufs], (kb + LA) % nkb);
+        load_b(ring[(i + D - 1) % D], min(s + D - 1, s1 - 1));
+#pragma unroll
+        for (int mt = 0; mt < MTC; ++mt) {
+          const i32x8 af = read_a(buf, mt);
+          const int sa = asc[(mt * 16 + col) * kMxScaleCols + 4 * kb + grp];
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) {
+            const u32x4 c4 = bc.codes[t];
+            const i32x8 bf = {(int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3], 0, 0, 0, 0};
+            acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[mt][t], 0, 4, 0, sa, 0,
+                                                                            (int)(bc.sc[t] & 0xFFu));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (!resident) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm((LA - 1) * NA + (D < LA ? D : LA) * NB));
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    epilogue(ch);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int MT, bool GATEUP, int EW, int NTW, bool RES>
+__global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int groups) {
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[MT * 16 * kKB];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[MT * 16 * kKB];
+  __shared__ __attribute__((aligned(1024))) uint8_t As2[MT * 16 * kKB];
+  __shared__ __attribute__((aligned(1024))) uint8_t As3[MT * 16 * kKB];
+  __shared__ __attribute__((aligned(16))) uint8_t asc[MT * 16 * kMxScaleCols];  // e8m0 scales of the pass rows
+  __shared__ int src_row[MT * 16];
+  __shared__ int row_route[GATEUP ? 1 : MT * 16];
+  __shared__ float row_w[GATEUP ? 1 : MT * 16];
+  __shared__ __attribute__((aligned(256))) uint32_t stg[EW * kWideStage / 4];
+  if (GATEUP) gateup_prologue(a);
+  const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
+  const int j = 8 * (q / groups) + xcd, g = q % groups;
+  if (j >= *a.n_active) return;
+  const int b = a.active_buckets[j];
+  const int p0 = a.active_block_begin[j] * a.B, p1 = a.active_block_begin[j + 1] * a.B;
+  if (p1 > a.h_rows || p0 >= p1) return;
+  constexpr int kThreads = 64 * EW;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int K = GATEUP ? a.H : a.I;
+  const int nkb = K / kKB;
+  const int nsc = K / 32;
+  const int nchunks = GATEUP ? a.I / (8 * NTW * EW) : a.H / (16 * NTW * EW);
+  const int c_begin = g * nchunks / groups, c_end = (g + 1) * nchunks / groups;
+  if (c_begin >= c_end) return;
+  const uint8_t* rec = static_cast<const uint8_t*>(a.bucket_rows[b]);
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)rec, (short)0, (int)a.lay.record_bytes, 0x00020000);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  int toff0[NTW], soff0[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) {
+    const int row0 = GATEUP ? (t < NTW / 2 ? 0 : a.I) + wv * 8 * NTW + 16 * (t % (NTW / 2)) : wv * 16 * NTW + 16 * t;
+    const int tb = (row0 / 16) * nkb;
+    toff0[t] = (int)(GATEUP ? a.lay.w13_off : a.lay.w2_off) + tb * 1024;
+    soff0[t] = (int)(GATEUP ? a.lay.w13_scale_off : a.lay.w2_scale_off) + tb * 64;
+  }
+  for (int m0 = p0; m0 < p1; m0 += MT * 16) {
+    const int rows = min(MT * 16, p1 - m0);
+    for (int i = tid; i < MT * 16; i += kThreads) {
+      int off = -1;
+      int r = -1;
+      if (i < rows) {
+        if (GATEUP) {
+          r = a.sorted_routes[m0 + i];
+          if (r >= 0 && r < a.R) off = (r / a.k) * K;
+        } else {
+          off = (m0 + i) * K;
+          r = a.sorted_routes[m0 + i];
+        }
+      }
+      src_row[i] = off;
+      if (!GATEUP) {
+        const bool valid = r >= 0 && r < a.R;
+        row_route[i] = valid ? r : -1;
+        row_w[i] = valid ? a.topk_w[r] : 0.0f;
+      }
+    }
+    __syncthreads();
+    // the scales of the pass rows (padding rows: those of row 0 of the source)
+    for (int e = tid; e < MT * 16 * nsc; e += kThreads) {
+      const int i = e / nsc, c = e - i * nsc;
+      const int off = src_row[i] >= 0 ? src_row[i] : 0;
+      asc[i * kMxScaleCols + c] = GATEUP ? a.xs[off / 32 + c] : a.hs[off / 32 + c];
+    }
+    __syncthreads();
+#define SCR_W4A8_PASS(n)                                                                                     \
+  case n:                                                                                                    \
+    if constexpr (MT >= n)                                                                                   \
+      w4a8_pass<MT, GATEUP, EW, NTW, n, RES>(a, src_row, asc, row_route, row_w, As0, As1, As2, As3, stg, m0,   \
+                                             wrsrc, toff0, soff0, nkb, c_begin, c_end);                        \
+    break;
+    switch (rows / 16) {
+      SCR_W4A8_PASS(1)
+      SCR_W4A8_PASS(2)
+      SCR_W4A8_PASS(3)
+      SCR_W4A8_PASS(4)
+      SCR_W4A8_PASS(5)
+      SCR_W4A8_PASS(6)
+      SCR_W4A8_PASS(7)
+      default: break;
+    }
+#undef SCR_W4A8_PASS
+    __syncthreads();
+  }
+}
+
 struct WsLayout {
   size_t h_off, o_off, flags_off, bytes;
+  size_t xq_off, xs_off, hs_off;  // W4A8 only (h_off then holds the MXFP8 codes of h)
   int h_rows;
 };
 
@@ -976,8 +1321,19 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
   long long rows = R + m * (B - 1);
   rows = (rows + B - 1) / B * B;
   w.h_rows = (int)rows;
+  w.xq_off = w.xs_off = w.hs_off = 0;
   w.h_off = 0;
-  w.o_off = align256(w.h_off + (size_t)rows * I * sizeof(uint16_t));
+  size_t end;
+  if (wdtype == SCR_W_MXFP4_A8) {
+    w.xq_off = 0;
+    w.xs_off = align256((size_t)T * H);
+    w.h_off = align256(w.xs_off + (size_t)T * (H / 32));
+    w.hs_off = align256(w.h_off + (size_t)rows * I);
+    end = w.hs_off + (size_t)rows * (I / 32);
+  } else {
+    end = w.h_off + (size_t)rows * I * sizeof(uint16_t);
+  }
+  w.o_off = align256(end);
   const size_t row_bytes = wdtype == SCR_W_BF16 ? sizeof(float) : sizeof(uint16_t);
   w.flags_off = align256(w.o_off + (size_t)R * H * row_bytes);
   w.bytes = align256(w.flags_off + (size_t)R * sizeof(int32_t));
@@ -1036,6 +1392,43 @@ static int launch_gemms(const GemmArgs& a, int max_active, hipEvent_t* marks, hi
   return SCR_OK;
 }
 
+// W4A8: the block-scaled kernels for every row count (their 16-row passes
+// serve few rows per expert as well); the shape must fit the wide tiling
+static bool w4a8_fits(const GemmArgs& a) {
+  return wide_gemms_fit<SCR_W_MXFP4>(a) && a.H / 32 <= kMxScaleCols && a.I / 32 <= kMxScaleCols;
+}
+
+static int launch_w4a8(const GemmArgs& a, int max_active, hipEvent_t* marks, hipStream_t s) {
+  constexpr int NTW = 4;
+  const int rows8 = (max_active + 7) / 8;
+  const int g_gu = a.I / (8 * NTW * kWideWaves);
+  const int nch_dn = a.H / (16 * NTW * kWideWaves);
+  const int g_dn = nch_dn >= 2 ? nch_dn / 2 : 1;
+  hipLaunchKernelGGL((moe_w4a8_kernel<7, true, kWideWaves, NTW, false>), dim3(8 * rows8 * g_gu),
+                     dim3(64 * kWideWaves), 0, s, a, g_gu);
+  SCR_CHECK_LAUNCH();
+  if (marks && marks[2]) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
+  if (a.I / kKB == kWideBufs)
+    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, true>), dim3(8 * rows8 * g_dn),
+                       dim3(64 * kWideWaves), 0, s, a, g_dn);
+  else
+    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, false>), dim3(8 * rows8 * g_dn),
+                       dim3(64 * kWideWaves), 0, s, a, g_dn);
+  SCR_CHECK_LAUNCH();
+  if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
+  return SCR_OK;
+}
+
+static int launch_mxfp8_quant(const bf16* x, long long rows, int cols, uint8_t* q, uint8_t* sc, hipStream_t s) {
+  const long long nb = rows * (cols / 32);
+  if (nb == 0) return SCR_OK;
+  long long grid = (nb + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  hipLaunchKernelGGL(mxfp8_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nb, q, sc);
+  SCR_CHECK_LAUNCH();
+  return SCR_OK;
+}
+
 // few rows per expert: the small-M kernels; many: the wide-tile kernels when
 // the shape fits them, else the small-M kernels with 112-row passes
 template <int WDT>
@@ -1051,7 +1444,8 @@ static int run_gemms(const scr_tile_cfg& cfg, const GemmArgs& a, int max_active,
 extern "C" int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_cfg* cfg) {
   SCR_CHECK_ARG(cfg != nullptr, "tile_config: cfg is null");
   SCR_CHECK_ARG(T >= 0 && k >= 1 && E_layer >= 1, "tile_config: bad T, k or E");
-  SCR_CHECK_ARG(wdtype == SCR_W_BF16 || wdtype == SCR_W_NVFP4 || wdtype == SCR_W_FP8 || wdtype == SCR_W_MXFP4,
+  SCR_CHECK_ARG(wdtype == SCR_W_BF16 || wdtype == SCR_W_NVFP4 || wdtype == SCR_W_FP8 || wdtype == SCR_W_MXFP4 ||
+                    wdtype == SCR_W_MXFP4_A8,
                 "tile_config: unknown wdtype");
   // rows per expert of the routed layer (never of the bank)
   const long long per_expert = ((long long)T * k + E_layer - 1) / E_layer;
@@ -1088,7 +1482,7 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   SCR_CHECK_ARG(I >= 128 && I % 128 == 0 && I <= 16384, "forward: I must be a multiple of 128 in [128, 16384]");
   SCR_CHECK_ARG(view->num_buckets >= 1 && view->bucket_rows && view->input_scale, "forward: bad view");
   SCR_CHECK_ARG(view->wdtype == SCR_W_BF16 || view->wdtype == SCR_W_NVFP4 || view->wdtype == SCR_W_FP8 ||
-                    view->wdtype == SCR_W_MXFP4,
+                    view->wdtype == SCR_W_MXFP4 || view->wdtype == SCR_W_MXFP4_A8,
                 "forward: unknown wdtype");
   SCR_CHECK_ARG(y_dtype == SCR_Y_F32 || y_dtype == SCR_Y_BF16, "forward: unknown y dtype");
   SCR_CHECK_ARG(T >= 0 && (long long)T * k < (1ll << 30) && (long long)T * H < (1ll << 31),
@@ -1119,6 +1513,10 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   a.n_active = n_active;
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   a.h = reinterpret_cast<scr::bf16*>(wsb + wl.h_off);
+  a.xq = wsb + wl.xq_off;
+  a.xs = wsb + wl.xs_off;
+  a.hq = wsb + wl.h_off;
+  a.hs = wsb + wl.hs_off;
   a.o = wsb + wl.o_off;
   a.flags = reinterpret_cast<int32_t*>(wsb + wl.flags_off);
   a.T = T;
@@ -1132,9 +1530,18 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   a.input_scale = view->input_scale;
   a.a_scale_out = a_scale_out;
   a.E = E;
-  // marks[0] and marks[1] bracket the (now empty) prologue: the gate/up
-  // kernel clears the flags and reports the activation scale itself
+  // marks[0] and marks[1] bracket the prologue (the activation quantisation
+  // of W4A8; otherwise empty: the gate/up kernel clears the flags and reports
+  // the activation scale itself)
+  if (view->wdtype == SCR_W_MXFP4_A8 && !scr::w4a8_fits(a)) {
+    scr::set_error("forward: W4A8 needs H a multiple of 512 and I of 512, both at most 4096 (H=%d I=%d)", H, I);
+    return SCR_ENOTSUP;
+  }
   if (marks && marks[0]) SCR_CHECK_HIP(hipEventRecord(marks[0], stream));
+  if (view->wdtype == SCR_W_MXFP4_A8) {
+    rc = scr::launch_mxfp8_quant(a.x, T, H, wsb + wl.xq_off, wsb + wl.xs_off, stream);
+    if (rc) return rc;
+  }
   if (marks && marks[1]) SCR_CHECK_HIP(hipEventRecord(marks[1], stream));
 
   // the grid covers at most min(R, E_layer) active buckets: a layer size
@@ -1143,7 +1550,8 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
     case SCR_W_BF16: rc = scr::run_gemms<SCR_W_BF16>(cfg, a, max_active, marks, stream); break;
     case SCR_W_NVFP4: rc = scr::run_gemms<SCR_W_NVFP4>(cfg, a, max_active, marks, stream); break;
     case SCR_W_FP8: rc = scr::run_gemms<SCR_W_FP8>(cfg, a, max_active, marks, stream); break;
-    default: rc = scr::run_gemms<SCR_W_MXFP4>(cfg, a, max_active, marks, stream); break;
+    case SCR_W_MXFP4: rc = scr::run_gemms<SCR_W_MXFP4>(cfg, a, max_active, marks, stream); break;
+    default: rc = scr::launch_w4a8(a, max_active, marks, stream); break;
   }
   if (rc) return rc;
 
@@ -1166,4 +1574,12 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   SCR_CHECK_LAUNCH();
   if (marks && marks[4]) SCR_CHECK_HIP(hipEventRecord(marks[4], stream));
   return SCR_OK;
+}
+
+extern "C" int scr_quantize_mxfp8(const void* x, long long rows, int cols, uint8_t* codes, uint8_t* scales,
+                                  hipStream_t stream) {
+  SCR_CHECK_ARG(rows >= 0 && cols >= 32 && cols % 32 == 0, "quantize_mxfp8: cols must be a positive multiple of 32");
+  if (rows == 0) return SCR_OK;
+  SCR_CHECK_ARG(x && codes && scales, "quantize_mxfp8: null pointer");
+  return scr::launch_mxfp8_quant(static_cast<const scr::bf16*>(x), rows, cols, codes, scales, stream);
 }

@@ -79,7 +79,7 @@ def test_align_capacity_formula(lib):
     lambda: L.align_blocks(1, 10, None, 0, 8, 16, 1, 1, 1, 1, 1, 1, 1, 4, None),         # tiny workspace
     lambda: L.tile_config(1, 0, 8, 0),
     lambda: L.tile_config(1, 1, 8, 7),
-    lambda: L.tile_config(1, 1, 8, 4),                        # no format 4
+    lambda: L.tile_config(1, 1, 8, 5),                        # no format 5
 ])
 def test_bad_arguments_are_rejected_before_any_launch(lib, call):
     with pytest.raises(L.ScrError) as ei:
