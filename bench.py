@@ -547,6 +547,21 @@ def decode_stream(args) -> dict:
     t_b.record(s)
     total_g = t_a.elapsed_ms(t_b)
     snap_g = bank_g.snapshot()
+    del step
+    torch.cuda.empty_cache()
+    # the same steps under scored (LRFU) eviction, half-life 16 queries
+    lrfu_decay = int(2 ** 32 * 2 ** (-1.0 / 16))
+    bank_f = LY.Bank(S, NL, E, L.SCR_W_BF16, rec, policy=L.SCR_POLICY_LRFU, lrfu_decay=lrfu_decay)
+    buf = LY.LayerBuffers(T, E, k, H, I, S, L.SCR_W_BF16, width=128, y_dtype=L.SCR_Y_BF16)
+    torch.cuda.synchronize()
+    t_a.record(s)
+    for st in range(steps):
+        for l in range(NL):
+            LY.demand_layer(bank_f, pool, l, logits[st][l], xs[st][l], sc, width=128, record_stats=True, buf=buf,
+                            batched=True, shape=(k, H, I))
+    t_b.record(s)
+    total_f = t_a.elapsed_ms(t_b)
+    hf, mf = [int(v) for v in bank_f.snapshot()["stats"][:2]]
     same = all(np.array_equal(np.asarray(snap[key]), np.asarray(snap_g[key]))
                for key in ("slot_key", "key_to_slot", "slot_stamp", "stats", "decode_freq", "clock"))
     return {
@@ -559,6 +574,8 @@ def decode_stream(args) -> dict:
         "miss_copy_GBps_effective": round(misses * rec / (total * 1e-3) / 1e9, 2),
         "step_ms_hip_graph": round(total_g / steps, 3),
         "hip_graph_bank_identical": bool(same),
+        "lrfu_half_life_16": {"step_ms": round(total_f / steps, 3), "hit_rate": round(hf / max(1, hf + mf), 4),
+                              "misses": mf},
         "note": "wall time of all layer-steps on the compute stream, PCIe-inclusive; step_ms_hip_graph replays "
                 "one graph per step holding every layer, from an empty bank, inputs copied in before each replay",
     }

@@ -129,7 +129,29 @@ int scr_record_layout_of(int wdtype, int H, int I, scr_record_layout* out);
  *   err         uint32 [1]    sticky SCR_ERR_* bits
  *   rows        uint8  [S * record_bytes]  the slots' expert records
  * slot_key and key_to_slot are kept inverse to each other by every call.
+ * Eviction policy (policy):
+ *   SCR_POLICY_LRU  victims in ascending (stamp, slot) among the slots the
+ *                   query did not touch [P1 author's reply: LRU only].
+ *   SCR_POLICY_LRFU scored eviction [P1 run notes: the author's build admits
+ *                   by LRFU; P1 Solution: earlier pieces pinned against later
+ *                   ones].  Per slot a combined recency-frequency value
+ *                   C = sum over its references of 2^-(lambda * age), kept in
+ *                   slot_crf as unsigned Q8.24 at the slot's stamp; lrfu_decay
+ *                   = D = 2^32 * 2^-lambda (0 < D < 2^32) is the per-tick
+ *                   factor.  D^n is r = 2^32, b = D, for each bit of n from the
+ *                   lowest: r = r * b >> 32 if set, b = b * b >> 32;
+ *                   decay(C, n) = C * r >> 32.  A hit sets C = min(decay(C,
+ *                   now - stamp) + 2^24, 2^32 - 1), an admission C = 2^24.
+ *                   Victims in ascending (decay(C, now - stamp), slot) among
+ *                   the slots untouched by the whole chunk: stamp below
+ *                   *chunk_start, the clock of the chunk's first query (set by
+ *                   scr_ensure_slots at q_begin = 0 and by the batched and
+ *                   one-launch planners).
+ *   slot_crf    uint32 [S]  LRFU only (may be NULL under LRU)
+ *   chunk_start uint64 [1]  LRFU only (may be NULL under LRU)
  */
+#define SCR_POLICY_LRU 0
+#define SCR_POLICY_LRFU 1
 typedef struct scr_bank_desc {
   int32_t S, L, E, wdtype;
   int32_t* slot_key;
@@ -141,6 +163,10 @@ typedef struct scr_bank_desc {
   uint32_t* err;
   uint8_t* rows;
   uint64_t record_bytes;
+  int32_t policy;
+  uint32_t lrfu_decay;
+  uint32_t* slot_crf;
+  uint64_t* chunk_start;
 } scr_bank_desc;
 
 /* ---------------------------------------------------------- host pool

@@ -18,6 +18,7 @@ SCR_OK, SCR_EINVAL, SCR_ENOTSUP, SCR_ECAPACITY, SCR_EHIP = 0, -1, -2, -3, -4
 SCR_ERR_CAPACITY = 1
 SCR_W_BF16, SCR_W_NVFP4, SCR_W_FP8, SCR_W_MXFP4, SCR_W_MXFP4_A8 = 0, 1, 2, 3, 4
 SCR_Y_F32, SCR_Y_BF16 = 0, 1
+SCR_POLICY_LRU, SCR_POLICY_LRFU = 0, 1
 SCR_MAX_TOPK = 32
 SCR_MAX_EXPERTS = 4096
 SCR_MAX_QUERY_WIDTH = 1024
@@ -52,7 +53,9 @@ class BankDesc(C.Structure):
     _fields_ = [("S", C.c_int32), ("L", C.c_int32), ("E", C.c_int32), ("wdtype", C.c_int32),
                 ("slot_key", C.c_void_p), ("slot_stamp", C.c_void_p), ("key_to_slot", C.c_void_p),
                 ("clock", C.c_void_p), ("stats", C.c_void_p), ("decode_freq", C.c_void_p),
-                ("err", C.c_void_p), ("rows", C.c_void_p), ("record_bytes", C.c_uint64)]
+                ("err", C.c_void_p), ("rows", C.c_void_p), ("record_bytes", C.c_uint64),
+                ("policy", C.c_int32), ("lrfu_decay", C.c_uint32), ("slot_crf", C.c_void_p),
+                ("chunk_start", C.c_void_p)]
 
 
 class HostPoolDesc(C.Structure):

@@ -5,7 +5,11 @@
 // queries evicted last; vLLM fork PR #48, What: a device-side planner over one
 // bank shared by all layers).  Recency is one stamp per query; candidates for
 // eviction are ordered by the 64-bit key (stamp << 20 | slot), found by an
-// 8-bit radix select in LDS instead of sorting the bank.
+// 8-bit radix select in LDS instead of sorting the bank.  Under the scored
+// policy (LRFU; FreeToken PR #676 run notes and Solution: earlier pieces of a
+// chunk pinned against the later ones) the key is (decayed value << 20 |
+// slot) over the slots the chunk has not touched; include/scr.h gives the
+// integer definition.
 #include "small_blocks.h"
 
 namespace scr {
@@ -25,7 +29,7 @@ struct EnsureShared {
   int victim[SCR_MAX_QUERY_WIDTH];
   unsigned hist[256];
   int wave_tot[kWave + 1];
-  int nhit, nmiss, nsel, evict;
+  int nhit, nmiss, nsel, evict, npinned;
   uint64_t prefix;
   unsigned rank;
 };
@@ -38,14 +42,45 @@ struct BankRefs {
   uint64_t* stats;
   uint32_t* decode_freq;
   uint32_t* err;
+  int policy;
+  uint32_t decay;         // LRFU per-tick factor, Q0.32
+  uint32_t* slot_crf;     // LRFU value at the slot's stamp, Q8.24
+  uint64_t* chunk_start;  // clock of the chunk's first query
 };
 
-// One LRU query with recency stamp `now`; the admitted misses are written in
-// query order to miss_slot/miss_key[0 ..) and their number returned (in every
-// thread).  Called by all threads of the workgroup.
-__device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, const int32_t* __restrict__ query,
-                            int width, int record_stats, int32_t* __restrict__ miss_slot,
-                            int32_t* __restrict__ miss_key) {
+constexpr uint32_t kCrfOne = 1u << 24;
+
+// D^n in Q0.32 by right-to-left binary exponentiation, truncating each product
+__device__ __forceinline__ uint64_t pow_q32(uint64_t D, uint64_t n) {
+  uint64_t r = 1ull << 32, b = D;
+  while (n != 0 && r != 0) {
+    if (n & 1) r = (r * b) >> 32;
+    b = (b * b) >> 32;
+    n >>= 1;
+  }
+  return r;
+}
+
+// an LRFU value (Q8.24) decayed over n ticks
+__device__ __forceinline__ uint64_t crf_decay(uint32_t c, uint64_t n, uint32_t D) {
+  return ((uint64_t)c * pow_q32(D, n)) >> 32;
+}
+
+// eviction order key of an untouched slot at time now
+__device__ __forceinline__ uint64_t victim_key(const BankRefs& bk, int s, uint64_t now) {
+  const uint64_t stamp = bk.slot_stamp[s];
+  if (bk.policy == SCR_POLICY_LRFU) return cand_key(crf_decay(bk.slot_crf[s], now - stamp, bk.decay), s);
+  return cand_key(stamp, s);
+}
+
+// One query with clock `now`; the admitted misses are written in query order
+// to miss_slot/miss_key[0 ..) and their number returned (in every thread).
+// `pin`: under LRFU only slots stamped before it are candidates (the chunk's
+// first query's clock).  Called by all threads of the workgroup.
+__device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, uint64_t pin,
+                            const int32_t* __restrict__ query, int width, int record_stats,
+                            int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_key) {
+  const bool lrfu = bk.policy == SCR_POLICY_LRFU;
   const int tid = threadIdx.x;
   const int S = bk.S, E = bk.E;
   const int nwords = (S + 31) / 32;
@@ -54,6 +89,7 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
     sh.nhit = 0;
     sh.evict = 0;
     sh.nsel = 0;
+    sh.npinned = 0;
   }
   __syncthreads();
 
@@ -65,6 +101,10 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
       my_key = bk.layer * E + e;
       const int s = bk.key_to_slot[my_key];
       if (s >= 0) {
+        if (lrfu) {  // the hit's value decayed to now, plus this reference
+          const uint64_t c = crf_decay(bk.slot_crf[s], now - bk.slot_stamp[s], bk.decay) + kCrfOne;
+          bk.slot_crf[s] = c > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)c;
+        }
         bk.slot_stamp[s] = now;  // touch the hit
         atomicOr(&sh.hit_bits[s >> 5], 1u << (s & 31));
         atomicAdd(&sh.nhit, 1);
@@ -102,9 +142,18 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
     if (tid == 0) sh.nmiss = sh.wave_tot[nw - 1];
   }
   __syncthreads();
+  // LRFU: untouched slots stamped at or after the pin (earlier queries of the
+  // chunk) are no candidates either
+  if (lrfu) {
+    int np = 0;
+    for (int s = tid; s < S; s += blockDim.x)
+      if (!((sh.hit_bits[s >> 5] >> (s & 31)) & 1u) && bk.slot_stamp[s] >= pin) ++np;
+    if (np) atomicAdd(&sh.npinned, np);
+    __syncthreads();
+  }
 
   const int m = sh.nmiss;
-  const int n_cand = S - sh.nhit;
+  const int n_cand = S - sh.nhit - sh.npinned;
   const int m_adm = m < n_cand ? m : n_cand;
 
   if (m_adm > 0) {
@@ -120,7 +169,8 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
       const uint64_t prefix = sh.prefix;
       for (int s = tid; s < S; s += blockDim.x) {
         if ((sh.hit_bits[s >> 5] >> (s & 31)) & 1u) continue;
-        const uint64_t key = cand_key(bk.slot_stamp[s], s);
+        if (lrfu && bk.slot_stamp[s] >= pin) continue;
+        const uint64_t key = victim_key(bk, s, now);
         const bool match = (shift == 56) ? true : ((key >> (shift + 8)) == prefix);
         if (match) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
       }
@@ -141,7 +191,8 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
     // collect the selected candidates (exactly m_adm distinct keys <= thresh)
     for (int s = tid; s < S; s += blockDim.x) {
       if ((sh.hit_bits[s >> 5] >> (s & 31)) & 1u) continue;
-      const uint64_t key = cand_key(bk.slot_stamp[s], s);
+      if (lrfu && bk.slot_stamp[s] >= pin) continue;
+      const uint64_t key = victim_key(bk, s, now);
       if (key <= thresh) {
         const int idx = atomicAdd(&sh.nsel, 1);
         if (idx < SCR_MAX_QUERY_WIDTH) sh.sel_key[idx] = key;
@@ -171,6 +222,7 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
         bk.slot_key[v] = key;
         bk.key_to_slot[key] = v;
         bk.slot_stamp[v] = now;
+        if (lrfu) bk.slot_crf[v] = kCrfOne;
         miss_slot[r] = v;
         miss_key[r] = key;
       }
@@ -196,10 +248,16 @@ __global__ __launch_bounds__(kLruThreads) void ensure_slots_kernel(BankRefs bk, 
                                                                   const int32_t* __restrict__ query, int width,
                                                                   int record_stats, int32_t* __restrict__ miss_slot,
                                                                   int32_t* __restrict__ miss_key,
-                                                                  int32_t* __restrict__ n_miss) {
+                                                                  int32_t* __restrict__ n_miss, int chunk_first) {
   __shared__ EnsureShared sh;
   const uint64_t now = *clock + 1;
-  const int m = ensure_query(sh, bk, now, query, width, record_stats, miss_slot, miss_key);
+  // a chunk starts at q_begin = 0; its later queries pin from that clock
+  uint64_t pin = now;
+  if (bk.chunk_start) {
+    if (!chunk_first) pin = *bk.chunk_start;
+    else if (threadIdx.x == 0) *bk.chunk_start = now;
+  }
+  const int m = ensure_query(sh, bk, now, pin, query, width, record_stats, miss_slot, miss_key);
   if (threadIdx.x == 0) {
     *n_miss = m;
     *clock = now;
@@ -216,11 +274,13 @@ __device__ __forceinline__ void ensure_batched_block(EnsureShared& sh, const Ban
                                                      int32_t* __restrict__ miss_key, int32_t* __restrict__ n_miss,
                                                      int32_t* __restrict__ n_total) {
   uint64_t now = *clock;
+  const uint64_t pin = now + 1;  // the call is one chunk: its first query's clock
+  if (bk.chunk_start && threadIdx.x == 0) *bk.chunk_start = pin;
   int total = 0;
   for (int q = 0; q < n_queries; ++q) {
     now += 1;
     const int w = q + 1 < n_queries ? width : last_width;
-    const int m = ensure_query(sh, bk, now, distinct + (size_t)q * width, w, record_stats, miss_slot + total,
+    const int m = ensure_query(sh, bk, now, pin, distinct + (size_t)q * width, w, record_stats, miss_slot + total,
                                miss_key + total);
     if (threadIdx.x == 0) n_miss[q] = m;
     total += m;
@@ -299,6 +359,9 @@ int check_bank(const scr_bank_desc* b) {
   SCR_CHECK_ARG(b->slot_key && b->slot_stamp && b->key_to_slot && b->clock && b->stats &&
                     b->decode_freq && b->err,
                 "bank: null state pointer");
+  SCR_CHECK_ARG(b->policy == SCR_POLICY_LRU || b->policy == SCR_POLICY_LRFU, "bank: unknown policy %d", b->policy);
+  SCR_CHECK_ARG(b->policy != SCR_POLICY_LRFU || (b->slot_crf && b->chunk_start && b->lrfu_decay > 0),
+                "bank: LRFU needs slot_crf, chunk_start and a decay factor in (0, 2^32)");
   return SCR_OK;
 }
 
@@ -313,6 +376,10 @@ static BankRefs bank_refs(const scr_bank_desc* b, int layer) {
   r.stats = b->stats;
   r.decode_freq = b->decode_freq;
   r.err = b->err;
+  r.policy = b->policy;
+  r.decay = b->lrfu_decay;
+  r.slot_crf = b->slot_crf;
+  r.chunk_start = b->chunk_start;
   return r;
 }
 
@@ -330,7 +397,7 @@ extern "C" int scr_ensure_slots(const scr_bank_desc* bank, int layer, const int3
   SCR_CHECK_ARG(distinct && miss_slot && miss_key && n_miss, "ensure_slots: null pointer");
   hipLaunchKernelGGL(scr::ensure_slots_kernel, dim3(1), dim3(scr::kLruThreads), 0, stream,
                      scr::bank_refs(bank, layer), bank->clock, distinct + q_begin, width, record_stats ? 1 : 0,
-                     miss_slot, miss_key, n_miss);
+                     miss_slot, miss_key, n_miss, q_begin == 0 ? 1 : 0);
   SCR_CHECK_LAUNCH();
   return SCR_OK;
 }

@@ -129,8 +129,11 @@ def pack_record_mxfp4(lay: L.RecordLayout, d: dict) -> np.ndarray:
 class Bank:
     """Device state of a slot bank plus its record rows (all caller-owned torch memory)."""
 
-    def __init__(self, S: int, n_layers: int, E: int, wdtype: int, record_bytes: int):
+    def __init__(self, S: int, n_layers: int, E: int, wdtype: int, record_bytes: int, policy: int = L.SCR_POLICY_LRU,
+                 lrfu_decay: int = 0):
+        """policy SCR_POLICY_LRFU takes lrfu_decay = floor(2^32 * 2^-lambda), 0 < it < 2^32."""
         self.S, self.L, self.E, self.wdtype, self.rec = S, n_layers, E, wdtype, int(record_bytes)
+        self.policy, self.lrfu_decay = int(policy), int(lrfu_decay)
         self.slot_key = _i32(S, -1)
         self.slot_stamp = torch.zeros(S, dtype=torch.int64, device=_DEV)
         self.key_to_slot = _i32(n_layers * E, -1)
@@ -140,9 +143,12 @@ class Bank:
         self.err = torch.zeros(1, dtype=torch.int32, device=_DEV)
         self.rows = torch.zeros(S * self.rec, dtype=torch.uint8, device=_DEV)
         self.row_table = torch.zeros(S, dtype=torch.int64, device=_DEV)
+        self.slot_crf = torch.zeros(S, dtype=torch.int32, device=_DEV)
+        self.chunk_start = torch.zeros(1, dtype=torch.int64, device=_DEV)
         self.desc = L.BankDesc(S, n_layers, E, wdtype, self.slot_key.data_ptr(), self.slot_stamp.data_ptr(),
                                self.key_to_slot.data_ptr(), self.clock.data_ptr(), self.stats.data_ptr(),
-                               self.decode_freq.data_ptr(), self.err.data_ptr(), self.rows.data_ptr(), self.rec)
+                               self.decode_freq.data_ptr(), self.err.data_ptr(), self.rows.data_ptr(), self.rec,
+                               self.policy, self.lrfu_decay, self.slot_crf.data_ptr(), self.chunk_start.data_ptr())
         L.fill_row_table(self.rows, S, self.rec, self.row_table, _stream())
 
     def load_fill(self, fill, stream=None):
@@ -153,6 +159,8 @@ class Bank:
         self.stats.zero_()
         self.decode_freq.zero_()
         self.err.zero_()
+        self.slot_crf.zero_()
+        self.chunk_start.zero_()
         L.bank_rebuild_map(self.desc, _stream(stream))
 
     def snapshot(self) -> dict:
@@ -165,6 +173,8 @@ class Bank:
             "stats": self.stats.cpu().numpy().astype(np.uint64),
             "decode_freq": self.decode_freq.cpu().numpy().astype(np.uint32),
             "err": int(self.err.item()),
+            "slot_crf": self.slot_crf.cpu().numpy().view(np.uint32).copy(),
+            "chunk_start": int(self.chunk_start.item()),
         }
 
     def slot_record(self, s: int) -> torch.Tensor:
