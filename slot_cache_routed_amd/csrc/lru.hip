@@ -83,6 +83,14 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
   const bool lrfu = bk.policy == SCR_POLICY_LRFU;
   const int tid = threadIdx.x;
   const int S = bk.S, E = bk.E;
+  // a query holding only sentinels (the tail of a chunk's padded distinct
+  // list) changes nothing but the clock (the caller's) and the query count
+  const int any_valid = __syncthreads_or(tid < width && query[tid] >= 0 && query[tid] < E);
+  if (!any_valid) {
+    if (tid == 0 && record_stats) bk.stats[3] += 1;
+    __syncthreads();
+    return 0;
+  }
   const int nwords = (S + 31) / 32;
   for (int i = tid; i < nwords; i += blockDim.x) sh.hit_bits[i] = 0;
   if (tid == 0) {

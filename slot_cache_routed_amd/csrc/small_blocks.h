@@ -100,6 +100,11 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
                                                   int32_t* __restrict__ n_active, int* cnt, int* rb, int* wave_tot) {
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave, nw = blockDim.x / kWave;
   for (int b = tid; b < nb; b += blockDim.x) cnt[b] = 0;
+  // every position a sentinel and every block unused, in coalesced passes;
+  // the layout and the scatter below overwrite the used ones (the barriers in
+  // between order the stores)
+  for (int q = tid; q < cap; q += blockDim.x) sorted_routes[q] = n;
+  for (int j = tid; j < cap / B; j += blockDim.x) block_bucket[j] = -1;
   __syncthreads();
   for (int r = tid; r < n; r += blockDim.x) {
     const int b = bucket_of(ids, map, num_ids, nb, r);
@@ -148,7 +153,6 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
       active_buckets[idx] = b;
       active_block_begin[idx] = off / B;
       ++idx;
-      for (int q = off + c; q < off + padded; ++q) sorted_routes[q] = n;
       for (int j = off / B; j < (off + padded) / B; ++j) block_bucket[j] = b;
     }
     cnt[b] = off;  // scatter position of the bucket's first route
@@ -159,8 +163,6 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
     *n_active = total1;
     active_block_begin[total1] = total0 / B;
   }
-  for (int q = total0 + tid; q < cap; q += blockDim.x) sorted_routes[q] = n;
-  for (int j = total0 / B + tid; j < cap / B; j += blockDim.x) block_bucket[j] = -1;
   __syncthreads();
   // Stable scatter in two steps.  First every wave takes 64-route chunks and
   // finds, by ballots over the bucket bits, each route's rank among the routes
@@ -185,9 +187,12 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
   }
   __syncthreads();
   if (wv == 0) {
+    // the next chunk's packed value is read one iteration ahead
+    int vn = lane < n ? rb[lane] : -1;
     for (int c = 0; c < nchunks; ++c) {
       const int r = c * kWave + lane;
-      const int v = r < n ? rb[r] : -1;
+      const int v = vn;
+      vn = r + kWave < n ? rb[r + kWave] : -1;
       const int b = v & 0x3fff, rank = (v >> 14) & 63;
       if (v >= 0) sorted_routes[cnt[b] + rank] = r;
       __builtin_amdgcn_wave_barrier();  // every lane has read the offsets before the leaders move them
