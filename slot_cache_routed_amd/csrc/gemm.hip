@@ -942,13 +942,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ o,
        i += (size_t)gridDim.x * blockDim.x) {
     const int t = (int)(i / h8), c8 = (int)(i % h8);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = t * k + j;
-      if (!flags[r]) continue;
-      float v[8];
-      load_row8(o + (size_t)r * H + 8 * c8, v);
+    // ranks in groups of four: every flag and row of a group is loaded
+    // unconditionally (clamped to the last rank), so the loads overlap; an
+    // unwritten route leaves the sum untouched (a select, not a branch)
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      int fl[4];
+      float v[4][8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += v[q];
+      for (int u = 0; u < 4; ++u) {
+        const int r = t * k + min(j0 + u, k - 1);
+        const int f = flags[r];
+        fl[u] = j0 + u < k ? f : 0;
+        load_row8(o + (size_t)r * H + 8 * c8, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fl[u] ? acc[q] + v[u][q] : acc[q];
     }
     if (BF16_OUT) {
       typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
