@@ -110,3 +110,31 @@ def test_lrfu_worked_example_through_the_abi():
         torch.cuda.synchronize()
         assert int(nm.item()) == 1 and int(ms.item()) == int(victim) and int(mk.item()) == experts[-1]
         assert before["slot_key"][int(victim)] == int(evicted)
+
+
+def test_lrfu_capacity_overflow_within_a_pinned_chunk():
+    # a chunk of three queries needing more slots than the bank has: the pin
+    # keeps its earlier admissions, so the last query's surplus misses set the
+    # capacity bit instead of evicting them (oracle and device alike)
+    L, LY, lay, pool = _setup(E=64, NL=1)
+    S, W_ = 10, 6
+    D = _decay(8)
+    bank = LY.Bank(S, 1, 64, L.SCR_W_BF16, lay.record_bytes, policy=L.SCR_POLICY_LRFU, lrfu_decay=D)
+    st = SlotBankState(S, 1, 64)
+    st.policy, st.decay_q32 = POLICY_LRFU, D
+    s = torch.cuda.current_stream().cuda_stream
+    distinct = np.arange(3, 3 + 18, dtype=np.int32)           # 18 distinct experts, 3 queries of 6
+    dev_d = torch.from_numpy(distinct).cuda()
+    ms = torch.full((W_,), -1, dtype=torch.int32, device="cuda")
+    mk = torch.full((W_,), -1, dtype=torch.int32, device="cuda")
+    nm = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for q0 in range(0, 18, W_):
+        L.ensure_slots(bank.desc, 0, dev_d, q0, W_, 1, ms, mk, nm, s)
+        rs, _ = ensure_slots(st, 0, distinct[q0:q0 + W_], True, chunk_first=(q0 == 0))
+        torch.cuda.synchronize()
+        assert int(nm.item()) == len(rs) and ms.cpu().numpy()[:len(rs)].tolist() == rs, q0
+    snap = bank.snapshot()
+    for key in STATE:
+        assert np.array_equal(np.asarray(snap[key]), np.asarray(_state(st)[key])), key
+    assert snap["err"] == st.err == 1
+    assert sorted(int(k) for k in snap["slot_key"]) == list(range(3, 13))   # the first ten admissions stay
