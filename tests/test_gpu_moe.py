@@ -132,6 +132,39 @@ def test_short_prefill_96_demand_path():
     assert torch.equal(d2["y"].float(), d["y"].to(torch.bfloat16).float())
 
 
+def test_real_size_chunk_of_200_tokens_admits_its_distinct_experts_in_queries_of_128():
+    # FreeToken PR #68's real-size case (200 tokens, top-10, 512 experts, 1,100
+    # slots): 2,000 routes, but the LRU only ever sees the chunk's distinct
+    # experts, at most 128 per query (handing it the routes was what broke)
+    from oracle import SlotBankState, dedup_sorted, ensure_slots
+    s = _setup("real_size_200", S=1100, W_=128, wdtype="bf16", T=200, E=512, k=10, H=2048, I=512, NL=3)
+    fill = W.bank_prefilled(s["seed"], s["S"], s["NL"], s["E"], 600, exclude_layer=0)
+    bank = _bank_for(s, fill)
+    sc = np.ones(s["E"], np.float32)
+    d = _run_demand(s, bank, sc)
+    y = _y(d)
+    ids, w = route_topk_softmax(s["logits"], s["k"])
+    distinct, nd, _ = dedup_sorted(ids.reshape(-1), s["E"])
+    st = SlotBankState.from_fill(fill)
+    expect = []
+    for q0 in range(0, len(distinct), 128):
+        ms, _ = ensure_slots(st, 0, distinct[q0:q0 + 128], False)
+        expect.append(len(ms))
+    nm = d["n_miss"].cpu().numpy().tolist()
+    flush(f"200-token chunk: {nd} distinct experts, misses per query {nm}")
+    assert nm == expect and max(nm) <= 128 and len(nm) == 4
+    snap = bank.snapshot()
+    for key in ("slot_key", "key_to_slot", "slot_stamp"):
+        assert np.array_equal(np.asarray(snap[key]), np.asarray(getattr(st, key))), key
+    tokens = list(range(0, 200, 13))
+    y_ref, _, _ = _oracle(s, tokens)
+    err = rel_max_err(y[tokens], y_ref)
+    flush(f"200-token chunk: rel max err on {len(tokens)} sampled tokens = {err:.3e}")
+    assert err <= TOL_BF16
+    st_y = _run_stream(s, sc)
+    assert torch.equal(d["y"], st_y["y"]), "slot path equals the whole-layer path bit for bit"
+
+
 def test_layer_view_sizes_tiles_and_scales_by_the_layer():
     s = _setup("layer_view_600")
     L = s["L"]
