@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "routed MoE layer ms + grouped-GEMM TFLOP/s at 96 and 4096 tokens, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+HOST_LINK_PEAK_GBS = 64.0   # PCIe Gen5 x16, one direction, nominal
 
 
 def _args():
@@ -273,6 +274,7 @@ def main():
         "kernels_us": {"gate_up": round(gu * 1e3, 2), "down": round(dn * 1e3, 2), "combine": round(cb * 1e3, 2)},
         "cold": {"ms_per_step": round(cold_ms, 3), "miss_copy_ms": round(copy_ms, 3),
                  "miss_copy_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 2), "misses": 160,
+                 "miss_copy_frac_host_link_peak": round(copy_bytes / (copy_ms * 1e-3) / 1e9 / HOST_LINK_PEAK_GBS, 3),
                  "note": "bank reset to its pre-filled state before each step; includes PCIe host-to-HBM copies"},
         "roofline": {"bound": "hbm", "kernel": "moe_gemm_kernel<bf16,2,2,gate/up>", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -407,6 +409,7 @@ def long_prefill(args) -> dict:
                     f"next-layer prefetch",
         "layer_ms_staged": round(total / NL, 3),
         "staging_GBps": round(staged_bytes / (total * 1e-3) / 1e9, 2),
+        "staging_frac_host_link_peak": round(staged_bytes / (total * 1e-3) / 1e9 / HOST_LINK_PEAK_GBS, 3),
         "staged_bytes_per_layer": staged_bytes // NL,
         "gemm_tflops": round(tflops, 2),
         "gemm_frac_bf16_mfma_peak": round(tflops / 2500.0, 4),
@@ -614,7 +617,8 @@ def align_bench() -> dict:
         us = t_a.elapsed_ms(t_b) * 1e3 / reps
         moved = 4 * n + 4 * cap + 4 * (cap // B)     # ids in, sorted routes and block ids out
         out[name] = {"routes": n, "buckets": nb, "block": B, "us": round(us, 2),
-                     "GBps": round(moved / (us * 1e-6) / 1e9, 1)}
+                     "GBps": round(moved / (us * 1e-6) / 1e9, 1),
+                     "frac_hbm_peak": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5)}
     return out
 
 
