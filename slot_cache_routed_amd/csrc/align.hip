@@ -3,207 +3,294 @@
 // A demand chunk aligns against the slot count, which is past the 1023 that
 // a one-block aligner can count (FreeToken PR #676, Solution third bullet
 // and Tests; gdevenyi's comment there: valid at 2100 and 4096).  Routes are
-// split into chunks; each chunk's per-bucket counts go to a bucket-major
-// matrix, a column scan turns them into per-chunk starting ranks, one
-// workgroup lays the buckets out, and a stable scatter places every route in
-// ascending route order inside its bucket (wave ballots give the rank among
-// equal buckets of one 64-route batch).
+// split into chunks of 1K-4K routes; each chunk's per-bucket counts go to a
+// chunk-major matrix, a column scan turns them into per-chunk starting
+// ranks, one workgroup lays the buckets out, and a stable scatter places
+// every route in ascending route order inside its bucket.  In the scatter
+// each wave of a chunk's workgroup owns a contiguous run of the chunk's
+// routes with its own LDS histogram, so the 64-route batches of one wave
+// need no workgroup barrier (wave ballots rank equal buckets of a batch).
 #include "small_blocks.h"
 
 namespace scr {
 
-constexpr int kAlignMatrixBudget = 1 << 18;  // entries of the chunk x bucket count matrix
+constexpr int kAlignMatrixBudget = 1 << 20;  // entries of the chunk x bucket count matrix (4 MiB)
+constexpr int kAlignLdsInts = 16384;         // per-wave histograms of the scatter: at most 64 KiB of LDS
+constexpr int kAlignLoads = 8;               // independent global loads a thread keeps in flight
 
 struct AlignPlan {
-  int nchunks, chunk;
+  int nchunks, chunk, waves;
 };
 
 static AlignPlan align_plan(int n, int nb) {
   AlignPlan p;
+  p.waves = nb <= kAlignLdsInts / 4 ? 4 : nb <= kAlignLdsInts / 2 ? 2 : 1;
+  // about 256 chunks for a large input, each of 1024..4096 routes (a chunk
+  // well past the bucket count keeps the per-bucket work of a workgroup
+  // small against its routes), fewer and longer if the matrix would pass its
+  // budget
+  long long chunk = ((long long)n + 255) / 256;
+  chunk = (chunk + 255) / 256 * 256;
+  if (chunk < 1024) chunk = 1024;
+  if (chunk > 4096) chunk = 4096;
+  long long nchunks = ((long long)n + chunk - 1) / chunk;
+  if (nchunks < 1) nchunks = 1;
   long long by_budget = kAlignMatrixBudget / nb;
   if (by_budget < 1) by_budget = 1;
-  long long by_n = (n + 63) / 64;
-  if (by_n < 1) by_n = 1;
-  p.nchunks = (int)(by_budget < by_n ? by_budget : by_n);
-  p.chunk = (int)(((long long)n + p.nchunks - 1) / p.nchunks);
-  if (p.chunk < 1) p.chunk = 1;
-  p.nchunks = (int)(((long long)n + p.chunk - 1) / p.chunk);
-  if (p.nchunks < 1) p.nchunks = 1;
+  if (nchunks > by_budget) {
+    nchunks = by_budget;
+    chunk = ((long long)n + nchunks - 1) / nchunks;
+    nchunks = ((long long)n + chunk - 1) / chunk;
+  }
+  p.chunk = (int)chunk;
+  p.nchunks = (int)nchunks;
   return p;
 }
 
+__device__ __forceinline__ void chunk_range(int n, int chunk, int c, int& r0, int& r1) {
+  const long long a = (long long)c * chunk;
+  r0 = (int)(a < n ? a : n);
+  r1 = (int)(a + chunk < n ? a + chunk : n);
+}
 
-// one wave per chunk: per-bucket counts of the chunk, written bucket-major
-__global__ __launch_bounds__(64) void align_count_kernel(const int32_t* __restrict__ ids, int n,
-                                                         const int32_t* __restrict__ map, int num_ids,
-                                                         int nb, int chunk, int nchunks,
-                                                         int32_t* __restrict__ cnt) {
+// one workgroup per chunk: per-bucket counts of the chunk, one matrix row
+__global__ __launch_bounds__(256) void align_count_kernel(const int32_t* __restrict__ ids, int n,
+                                                          const int32_t* __restrict__ map, int num_ids,
+                                                          int nb, int chunk, int32_t* __restrict__ cnt) {
   extern __shared__ int hist[];
   const int c = blockIdx.x;
   for (int b = threadIdx.x; b < nb; b += blockDim.x) hist[b] = 0;
   __syncthreads();
-  const int r0 = c * chunk, r1 = min(n, r0 + chunk);
-  for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) {
-    const int b = bucket_of(ids, map, num_ids, nb, r);
-    if (b >= 0) atomicAdd(&hist[b], 1);
+  int r0, r1;
+  chunk_range(n, chunk, c, r0, r1);
+  for (int rb = r0; rb < r1; rb += kAlignLoads * (int)blockDim.x) {  // loads in flight per thread
+    int bk[kAlignLoads];
+#pragma unroll
+    for (int u = 0; u < kAlignLoads; ++u) {
+      const int r = rb + u * (int)blockDim.x + (int)threadIdx.x;
+      bk[u] = r < r1 ? bucket_of(ids, map, num_ids, nb, r) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kAlignLoads; ++u)
+      if (bk[u] >= 0) atomicAdd(&hist[bk[u]], 1);
   }
   __syncthreads();
-  for (int b = threadIdx.x; b < nb; b += blockDim.x) cnt[(size_t)b * nchunks + c] = hist[b];
+  int32_t* row = cnt + (size_t)c * nb;
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) row[b] = hist[b];
 }
 
-// one wave per bucket: exclusive scan over chunks in place, bucket total out
-__global__ __launch_bounds__(256) void align_colscan_kernel(int32_t* __restrict__ cnt, int nb, int nchunks,
-                                                            int32_t* __restrict__ total) {
-  const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-  if (b >= nb) return;
-  const int lane = lane_id();
-  int32_t* col = cnt + (size_t)b * nchunks;
-  int carry = 0;
-  for (int c0 = 0; c0 < nchunks; c0 += kWave) {
-    const int c = c0 + lane;
-    const int v = c < nchunks ? col[c] : 0;
-    int s = v;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(s, off, kWave);
-      if (lane >= off) s += o;
-    }
-    if (c < nchunks) col[c] = carry + s - v;
-    carry += __shfl(s, kWave - 1, kWave);
-  }
-  if (lane == 0) total[b] = carry;
-}
+// 64 buckets per workgroup, one lane per bucket; the 16 waves split the
+// chunks into contiguous runs: exclusive scan down each column in place,
+// bucket total out
+constexpr int kColRun = 16;  // chunks per wave held in registers
 
-// one workgroup: padded bucket offsets, active list, padded total
-__global__ __launch_bounds__(1024) void align_layout_kernel(const int32_t* __restrict__ total, int nb, int B,
-                                                            int32_t* __restrict__ bucket_off,
-                                                            int32_t* __restrict__ active_buckets,
-                                                            int32_t* __restrict__ active_block_begin,
-                                                            int32_t* __restrict__ n_active,
-                                                            int32_t* __restrict__ n_post_pad) {
-  __shared__ int wave_tot[2][kWave];
-  __shared__ int carry[2];
-  if (threadIdx.x == 0) carry[0] = carry[1] = 0;
-  __syncthreads();
-  const int lane = lane_id(), wv = threadIdx.x / kWave, nw = blockDim.x / kWave;
-  for (int b0 = 0; b0 < nb; b0 += blockDim.x) {
-    const int b = b0 + threadIdx.x;
-    const int c = b < nb ? total[b] : 0;
-    const int padded = (c + B - 1) / B * B;
-    const int act = c > 0;
-    int s0 = padded, s1 = act;
+__global__ __launch_bounds__(1024) void align_colscan_kernel(int32_t* __restrict__ cnt, int nb, int nchunks,
+                                                             int32_t* __restrict__ total) {
+  __shared__ int part[1024 / kWave][kWave];
+  const int lane = lane_id(), w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const int b = blockIdx.x * kWave + lane;
+  const int q = (nchunks + nw - 1) / nw;
+  const int c0 = min(nchunks, w * q), c1 = min(nchunks, c0 + q);
+  int run = 0;
+  if (q <= kColRun) {  // the usual case: one load per chunk, all in flight at once
+    int v[kColRun];
+    int sum = 0;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o0 = __shfl_up(s0, off, kWave), o1 = __shfl_up(s1, off, kWave);
-      if (lane >= off) {
-        s0 += o0;
-        s1 += o1;
-      }
+    for (int i = 0; i < kColRun; ++i) {
+      v[i] = (b < nb && c0 + i < c1) ? cnt[(size_t)(c0 + i) * nb + b] : 0;
+      sum += v[i];
     }
-    if (lane == kWave - 1) {
-      wave_tot[0][wv] = s0;
-      wave_tot[1][wv] = s1;
-    }
+    part[w][lane] = sum;
     __syncthreads();
-    int before0 = carry[0], before1 = carry[1];
-    for (int w = 0; w < wv; ++w) {
-      before0 += wave_tot[0][w];
-      before1 += wave_tot[1][w];
+    for (int u = 0; u < w; ++u) run += part[u][lane];
+#pragma unroll
+    for (int i = 0; i < kColRun; ++i) {
+      if (b < nb && c0 + i < c1) cnt[(size_t)(c0 + i) * nb + b] = run;
+      run += v[i];
     }
-    const int off_b = before0 + s0 - padded;  // exclusive
-    const int idx = before1 + s1 - act;
+  } else {
+    int sum = 0;
     if (b < nb) {
-      bucket_off[b] = off_b;
-      if (act) {
-        active_buckets[idx] = b;
-        active_block_begin[idx] = off_b / B;
+#pragma unroll 8
+      for (int c = c0; c < c1; ++c) sum += cnt[(size_t)c * nb + b];
+    }
+    part[w][lane] = sum;
+    __syncthreads();
+    for (int u = 0; u < w; ++u) run += part[u][lane];
+    if (b < nb) {
+#pragma unroll 8
+      for (int c = c0; c < c1; ++c) {
+        const int v = cnt[(size_t)c * nb + b];
+        cnt[(size_t)c * nb + b] = run;
+        run += v;
       }
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int t0 = 0, t1 = 0;
-      for (int w = 0; w < nw; ++w) {
-        t0 += wave_tot[0][w];
-        t1 += wave_tot[1][w];
-      }
-      carry[0] += t0;
-      carry[1] += t1;
-    }
-    __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    *n_post_pad = carry[0];
-    *n_active = carry[1];
-    active_block_begin[carry[1]] = carry[0] / B;
+  if (w == nw - 1 && b < nb) total[b] = run;  // the last run ends at the last chunk
+}
+
+// one workgroup: padded bucket offsets, active list, padded total.  Each
+// thread owns a contiguous run of at most 16 buckets.
+constexpr int kLayoutThreads = 1024;
+constexpr int kLayoutRun = SCR_MAX_BUCKETS / kLayoutThreads;
+static_assert(kLayoutRun * kLayoutThreads == SCR_MAX_BUCKETS, "layout runs cover every bucket");
+
+__global__ __launch_bounds__(kLayoutThreads) void align_layout_kernel(const int32_t* __restrict__ total, int nb,
+                                                                      int B, int32_t* __restrict__ bucket_off,
+                                                                      int32_t* __restrict__ active_buckets,
+                                                                      int32_t* __restrict__ active_block_begin,
+                                                                      int32_t* __restrict__ n_active,
+                                                                      int32_t* __restrict__ n_post_pad) {
+  __shared__ int wave_tot[2][kLayoutThreads / kWave];
+  const int lane = lane_id(), wv = threadIdx.x / kWave;
+  const int per = (nb + kLayoutThreads - 1) / kLayoutThreads;
+  const int b0 = min(nb, (int)threadIdx.x * per), b1 = min(nb, b0 + per);
+  int cnt[kLayoutRun];
+  int pad_sum = 0, act_sum = 0;
+#pragma unroll
+  for (int i = 0; i < kLayoutRun; ++i) {
+    cnt[i] = b0 + i < b1 ? total[b0 + i] : 0;
+    pad_sum += (cnt[i] + B - 1) / B * B;
+    act_sum += cnt[i] > 0;
+  }
+  int s0 = pad_sum, s1 = act_sum;  // inclusive scans over the wave
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o0 = __shfl_up(s0, off, kWave), o1 = __shfl_up(s1, off, kWave);
+    if (lane >= off) {
+      s0 += o0;
+      s1 += o1;
+    }
+  }
+  if (lane == kWave - 1) {
+    wave_tot[0][wv] = s0;
+    wave_tot[1][wv] = s1;
+  }
+  __syncthreads();
+  int off = s0 - pad_sum, idx = s1 - act_sum;  // exclusive, then past the earlier waves
+  for (int u = 0; u < wv; ++u) {
+    off += wave_tot[0][u];
+    idx += wave_tot[1][u];
+  }
+#pragma unroll
+  for (int i = 0; i < kLayoutRun; ++i) {
+    if (b0 + i < b1) {
+      bucket_off[b0 + i] = off;
+      if (cnt[i] > 0) {
+        active_buckets[idx] = b0 + i;
+        active_block_begin[idx] = off / B;
+        ++idx;
+      }
+      off += (cnt[i] + B - 1) / B * B;
+    }
+  }
+  if (threadIdx.x == kLayoutThreads - 1) {  // the last run ends at the last bucket
+    *n_post_pad = off;
+    *n_active = idx;
+    active_block_begin[idx] = off / B;
   }
 }
 
-// one wave per chunk: stable scatter of the chunk's routes, 64 at a time
-__global__ __launch_bounds__(64) void align_scatter_kernel(const int32_t* __restrict__ ids, int n,
-                                                           const int32_t* __restrict__ map, int num_ids,
-                                                           int nb, int chunk, int nchunks,
-                                                           const int32_t* __restrict__ cnt,
-                                                           const int32_t* __restrict__ bucket_off,
-                                                           int32_t* __restrict__ sorted_routes) {
-  extern __shared__ int base[];
-  const int c = blockIdx.x;
-  const int lane = lane_id();
-  for (int b = lane; b < nb; b += kWave) base[b] = bucket_off[b] + cnt[(size_t)b * nchunks + c];
+// One workgroup per chunk, one contiguous run of it per wave: the wave's
+// histogram, per-wave starting positions of every bucket, then a stable
+// scatter of the run 64 routes at a time.  The same launch writes the block
+// table and the padding: every nchunks-th bucket (from the chunk index on)
+// gets its block ids and the sentinel in its padding, and the blocks past the
+// last bucket are split over the workgroups.
+__global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int n,
+                                                            const int32_t* __restrict__ map, int num_ids,
+                                                            int nb, int B, int chunk, int stash_ok,
+                                                            const int32_t* __restrict__ cnt,
+                                                            const int32_t* __restrict__ total,
+                                                            const int32_t* __restrict__ bucket_off,
+                                                            const int32_t* __restrict__ n_post_pad, int nblocks,
+                                                            int32_t* __restrict__ block_bucket,
+                                                            int32_t* __restrict__ sorted_routes) {
+  extern __shared__ int lds[];
+  const int c = blockIdx.x, nchunks = gridDim.x;
+  const int lane = lane_id(), w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  int* base = lds;             // [waves][nb]: counts of each wave's run, then its running positions
+  int* stash = lds + nw * nb;  // [chunk] when stash_ok: the bucket of every route of the chunk
+  for (int i = threadIdx.x; i < nw * nb; i += blockDim.x) base[i] = 0;
+  __syncthreads();
+  int r0, r1;
+  chunk_range(n, chunk, c, r0, r1);
+  const int per = ((r1 - r0 + nw - 1) / nw + kWave - 1) / kWave * kWave;
+  const int s0 = min(r1, r0 + w * per), s1 = min(r1, s0 + per);
+  int* mine = base + w * nb;
+  for (int rb = s0; rb < s1; rb += kAlignLoads * kWave) {
+    int bk[kAlignLoads];
+#pragma unroll
+    for (int u = 0; u < kAlignLoads; ++u) {
+      const int r = rb + u * kWave + lane;
+      bk[u] = r < s1 ? bucket_of(ids, map, num_ids, nb, r) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kAlignLoads; ++u) {
+      const int r = rb + u * kWave + lane;
+      if (r < s1) {
+        if (stash_ok) stash[r - r0] = bk[u];
+        if (bk[u] >= 0) atomicAdd(&mine[bk[u]], 1);
+      }
+    }
+  }
+  __syncthreads();
+  const int32_t* row = cnt + (size_t)c * nb;
+  for (int b0 = threadIdx.x; b0 < nb; b0 += kAlignLoads * (int)blockDim.x) {
+    int start[kAlignLoads];
+#pragma unroll
+    for (int u = 0; u < kAlignLoads; ++u) {
+      const int b = b0 + u * (int)blockDim.x;
+      start[u] = b < nb ? bucket_off[b] + row[b] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kAlignLoads; ++u) {
+      const int b = b0 + u * (int)blockDim.x;
+      if (b < nb) {
+        int run = start[u];
+        for (int v = 0; v < nw; ++v) {
+          const int t = base[v * nb + b];
+          base[v * nb + b] = run;
+          run += t;
+        }
+      }
+    }
+  }
   __syncthreads();
   int nbits = 0;
   while ((1 << nbits) < nb) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int r0 = c * chunk, r1 = min(n, r0 + chunk);
-  for (int rb = r0; rb < r1; rb += kWave) {
+  for (int rb = s0; rb < s1; rb += kWave) {  // the same trip count on every lane of the wave
     const int r = rb + lane;
-    const int b = r < r1 ? bucket_of(ids, map, num_ids, nb, r) : -1;
-    uint64_t peers = __ballot(b >= 0);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const uint64_t ones = __ballot(b >= 0 && ((b >> bit) & 1));
-      peers &= ((b >> bit) & 1) ? ones : ~ones;
-    }
+    int b = -1;
+    if (r < s1) b = stash_ok ? stash[r - r0] : bucket_of(ids, map, num_ids, nb, r);
+    const uint64_t peers = bucket_peers(b, nbits);
+    const uint64_t below = peers & lt_mask;
     int pos = 0;
-    if (b >= 0) pos = base[b] + __popcll(peers & lt_mask);
-    __syncthreads();  // every lane has read base[] before it moves
+    if (b >= 0) pos = mine[b] + __popcll(below);
+    __builtin_amdgcn_wave_barrier();  // the wave's reads of its histogram precede the update below
     if (b >= 0) {
       sorted_routes[pos] = r;
-      if ((peers & lt_mask) == 0) base[b] += __popcll(peers);  // lowest peer advances the bucket
+      if (below == 0) mine[b] += __popcll(peers);  // lowest peer advances the bucket
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
   }
-}
-
-// grid-stride over blocks: block bucket ids and the sentinel in every padding entry
-__global__ __launch_bounds__(256) void align_fill_kernel(int n, int B, int nblocks,
-                                                         const int32_t* __restrict__ total,
-                                                         const int32_t* __restrict__ bucket_off,
-                                                         const int32_t* __restrict__ active_buckets,
-                                                         const int32_t* __restrict__ active_block_begin,
-                                                         const int32_t* __restrict__ n_active_p,
-                                                         int32_t* __restrict__ block_bucket,
-                                                         int32_t* __restrict__ sorted_routes) {
-  const int n_active = *n_active_p;
-  const int end_block = active_block_begin[n_active];
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < nblocks; j += gridDim.x * blockDim.x) {
-    if (j >= end_block) {
-      block_bucket[j] = -1;
-      for (int q = 0; q < B; ++q) sorted_routes[(size_t)j * B + q] = n;
-      continue;
-    }
-    // last active entry whose first block is <= j
-    int lo = 0, hi = n_active - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (active_block_begin[mid] <= j) lo = mid;
-      else hi = mid - 1;
-    }
-    const int b = active_buckets[lo];
-    block_bucket[j] = b;
-    const int fill_from = bucket_off[b] + total[b];  // first padding position of the bucket
-    for (int q = 0; q < B; ++q) {
-      const int pos = j * B + q;
-      if (pos >= fill_from) sorted_routes[pos] = n;
-    }
+  // block ids and padding of this workgroup's buckets
+  for (long long bl = c + (long long)threadIdx.x * nchunks; bl < nb; bl += (long long)blockDim.x * nchunks) {
+    const int b = (int)bl;
+    const int t = total[b];
+    if (t == 0) continue;
+    const int off = bucket_off[b];
+    const int end = off + (t + B - 1) / B * B;
+    for (int j = off / B; j < end / B; ++j) block_bucket[j] = b;
+    for (int q = off + t; q < end; ++q) sorted_routes[q] = n;
+  }
+  // this workgroup's share of the unused blocks
+  const int end_block = *n_post_pad / B;
+  const long long tail = (long long)(nblocks - end_block) * B;
+  for (long long e = (long long)c * blockDim.x + threadIdx.x; e < tail; e += (long long)nchunks * blockDim.x) {
+    sorted_routes[(size_t)end_block * B + e] = n;
+    if (e % B == 0) block_bucket[end_block + e / B] = -1;
   }
 }
 
@@ -271,25 +358,22 @@ extern "C" int scr_align_blocks(const int32_t* ids, int n, const int32_t* id_to_
   int32_t* total = cnt + (size_t)p.nchunks * num_buckets;
   int32_t* bucket_off = total + num_buckets;
   const size_t lds = (size_t)num_buckets * sizeof(int);
-  hipLaunchKernelGGL(scr::align_count_kernel, dim3(p.nchunks), dim3(64), lds, stream, ids, n, id_to_bucket,
-                     num_ids, num_buckets, p.chunk, p.nchunks, cnt);
+  hipLaunchKernelGGL(scr::align_count_kernel, dim3(p.nchunks), dim3(256), lds, stream, ids, n, id_to_bucket,
+                     num_ids, num_buckets, p.chunk, cnt);
   SCR_CHECK_LAUNCH();
-  hipLaunchKernelGGL(scr::align_colscan_kernel, dim3((num_buckets + 3) / 4), dim3(256), 0, stream, cnt,
-                     num_buckets, p.nchunks, total);
+  hipLaunchKernelGGL(scr::align_colscan_kernel, dim3((num_buckets + scr::kWave - 1) / scr::kWave), dim3(1024), 0,
+                     stream, cnt, num_buckets, p.nchunks, total);
   SCR_CHECK_LAUNCH();
-  hipLaunchKernelGGL(scr::align_layout_kernel, dim3(1), dim3(1024), 0, stream, total, num_buckets, block_size,
-                     bucket_off, active_buckets, active_block_begin, n_active, n_post_pad);
-  SCR_CHECK_LAUNCH();
-  hipLaunchKernelGGL(scr::align_scatter_kernel, dim3(p.nchunks), dim3(64), lds, stream, ids, n, id_to_bucket,
-                     num_ids, num_buckets, p.chunk, p.nchunks, cnt, bucket_off, sorted_routes);
+  hipLaunchKernelGGL(scr::align_layout_kernel, dim3(1), dim3(scr::kLayoutThreads), 0, stream, total, num_buckets,
+                     block_size, bucket_off, active_buckets, active_block_begin, n_active, n_post_pad);
   SCR_CHECK_LAUNCH();
   const int nblocks = (int)(scr_align_capacity(n, num_buckets, block_size) / block_size);
-  if (nblocks > 0) {
-    int grid = (nblocks + 255) / 256;
-    if (grid > 1024) grid = 1024;
-    hipLaunchKernelGGL(scr::align_fill_kernel, dim3(grid), dim3(256), 0, stream, n, block_size, nblocks, total,
-                       bucket_off, active_buckets, active_block_begin, n_active, block_bucket, sorted_routes);
-    SCR_CHECK_LAUNCH();
-  }
+  const int hist_ints = p.waves * num_buckets;
+  const int stash_ok = hist_ints + p.chunk <= scr::kAlignLdsInts;
+  const size_t scatter_lds = (size_t)(hist_ints + (stash_ok ? p.chunk : 0)) * sizeof(int);
+  hipLaunchKernelGGL(scr::align_scatter_kernel, dim3(p.nchunks), dim3(scr::kWave * p.waves), scatter_lds, stream,
+                     ids, n, id_to_bucket, num_ids, num_buckets, block_size, p.chunk, stash_ok, cnt, total,
+                     bucket_off, n_post_pad, nblocks, block_bucket, sorted_routes);
+  SCR_CHECK_LAUNCH();
   return SCR_OK;
 }

@@ -48,6 +48,23 @@ __device__ __forceinline__ int bucket_of(const int32_t* __restrict__ ids, const 
   return (b >= 0 && b < nb) ? b : -1;
 }
 
+// Lanes of the wave whose bucket equals this lane's, from one ballot per
+// bucket bit (every lane of the wave calls it; nbits = bits of the largest
+// bucket, at most 14).  Dropped lanes (b < 0) are in no lane's mask; a
+// dropped lane's own result is meaningless.
+__device__ __forceinline__ uint64_t bucket_peers(int b, int nbits) {
+  uint64_t peers = __ballot(b >= 0);
+#pragma unroll
+  for (int bit = 0; bit < 14; ++bit) {
+    if (bit < nbits) {  // the same on every lane
+      const int set = (b >> bit) & 1;
+      const uint64_t ones = __ballot(set);
+      peers &= ones ^ ((uint64_t)set - 1);  // ones where the bit is set, ~ones where it is clear
+    }
+  }
+  return peers;
+}
+
 // Distinct ids as a sorted fixed-length list: marks in LDS, a scan, a
 // scatter (a counting sort over ids).  pos: LDS [kDedupMaxE]; wave_tot: LDS
 // [kWave + 1].
@@ -177,11 +194,7 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
   for (int c = wv; c < nchunks; c += nw) {
     const int r = c * kWave + lane;
     const int b = r < n ? rb[r] : -1;
-    uint64_t peers = __ballot(b >= 0);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const uint64_t ones = __ballot(b >= 0 && ((b >> bit) & 1));
-      peers &= ((b >> bit) & 1) ? ones : ~ones;
-    }
+    const uint64_t peers = bucket_peers(b, nbits);
     const int rank = __popcll(peers & lt_mask);
     if (b >= 0) rb[r] = b | (rank << 14) | ((rank == 0 ? __popcll(peers) : 0) << 20);
   }

@@ -89,3 +89,24 @@ def test_align_long_prefill_routes():
     ids, _ = route_topk_softmax(lg, 10)
     ids = ids.reshape(-1)
     _compare(_align_gpu(ids, None, 512, 16), align_blocks(ids, None, 512, 16))
+
+
+@pytest.mark.parametrize("n,Nb,B", [
+    (300000, 2100, 16),     # ~235 chunks of four waves, a ragged last chunk and ragged wave runs
+    (100000, 8192, 32),     # two waves per chunk
+    (300000, 16384, 16),    # one wave per chunk, chunks lengthened past 4096 by the matrix budget
+    (5000, 1024, 64),       # a single chunk
+])
+def test_align_many_chunks_matches_oracle(n, Nb, B):
+    flush(f"align many chunks n={n} Nb={Nb} B={B}")
+    ids = W.uniform_ids(11, n, Nb + Nb // 8).copy()   # about one id in nine is past the buckets
+    _compare(_align_gpu(ids, None, Nb, B), align_blocks(ids, None, Nb, B))
+
+
+def test_align_many_chunks_with_few_hot_buckets():
+    # long runs of equal buckets inside every 64-route batch: the lowest peer
+    # advances each bucket by the batch's whole count
+    flush("align hot buckets")
+    ids = (W.uniform_ids(12, 200000, 4) * 997 + 5).astype(np.int32)
+    ids[::7] = W.uniform_ids(13, ids[::7].size, 4096)
+    _compare(_align_gpu(ids, None, 4096, 16), align_blocks(ids, None, 4096, 16))
