@@ -3,7 +3,7 @@
 // A demand chunk aligns against the slot count, which is past the 1023 that
 // a one-block aligner can count (FreeToken PR #676, Solution third bullet
 // and Tests; gdevenyi's comment there: valid at 2100 and 4096).  Routes are
-// split into chunks of 1K-4K routes; each chunk's per-bucket counts go to a
+// split into chunks of 512-4K routes; each chunk's per-bucket counts go to a
 // chunk-major matrix, a column scan turns them into per-chunk starting
 // ranks, one workgroup lays the buckets out, and a stable scatter places
 // every route in ascending route order inside its bucket.  In the scatter
@@ -25,13 +25,13 @@ struct AlignPlan {
 static AlignPlan align_plan(int n, int nb) {
   AlignPlan p;
   p.waves = nb <= kAlignLdsInts / 4 ? 4 : nb <= kAlignLdsInts / 2 ? 2 : 1;
-  // about 256 chunks for a large input, each of 1024..4096 routes (a chunk
+  // about 256 chunks for a large input, each of 512..4096 routes (a chunk
   // well past the bucket count keeps the per-bucket work of a workgroup
   // small against its routes), fewer and longer if the matrix would pass its
   // budget
   long long chunk = ((long long)n + 255) / 256;
   chunk = (chunk + 255) / 256 * 256;
-  if (chunk < 1024) chunk = 1024;
+  if (chunk < 512) chunk = 512;
   if (chunk > 4096) chunk = 4096;
   long long nchunks = ((long long)n + chunk - 1) / chunk;
   if (nchunks < 1) nchunks = 1;
