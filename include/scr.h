@@ -333,7 +333,8 @@ int scr_align_blocks(const int32_t* ids, int n, const int32_t* id_to_bucket, int
 int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_cfg* cfg);
 /* workspace of scr_grouped_moe_forward: h [cap][I] bf16 + per-route rows [T*k][H]
  * (fp32 for bf16 weights, bf16 for the narrow formats) + per-route flags; for
- * SCR_W_MXFP4_A8 the MXFP8 codes and scales of x and of h in place of h */
+ * SCR_W_MXFP4_A8 the MXFP8 codes and scales of x and of h in place of h; for
+ * SCR_W_NVFP4 also an fp16 copy of x [T][H] and its row exponents [T] */
 int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cfg* cfg,
                       size_t* bytes);
 
@@ -365,7 +366,15 @@ int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cf
  * to MXFP8 per row (scr_quantize_mxfp8, between marks 0 and 1), each route's
  * h to MXFP8 per 32-column block in the gate/up epilogue, and both GEMMs run
  * on the block-scaled fp8 x fp4 MFMA; needs H and I multiples of 512, at most
- * 4096 (SCR_ENOTSUP otherwise, nothing launched). */
+ * 4096 (SCR_ENOTSUP otherwise, nothing launched).
+ * SCR_W_NVFP4 with many rows per expert (the wide kernels: cfg.m_chunk 112,
+ * H and I multiples of 512): the gate/up runs on the fp16 MFMA.  Between
+ * marks 1 and 2 (so inside the gate/up time) each row of x is copied to
+ * fp16 times 2^e, e putting the row's largest magnitude in [2^14, 2^15); the
+ * weights decode exactly to fp16 (e2m1 times e4m3 fits), and the fp32
+ * accumulators are multiplied by 2^-e after the global scale.  The products
+ * and sums are those of the bf16 values, except that elements below 2^-28
+ * of their row's largest magnitude round as fp16 subnormals. */
 int scr_grouped_moe_forward(const scr_routed_experts* view, const void* x, int T,
                             const float* topk_w, const int32_t* sorted_routes,
                             const int32_t* active_buckets, const int32_t* active_block_begin,

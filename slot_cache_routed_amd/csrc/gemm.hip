@@ -55,6 +55,13 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// the same product on fp16 operands (carried in the same 16-byte registers)
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma16_f16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+
 // ------------------------------------------------------------ NVFP4 decode
 // e4m3 (OCP E4M3FN) code -> float (finite codes only), without branches:
 // |v| = (m + 8 [e > 0]) * 2^(max(e, 1) - 10), exact in fp32 (the subnormal
@@ -121,6 +128,9 @@ struct GemmArgs {
   const uint8_t* xs;  // [T][H/32]
   uint8_t* hq;        // [h_rows][I]
   uint8_t* hs;        // [h_rows][I/32]
+  // NVFP4 wide gate/up: x as fp16, row t scaled by 2^xe[t]
+  const uint16_t* x16;  // [T][H]
+  const int32_t* xe;    // [T]
   int T, k, R, H, I, B, h_rows, E;
 };
 
@@ -263,6 +273,22 @@ struct BFrag<SCR_W_NVFP4, NT> {
   __device__ __forceinline__ bf16x8 get_hw(int t, int st) const {
     const float scale = (st >> 1) ? __builtin_amdgcn_cvt_f32_fp8((int)sc[t], 1) : __builtin_amdgcn_cvt_f32_fp8((int)sc[t], 0);
     return dequant8_hw(codes[t][st], scale);
+  }
+  // as fp16: e2m1 codes and the e4m3 scale both convert exactly, and their
+  // product (at most 6 significant bits, magnitude in [2^-10, 2688]) is exact
+  // in fp16, so one packed fp16 multiply per pair finishes the decode
+  __device__ __forceinline__ bf16x8 get_f16(int t, int st) const {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)sc[t], 1.0f, false);
+    const _Float16 sv = (st >> 1) ? s2[1] : s2[0];
+    const h2 sa = {sv, sv};
+    const unsigned c = codes[t][st];
+    u32x4 o;
+    o[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0) * sa);
+    o[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1) * sa);
+    o[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2) * sa);
+    o[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3) * sa);
+    return __builtin_bit_cast(bf16x8, o);
   }
 };
 
@@ -605,6 +631,92 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
+// the NVFP4 wide gate/up runs on fp16 (half the decode work of bf16: see
+// BFrag<SCR_W_NVFP4>::get_f16); every other wide pass on bf16
+template <int WDT, bool GATEUP>
+struct WideF16A {
+  static constexpr bool value = WDT == SCR_W_NVFP4 && GATEUP;
+};
+
+// x as fp16 for the F16A gate/up, one wave per token: the row is scaled by
+// 2^e, e = 15 - (the exponent of its largest magnitude in frexp form), which
+// puts that magnitude in [2^14, 2^15).  Every bf16 value of the row at or
+// above 2^-28 of it is then exact in fp16, so the products and fp32 sums are
+// those of the bf16 values times 2^e (smaller values round as fp16
+// subnormals).  An all-zero or non-finite row keeps e = 0.  NC > 0: the row
+// is H = 512 * NC wide and stays in registers between the two steps; NC = 0:
+// any multiple of 512, read twice.
+__device__ __forceinline__ float bf16_lo(unsigned v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+__device__ __forceinline__ u32x4 scaled_f16x8(const u32x4& v, int e) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const h2 p = {(_Float16)__builtin_ldexpf(bf16_lo(v[i]), e), (_Float16)__builtin_ldexpf(bf16_hi(v[i]), e)};
+    o[i] = __builtin_bit_cast(unsigned, p);
+  }
+  return o;
+}
+
+template <int NC>
+__global__ __launch_bounds__(256) void x_to_f16_kernel(const bf16* __restrict__ x, int T, int H,
+                                                       uint16_t* __restrict__ x16, int32_t* __restrict__ xe) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;
+  if (t >= T) return;
+  const u32x4* row = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
+  u32x4* out = reinterpret_cast<u32x4*>(x16 + (size_t)t * H);
+  const int n8 = H / 8;
+  float m = 0.0f;
+  u32x4 v[NC > 0 ? NC : 1];
+  if constexpr (NC > 0) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) v[c] = row[c * 64 + lane];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[c][i])), fabsf(bf16_hi(v[c][i]))));
+  } else {
+    for (int c = lane; c < n8; c += 64) {
+      const u32x4 w = row[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  int e = 0;
+  if (m > 0.0f && m <= 3.4028235e38f) {
+    int ex;
+    (void)__builtin_frexpf(m, &ex);
+    e = 15 - ex;
+  }
+  if constexpr (NC > 0) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) out[c * 64 + lane] = scaled_f16x8(v[c], e);
+  } else {
+    for (int c = lane; c < n8; c += 64) out[c] = scaled_f16x8(row[c], e);
+  }
+  if (lane == 0) xe[t] = e;
+}
+
+static int launch_x_to_f16(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid((a.T + 3) / 4), block(256);
+  uint16_t* x16 = const_cast<uint16_t*>(a.x16);
+  int32_t* xe = const_cast<int32_t*>(a.xe);
+  switch (a.H / 512) {
+    case 1: hipLaunchKernelGGL(x_to_f16_kernel<1>, grid, block, 0, s, a.x, a.T, a.H, x16, xe); break;
+    case 2: hipLaunchKernelGGL(x_to_f16_kernel<2>, grid, block, 0, s, a.x, a.T, a.H, x16, xe); break;
+    case 4: hipLaunchKernelGGL(x_to_f16_kernel<4>, grid, block, 0, s, a.x, a.T, a.H, x16, xe); break;
+    case 8: hipLaunchKernelGGL(x_to_f16_kernel<8>, grid, block, 0, s, a.x, a.T, a.H, x16, xe); break;
+    default: hipLaunchKernelGGL(x_to_f16_kernel<0>, grid, block, 0, s, a.x, a.T, a.H, x16, xe); break;
+  }
+  SCR_CHECK_LAUNCH();
+  return SCR_OK;
+}
+
 template <int WDT, int NTW>
 struct BLoads {  // vector memory instructions per wave for one K block of weights
   static constexpr int value = WDT == SCR_W_BF16 ? 4 * NTW : 2 * NTW;  // fp8: two code loads; fp4: codes + scales
@@ -612,7 +724,7 @@ struct BLoads {  // vector memory instructions per wave for one K block of weigh
 
 template <int WDT, int MT, bool GATEUP, int EW, int NTW, int MTC>
 __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row, const int* row_route,
-                                          const float* row_w, bf16* As0, bf16* As1, bf16* As2,
+                                          const float* row_w, const float* row_rs, bf16* As0, bf16* As1, bf16* As2,
                                           bf16* As3, uint32_t* stg, int m0, __amdgpu_buffer_rsrc_t wrsrc,
                                           const int* toff0, const int* soff0, float gs, int nkb, int c_begin,
                                           int c_end) {
@@ -622,12 +734,14 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
   constexpr int CT = GATEUP ? EW * NTW / 2 : EW * NTW;  // row tiles per chunk and tensor half
   constexpr int tile_bytes = WFmt<WDT>::tile;
   constexpr int stile_bytes = WFmt<WDT>::stile;
+  constexpr bool F16A = WideF16A<WDT, GATEUP>::value;  // fp16 activations and weights
   bf16* const bufs[kWideBufs] = {As0, As1, As2, As3};
 
-  // activations through a buffer resource over x (gate/up) or h (down)
-  const __amdgpu_buffer_rsrc_t arsrc =
-      GATEUP ? __builtin_amdgcn_make_buffer_rsrc((void*)a.x, (short)0, a.T * a.H * 2, 0x00020000)
-             : __builtin_amdgcn_make_buffer_rsrc((void*)a.h, (short)0, a.h_rows * a.I * 2, 0x00020000);
+  // activations through a buffer resource over x (gate/up; its fp16 copy
+  // for F16A) or h (down)
+  const void* const abase = GATEUP ? (F16A ? (const void*)a.x16 : (const void*)a.x) : (const void*)a.h;
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)abase, (short)0, GATEUP ? a.T * a.H * 2 : a.h_rows * a.I * 2, 0x00020000);
   // direct-load sources of this lane: the 4 * MTC wave instructions of a K
   // block (each fills 64 16-byte chunks = 4 rows) are dealt round-robin to the
   // EW waves; every wave issues the same count NA (a wave past the end repeats
@@ -695,8 +809,17 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
         for (int i = 0; i < 4; i += 2)
 #pragma unroll
           for (int t = 0; t < NTW / 2; ++t) {
-            const unsigned p = pack_bf16(silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]),
-                                         silu_mul(gs * acc[mt][t][i + 1], gs * acc[mt][t + NTW / 2][i + 1]));
+            unsigned p;
+            if constexpr (F16A) {
+              // the row's power of two comes off after the global scale, as
+              // exact multiplies (gs * acc is then the bf16 path's value)
+              const float s0 = row_rs[mt * 16 + grp * 4 + i], s1 = row_rs[mt * 16 + grp * 4 + i + 1];
+              p = pack_bf16(silu_mul(gs * acc[mt][t][i] * s0, gs * acc[mt][t + NTW / 2][i] * s0),
+                            silu_mul(gs * acc[mt][t][i + 1] * s1, gs * acc[mt][t + NTW / 2][i + 1] * s1));
+            } else {
+              p = pack_bf16(silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]),
+                            silu_mul(gs * acc[mt][t][i + 1], gs * acc[mt][t + NTW / 2][i + 1]));
+            }
             sh16[(grp * 4 + i) * HC + 16 * t + col] = (uint16_t)p;
             sh16[(grp * 4 + i + 1) * HC + 16 * t + col] = (uint16_t)(p >> 16);
           }
@@ -802,9 +925,15 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
           // one weight tile at a time: its decode, then its MTC products
 #pragma unroll
           for (int t = 0; t < NTW; ++t) {
-            const bf16x8 bt = bc.get_hw(t, st);
+            if constexpr (F16A) {
+              const bf16x8 bt = bc.get_f16(t, st);
 #pragma unroll
-            for (int mt = 0; mt < MTC; ++mt) acc[mt][t] = mfma16(af[mt], bt, acc[mt][t]);
+              for (int mt = 0; mt < MTC; ++mt) acc[mt][t] = mfma16_f16(af[mt], bt, acc[mt][t]);
+            } else {
+              const bf16x8 bt = bc.get_hw(t, st);
+#pragma unroll
+              for (int mt = 0; mt < MTC; ++mt) acc[mt][t] = mfma16(af[mt], bt, acc[mt][t]);
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -838,6 +967,8 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
   // read once per pass so that the epilogue does no dependent global loads
   __shared__ int row_route[GATEUP ? 1 : MT * 16];
   __shared__ float row_w[GATEUP ? 1 : MT * 16];
+  // F16A gate/up: 2^-xe of each pass row's token, undoing its fp16 scaling
+  __shared__ float row_rs[WideF16A<WDT, GATEUP>::value ? MT * 16 : 1];
   __shared__ __attribute__((aligned(256))) uint32_t stg[EW * kWideStage / 4];  // per-wave epilogue tiles
   if (GATEUP) gateup_prologue(a);
   // XCD-aware order: all groups of bucket j run on XCD j mod 8
@@ -886,6 +1017,10 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
         }
       }
       src_row[i] = off;
+      if constexpr (WideF16A<WDT, GATEUP>::value) {
+        const int r = i < rows ? a.sorted_routes[m0 + i] : -1;
+        row_rs[i] = (r >= 0 && r < a.R) ? __builtin_ldexpf(1.0f, -a.xe[r / a.k]) : 1.0f;
+      }
       if (!GATEUP) {
         const int r = i < rows ? a.sorted_routes[m0 + i] : -1;
         const bool valid = r >= 0 && r < a.R;
@@ -897,8 +1032,8 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
 #define SCR_WIDE_PASS(n)                                                                                   \
   case n:                                                                                                  \
     if constexpr (MT >= n)                                                                                 \
-      wide_pass<WDT, MT, GATEUP, EW, NTW, n>(a, src_row, row_route, row_w, As0, As1, As2, As3, stg, m0, wrsrc, \
-                                             toff0, soff0, gs, nkb, c_begin, c_end);                            \
+      wide_pass<WDT, MT, GATEUP, EW, NTW, n>(a, src_row, row_route, row_w, row_rs, As0, As1, As2, As3, stg, m0, \
+                                             wrsrc, toff0, soff0, gs, nkb, c_begin, c_end);                     \
     break;
     switch (rows / 16) {
       SCR_WIDE_PASS(1)
@@ -1319,6 +1454,7 @@ __global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int group
 struct WsLayout {
   size_t h_off, o_off, flags_off, bytes;
   size_t xq_off, xs_off, hs_off;  // W4A8 only (h_off then holds the MXFP8 codes of h)
+  size_t x16_off, xe_off;         // NVFP4 only: x as fp16 and its row exponents
   int h_rows;
 };
 
@@ -1347,6 +1483,12 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
   const size_t row_bytes = wdtype == SCR_W_BF16 ? sizeof(float) : sizeof(uint16_t);
   w.flags_off = align256(w.o_off + (size_t)R * H * row_bytes);
   w.bytes = align256(w.flags_off + (size_t)R * sizeof(int32_t));
+  w.x16_off = w.xe_off = 0;
+  if (wdtype == SCR_W_NVFP4) {
+    w.x16_off = w.bytes;
+    w.xe_off = align256(w.x16_off + (size_t)T * H * sizeof(uint16_t));
+    w.bytes = align256(w.xe_off + (size_t)T * sizeof(int32_t));
+  }
   return w;
 }
 
@@ -1375,6 +1517,10 @@ static int launch_wide_gemms(const GemmArgs& a, int max_active, hipEvent_t* mark
   const int g_gu = a.I / (8 * NTW * kWideWaves);
   const int nch_dn = a.H / (16 * NTW * kWideWaves);
   const int g_dn = nch_dn >= 2 ? nch_dn / 2 : 1;  // two chunks per workgroup
+  if constexpr (WideF16A<WDT, true>::value) {
+    const int rc = launch_x_to_f16(a, s);
+    if (rc) return rc;
+  }
   hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, true, kWideWaves, NTW>), dim3(8 * rows8 * g_gu), dim3(64 * kWideWaves),
                      0, s, a, g_gu);
   SCR_CHECK_LAUNCH();
@@ -1527,6 +1673,8 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   a.xs = wsb + wl.xs_off;
   a.hq = wsb + wl.h_off;
   a.hs = wsb + wl.hs_off;
+  a.x16 = reinterpret_cast<const uint16_t*>(wsb + wl.x16_off);
+  a.xe = reinterpret_cast<const int32_t*>(wsb + wl.xe_off);
   a.o = wsb + wl.o_off;
   a.flags = reinterpret_cast<int32_t*>(wsb + wl.flags_off);
   a.T = T;

@@ -325,6 +325,50 @@ def test_nvfp4_every_scale_code_and_every_e2m1_code(H, I):
     assert err <= TOL_FP4
 
 
+@pytest.mark.parametrize("H", [512, 1536])
+def test_nvfp4_wide_gate_up_rows_of_every_magnitude(H):
+    """The wide NVFP4 gate/up takes x as fp16 scaled per token by a power of
+    two.  Tokens whose rows are zero, scaled by 2^-40 or 2^40, or hold one
+    element 2^20 or 2^35 above the rest (the rest then fp16 subnormals) each
+    match the oracle to the FP4 tolerance relative to their own row, and the
+    stream path stays bit-identical.  H = 512 keeps the row in registers
+    during its conversion, H = 1536 takes the conversion's general loop."""
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    T, E, k, I = 48, 4, 2, 512                  # 24 rows per expert: the wide kernels
+    src = ExpertSource(61, H, I, "nvfp4")
+    lay = LY.record_layout(L.SCR_W_NVFP4, H, I)
+    pool = LY.HostPool(1, E, lay.record_bytes, E)
+    fill_pool(pool, src, lay, range(E))
+    lg = W.logits_normal(61, 0, T, E)
+    x = W.activations_normal(61, T, H).astype(np.float64)
+    x[0] = 0.0
+    x[1] *= 2.0 ** -40
+    x[2] *= 2.0 ** 40
+    x[3, 7] = 2.0 ** 20
+    x[4, H - 212] = -(2.0 ** 35)
+    x[5] *= 2.0 ** -20
+    x[5, 0] = 2.0 ** 10
+    xb = W.f32_to_bf16_bits(x.astype(np.float32))
+    bank = LY.Bank(E, 1, E, L.SCR_W_NVFP4, lay.record_bytes)
+    sc = np.ones(E, np.float32)
+    d = LY.demand_layer(bank, pool, 0, _dev(lg), _dev(xb.view(np.int16)), _dev(sc), width=4, shape=(k, H, I))
+    assert d.cfg_used.m_chunk == 112
+    y = _y(d)
+    ids, w = route_topk_softmax(lg, k)
+    y_ref = moe_layer(bf16_bits_to_f64(xb), ids, w, src.f64)
+    assert np.all(y[0] == 0.0)
+    for t in range(1, T):
+        r = float(np.sqrt(np.mean(y_ref[t] ** 2)))
+        err = float(np.max(np.abs(y[t].astype(np.float64) - y_ref[t]))) / r
+        if t < 8:
+            flush(f"nvfp4 wide row {t}: rms {r:.3e}, rel max err {err:.3e}")
+        assert np.isfinite(err) and err <= TOL_FP4, (t, err)
+    lb = LY.LayerStreamBuffer(E, lay.record_bytes)
+    st = LY.stream_layer(pool, 0, _dev(lg), _dev(xb.view(np.int16)), _dev(sc), lb, L.SCR_W_NVFP4, shape=(k, H, I))
+    assert torch.equal(d["y"], st["y"])
+
+
 def test_forward_with_no_tokens_launches_nothing():
     import slot_cache_routed_amd.layer as LY
     import slot_cache_routed_amd._lib as L
