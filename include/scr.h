@@ -173,7 +173,8 @@ typedef struct scr_bank_desc {
  * The pinned host source of every copy [P3 What; P4 Prefill staging].
  *   key_rows_dev  device [L*E]: device-accessible addresses (the device-mapped
  *                 view of pinned memory) of each key's record, read by kernels;
- *   key_rows_host host   [L*E]: the same records' host addresses, used by DMA.
+ *   key_rows_host host   [L*E]: the same records' host addresses (stage_plan
+ *                 merges host-adjacent records into runs with them).
  * Several keys may share one record (payload aliasing); records are 16-byte
  * aligned and record_bytes is a multiple of 16.
  */
@@ -396,8 +397,9 @@ int scr_quantize_mxfp8(const void* x, long long rows, int cols, uint8_t* codes, 
 
 /* stream_layer_async [P1 Problem: the streamed path copies every expert of the
  * layer].  Copies the records of experts 0..E-1 of `layer` from the pool into
- * dst (device, E * record_bytes), expert e at e * record_bytes, by DMA on
- * `stream` (adjacent host records are merged into one copy). */
+ * dst (device, E * record_bytes), expert e at e * record_bytes, on `stream`:
+ * a copy kernel reads each record through key_rows_dev (the pinned pool's
+ * device-mapped view; about 57 GB/s over PCIe 5 against about 50 for DMA). */
 int scr_stream_layer_async(const scr_host_pool* pool, int layer, void* dst, hipStream_t stream);
 
 /* stage_plan [P4 Prefill staging: the placement tables only change in decode,
@@ -412,10 +414,14 @@ int scr_stage_plan(const scr_bank_desc* bank, const scr_host_pool* pool, int lay
                    int n_layers, int32_t* host_map, scr_run* runs, int max_runs, int* n_runs,
                    hipStream_t stream);
 
-/* stage_rows_async [P4 Prefill staging: DMA from the pinned source on a side
- * stream, layer i+1 while layer i computes, ordered with events].  On `side`:
- * waits for wait_on (nullable), copies every run of `layer` in runs[0..n_runs)
- * into dst_layer_buf at e * record_bytes, then records `done` (nullable). */
+/* stage_rows_async [P4 Prefill staging: copies from the pinned source on a
+ * side stream, layer i+1 while layer i computes, ordered with events].  On
+ * `side`: waits for wait_on (nullable), copies every run of `layer` in
+ * runs[0..n_runs) into dst_layer_buf at e * record_bytes, then records `done`
+ * (nullable).  The copy is a kernel of 64 workgroups reading each record
+ * through key_rows_dev (the pages' design uses DMA; the kernel sustains about
+ * 57 GB/s against about 50 and leaves most CUs to the GEMM on the other
+ * stream); the run list travels as kernel arguments, 240 runs per launch. */
 int scr_stage_rows_async(const scr_host_pool* pool, const scr_run* runs, int n_runs, int layer,
                          void* dst_layer_buf, hipStream_t side, hipEvent_t wait_on,
                          hipEvent_t done);

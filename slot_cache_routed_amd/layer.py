@@ -2,8 +2,7 @@
 path and the staged prefill path.
 
 PyTorch is used here only to own device / pinned memory and to name streams
-and events; every step of the path is a libscr entry point (HIP kernels or
-DMA).  The drivers keep every intermediate buffer so tests can compare each
+and events; every step of the path is a libscr entry point (HIP kernels).  The drivers keep every intermediate buffer so tests can compare each
 step with the oracle.
 """
 from __future__ import annotations
@@ -418,7 +417,7 @@ class StagedPrefill:
     Two device buffers, each the size of a whole layer, alternate by layer;
     the non-resident map of every layer is read back once (scr_stage_plan,
     the step's one host sync) and turned into runs; layer i+1's runs are
-    copied by DMA on a side stream while layer i computes, ordered with events
+    copied by a copy kernel on a side stream while layer i computes, ordered with events
     (the copy into a buffer waits for the layer that last read it).  Each
     layer then runs route, align over its experts and the grouped GEMM on a
     view whose rows point into the bank (resident) or the staging buffer.
