@@ -306,8 +306,9 @@ __global__ __launch_bounds__(kPlanThreads) void align_small_kernel(const int32_t
   __shared__ int cnt[kSmallBuckets];  // counts, then running scatter positions
   __shared__ int rb[kSmallRoutes];    // bucket of each route (-1 dropped)
   __shared__ int wave_tot[2 * kWave];
+  __shared__ uint16_t tab[kAlignTab];  // per-(bucket, batch) counts of the scatter
   align_small_block(ids, n, map, num_ids, nb, B, cap, sorted_routes, block_bucket, n_post_pad, active_buckets,
-                    active_block_begin, n_active, cnt, rb, wave_tot);
+                    active_block_begin, n_active, cnt, rb, wave_tot, tab);
 }
 
 }  // namespace scr

@@ -22,6 +22,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kCopyThreads = 256;
 constexpr uint64_t kCopyChunk = 64 * 1024;  // bytes per work item
 constexpr int kCopyUnroll = kCopyChunk / (kCopyThreads * 16);  // 16-byte loads per thread
+constexpr uint64_t kMissGrid = 256;  // workgroups of a miss copy
 
 // Work item w = (miss i, chunk c).  Each thread issues all of its 16-byte
 // loads before its stores so many PCIe reads are in flight.
@@ -165,8 +166,10 @@ extern "C" int scr_copy_misses(const scr_bank_desc* bank, const scr_host_pool* p
   SCR_CHECK_ARG(miss_slot && miss_key && n_miss, "copy_misses: null pointer");
   if (max_miss == 0) return SCR_OK;
   const uint64_t chunks = (pool->record_bytes + scr::kCopyChunk - 1) / scr::kCopyChunk;
+  // 256 workgroups keep 16 MB of host reads in flight, several times what the
+  // host link needs; a launch with nothing to copy (a warm chunk) stays short
   uint64_t grid = (uint64_t)max_miss * chunks;
-  if (grid > 2048) grid = 2048;
+  if (grid > scr::kMissGrid) grid = scr::kMissGrid;
   hipLaunchKernelGGL(scr::copy_misses_kernel, dim3((unsigned)grid), dim3(scr::kCopyThreads), 0, stream,
                      bank->rows, pool->record_bytes, pool->key_rows_dev, miss_slot, miss_key, n_miss,
                      max_miss, bank->L * bank->E, bank->S);

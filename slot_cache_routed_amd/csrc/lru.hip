@@ -326,6 +326,7 @@ union PlanShared {
     int cnt[kSmallBuckets];
     int rb[kSmallRoutes];
     int wave_tot[2 * kWave];
+    uint16_t tab[kAlignTab];
   } al;
 };
 
@@ -344,7 +345,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_chunk_kernel(
   __syncthreads();
   align_small_block(ids, n, bk.key_to_slot + (size_t)bk.layer * bk.E, bk.E, bk.S, B, cap, sorted_routes,
                     block_bucket, n_post_pad, active_buckets, active_block_begin, n_active, sh.al.cnt, sh.al.rb,
-                    sh.al.wave_tot);
+                    sh.al.wave_tot, sh.al.tab);
 }
 
 __global__ void rebuild_map_clear(int32_t* __restrict__ key_to_slot, int n) {

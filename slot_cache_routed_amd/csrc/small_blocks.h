@@ -10,6 +10,7 @@ constexpr int kPlanThreads = 1024;
 constexpr int kDedupMaxE = 8192;
 constexpr int kSmallRoutes = 4096;   // routes the one-workgroup align takes
 constexpr int kSmallBuckets = 8192;  // buckets the one-workgroup align takes
+constexpr int kAlignTab = 20480;     // entries of its (bucket, 64-route batch) count table
 
 // inclusive scan of one int per thread across the block; returns the block total
 __device__ __forceinline__ int block_inclusive_scan(int v, int* wave_tot) {
@@ -114,9 +115,18 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
                                                   int32_t* __restrict__ block_bucket, int32_t* __restrict__ n_post_pad,
                                                   int32_t* __restrict__ active_buckets,
                                                   int32_t* __restrict__ active_block_begin,
-                                                  int32_t* __restrict__ n_active, int* cnt, int* rb, int* wave_tot) {
+                                                  int32_t* __restrict__ n_active, int* cnt, int* rb, int* wave_tot,
+                                                  uint16_t* tab) {
   const int tid = threadIdx.x, lane = lane_id(), wv = tid / kWave, nw = blockDim.x / kWave;
+  const int nchunks = (n + kWave - 1) / kWave;
+  // the scatter ranks across 64-route batches through a table of per-(bucket,
+  // batch) counts when it fits, else by one wave walking the batches in order
+  const bool use_tab = (long long)nb * nchunks <= kAlignTab;
   for (int b = tid; b < nb; b += blockDim.x) cnt[b] = 0;
+  if (use_tab) {
+    uint32_t* t32 = reinterpret_cast<uint32_t*>(tab);
+    for (int i = tid; i < (nb * nchunks + 1) / 2; i += blockDim.x) t32[i] = 0;
+  }
   // every position a sentinel and every block unused, in coalesced passes;
   // the layout and the scatter below overwrite the used ones (the barriers in
   // between order the stores)
@@ -181,25 +191,57 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
     active_block_begin[total1] = total0 / B;
   }
   __syncthreads();
-  // Stable scatter in two steps.  First every wave takes 64-route chunks and
-  // finds, by ballots over the bucket bits, each route's rank among the routes
-  // of its bucket in the chunk and (at the first of them) their count, packed
-  // into rb as bucket | rank << 14 | count << 20 (buckets < 2^13).  Then one
-  // wave walks the chunks in order: position = the bucket's running offset +
-  // rank, and the first route of each bucket advances the offset.
+  // Stable scatter.  First every wave takes 64-route batches and finds, by
+  // ballots over the bucket bits, each route's rank among the routes of its
+  // bucket in the batch, packed into rb as bucket | rank << 14 (buckets <
+  // 2^13), and at the first of them their count.  With the table: each count
+  // goes to tab[bucket][batch], one thread per bucket turns its row into
+  // running counts, and every route lands at offset + running count + rank.
+  // Without it the count rides in rb (<< 20) and one wave walks the batches in
+  // order: position = the bucket's running offset + rank, and the first route
+  // of each bucket advances the offset.
   int nbits = 0;
   while ((1 << nbits) < nb) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int nchunks = (n + kWave - 1) / kWave;
   for (int c = wv; c < nchunks; c += nw) {
     const int r = c * kWave + lane;
     const int b = r < n ? rb[r] : -1;
     const uint64_t peers = bucket_peers(b, nbits);
     const int rank = __popcll(peers & lt_mask);
-    if (b >= 0) rb[r] = b | (rank << 14) | ((rank == 0 ? __popcll(peers) : 0) << 20);
+    if (b >= 0) {
+      if (use_tab) {
+        rb[r] = b | (rank << 14);
+        if (rank == 0) tab[b * nchunks + c] = (uint16_t)__popcll(peers);
+      } else {
+        rb[r] = b | (rank << 14) | ((rank == 0 ? __popcll(peers) : 0) << 20);
+      }
+    }
   }
   __syncthreads();
-  if (wv == 0) {
+  if (use_tab) {
+    for (int b = tid; b < nb; b += blockDim.x) {
+      uint16_t* row = tab + b * nchunks;
+      int run = 0;
+      for (int c0 = 0; c0 < nchunks; c0 += 16) {  // 16 reads in flight, then the running counts
+        int v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) v[u] = c0 + u < nchunks ? row[c0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if (c0 + u < nchunks) row[c0 + u] = (uint16_t)run;
+          run += v[u];
+        }
+      }
+    }
+    __syncthreads();
+    for (int r = tid; r < n; r += blockDim.x) {
+      const int v = rb[r];
+      if (v >= 0) {
+        const int b = v & 0x3fff, rank = v >> 14;
+        sorted_routes[cnt[b] + tab[b * nchunks + r / kWave] + rank] = r;
+      }
+    }
+  } else if (wv == 0) {
     // the next chunk's packed value is read one iteration ahead
     int vn = lane < n ? rb[lane] : -1;
     for (int c = 0; c < nchunks; ++c) {

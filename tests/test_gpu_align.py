@@ -110,3 +110,15 @@ def test_align_many_chunks_with_few_hot_buckets():
     ids = (W.uniform_ids(12, 200000, 4) * 997 + 5).astype(np.int32)
     ids[::7] = W.uniform_ids(13, ids[::7].size, 4096)
     _compare(_align_gpu(ids, None, 4096, 16), align_blocks(ids, None, 4096, 16))
+
+
+@pytest.mark.parametrize("n,Nb,B", [(4096, 200, 16), (4000, 256, 32), (960, 1100, 16), (64, 8192, 64),
+                                    (2000, 4096, 16), (4096, 8192, 32)])
+def test_align_one_workgroup_table_and_walk_scatters(n, Nb, B):
+    # the one-workgroup align ranks across 64-route batches through a
+    # (bucket, batch) count table of up to 20480 entries when it fits (the
+    # first four: 64, 63, 15 and 1 batches) and by one wave walking the
+    # batches otherwise (the last two)
+    flush(f"align small n={n} Nb={Nb} B={B}")
+    ids = W.uniform_ids(21, n, Nb + Nb // 10).copy()
+    _compare(_align_gpu(ids, None, Nb, B), align_blocks(ids, None, Nb, B))
