@@ -16,6 +16,10 @@ namespace scr {
 
 constexpr int kLruThreads = kPlanThreads;
 constexpr int kSlotBits = 20;  // SCR_MAX_SLOTS <= 2^18 < 2^20
+// a batched call reads every query entry's slot once, up front, when the
+// chunk has at most kEnsPrefetch entries and the bank at most kPrefetchSlots
+constexpr int kEnsPrefetch = 4096;
+constexpr int kPrefetchSlots = 65536;
 
 __device__ __forceinline__ uint64_t cand_key(uint64_t stamp, int slot) {
   return (stamp << kSlotBits) | (uint64_t)slot;
@@ -32,6 +36,11 @@ struct EnsureShared {
   int nhit, nmiss, nsel, evict, npinned;
   uint64_t prefix;
   unsigned rank;
+  // batched calls: the chunk's query entries and their slots at its start,
+  // and the slots its earlier queries gave to misses
+  int pf_e[kEnsPrefetch];
+  int pf_s[kEnsPrefetch];
+  uint32_t taken[kPrefetchSlots / 32];
 };
 
 struct BankRefs {
@@ -77,20 +86,18 @@ __device__ __forceinline__ uint64_t victim_key(const BankRefs& bk, int s, uint64
 // to miss_slot/miss_key[0 ..) and their number returned (in every thread).
 // `pin`: under LRFU only slots stamped before it are candidates (the chunk's
 // first query's clock).  Called by all threads of the workgroup.
+// pfe, pfs, taken (all null, or all set by a batched call): this query's
+// entries and their slots read at the chunk's start, and the bitmap of slots
+// that the chunk's earlier queries gave to misses.  A key's slot changes only
+// when an earlier query of the chunk takes it for a miss (keys are distinct
+// across the chunk's queries), so a prefetched slot is exact unless taken.
 __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, uint64_t pin,
                             const int32_t* __restrict__ query, int width, int record_stats,
-                            int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_key) {
+                            int32_t* __restrict__ miss_slot, int32_t* __restrict__ miss_key,
+                            const int* pfe = nullptr, const int* pfs = nullptr, uint32_t* taken = nullptr) {
   const bool lrfu = bk.policy == SCR_POLICY_LRFU;
   const int tid = threadIdx.x;
   const int S = bk.S, E = bk.E;
-  // a query holding only sentinels (the tail of a chunk's padded distinct
-  // list) changes nothing but the clock (the caller's) and the query count
-  const int any_valid = __syncthreads_or(tid < width && query[tid] >= 0 && query[tid] < E);
-  if (!any_valid) {
-    if (tid == 0 && record_stats) bk.stats[3] += 1;
-    __syncthreads();
-    return 0;
-  }
   const int nwords = (S + 31) / 32;
   for (int i = tid; i < nwords; i += blockDim.x) sh.hit_bits[i] = 0;
   if (tid == 0) {
@@ -99,15 +106,24 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
     sh.nsel = 0;
     sh.npinned = 0;
   }
-  __syncthreads();
+  // a query holding only sentinels (the tail of a chunk's padded distinct
+  // list) changes nothing but the clock (the caller's) and the query count
+  const int qe = tid < width ? (pfe ? pfe[tid] : query[tid]) : -1;
+  const int any_valid = __syncthreads_or(qe >= 0 && qe < E);
+  if (!any_valid) {
+    if (tid == 0 && record_stats) bk.stats[3] += 1;
+    __syncthreads();
+    return 0;
+  }
 
   // lookup: one query entry per thread (width <= blockDim)
   int my_key = -1, is_miss = 0;
   if (tid < width) {
-    const int e = query[tid];
+    const int e = qe;
     if (e >= 0 && e < E) {
       my_key = bk.layer * E + e;
-      const int s = bk.key_to_slot[my_key];
+      int s = pfs ? pfs[tid] : bk.key_to_slot[my_key];
+      if (pfs && s >= 0 && ((taken[s >> 5] >> (s & 31)) & 1u)) s = -1;  // evicted by an earlier query
       if (s >= 0) {
         if (lrfu) {  // the hit's value decayed to now, plus this reference
           const uint64_t c = crf_decay(bk.slot_crf[s], now - bk.slot_stamp[s], bk.decay) + kCrfOne;
@@ -121,8 +137,9 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
       }
     }
   }
+  const int m = __syncthreads_count(is_miss);
   // misses keep query order: exclusive scan of the miss flags
-  {
+  if (m > 0) {
     const int lane = lane_id(), wv = tid / kWave, nw = blockDim.x / kWave;
     int v = is_miss;
 #pragma unroll
@@ -147,9 +164,8 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
       sh.q_key[tid] = my_key;
       sh.q_miss_rank[tid] = is_miss ? before + v - 1 : -1;
     }
-    if (tid == 0) sh.nmiss = sh.wave_tot[nw - 1];
+    __syncthreads();
   }
-  __syncthreads();
   // LRFU: untouched slots stamped at or after the pin (earlier queries of the
   // chunk) are no candidates either
   if (lrfu) {
@@ -160,7 +176,6 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
     __syncthreads();
   }
 
-  const int m = sh.nmiss;
   const int n_cand = S - sh.nhit - sh.npinned;
   const int m_adm = m < n_cand ? m : n_cand;
 
@@ -231,6 +246,7 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
         bk.key_to_slot[key] = v;
         bk.slot_stamp[v] = now;
         if (lrfu) bk.slot_crf[v] = kCrfOne;
+        if (taken) atomicOr(&taken[v >> 5], 1u << (v & 31));
         miss_slot[r] = v;
         miss_key[r] = key;
       }
@@ -284,12 +300,24 @@ __device__ __forceinline__ void ensure_batched_block(EnsureShared& sh, const Ban
   uint64_t now = *clock;
   const uint64_t pin = now + 1;  // the call is one chunk: its first query's clock
   if (bk.chunk_start && threadIdx.x == 0) *bk.chunk_start = pin;
+  const int entries = (n_queries - 1) * width + last_width;
+  const bool pf = entries <= kEnsPrefetch && bk.S <= kPrefetchSlots;
+  if (pf) {  // every entry's slot in one round of loads
+    for (int i = threadIdx.x; i < entries; i += blockDim.x) {
+      const int e = distinct[i];
+      sh.pf_e[i] = e;
+      sh.pf_s[i] = (e >= 0 && e < bk.E) ? bk.key_to_slot[(size_t)bk.layer * bk.E + e] : -1;
+    }
+    for (int i = threadIdx.x; i < (bk.S + 31) / 32; i += blockDim.x) sh.taken[i] = 0;
+    __syncthreads();
+  }
   int total = 0;
   for (int q = 0; q < n_queries; ++q) {
     now += 1;
     const int w = q + 1 < n_queries ? width : last_width;
     const int m = ensure_query(sh, bk, now, pin, distinct + (size_t)q * width, w, record_stats, miss_slot + total,
-                               miss_key + total);
+                               miss_key + total, pf ? sh.pf_e + q * width : nullptr,
+                               pf ? sh.pf_s + q * width : nullptr, pf ? sh.taken : nullptr);
     if (threadIdx.x == 0) n_miss[q] = m;
     total += m;
   }
