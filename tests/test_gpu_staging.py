@@ -84,3 +84,46 @@ def test_staged_layers_equal_stream_and_oracle(T, n_layers, E, k, H, I, n_res, S
         err = rel_max_err(y, y_ref)
         flush(f"layer {layer}: sampled rel max err {err:.3e}")
         assert err <= 5e-2
+
+
+@pytest.mark.parametrize("pattern", ["alternating", "ragged"])
+def test_stage_rows_copies_every_run_across_launches(pattern):
+    """stage_rows_async moves each run of a layer's non-resident experts from
+    the pinned pool into the staging buffer at e * record_bytes and nothing
+    else: 256 single-record runs (more than one launch's worth of run
+    descriptors) or runs of mixed length, checked byte for byte against the
+    host records, with the staging buffer's other records left untouched."""
+    import slot_cache_routed_amd._lib as L
+    import slot_cache_routed_amd.layer as LY
+    NL, E, rec = 2, 512, 4096 + 256
+    layer = 1
+    flush(f"stage_rows runs: {pattern}")
+    pool = LY.HostPool(NL, E, rec, NL * E)
+    g = np.random.default_rng(17)
+    pool.records.copy_(torch.from_numpy(g.integers(0, 256, NL * E * rec, dtype=np.uint8)))
+    if pattern == "alternating":
+        runs = [(layer, e, 1) for e in range(0, E, 2)]
+    else:
+        runs, e = [], 0
+        while e < E:
+            n = int(g.integers(1, 9))
+            if g.random() < 0.6:
+                runs.append((layer, e, min(n, E - e)))
+            e += n + int(g.integers(1, 4))
+        runs.append((0, 3, 5))          # another layer's run: skipped for this layer
+    arr = (L.Run * len(runs))(*[L.Run(*r) for r in runs])
+    dst = torch.full((E * rec,), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    L.stage_rows_async(pool.desc, arr, len(runs), layer, dst, s, None, None)
+    torch.cuda.synchronize()
+    got = dst.cpu().view(E, rec)
+    staged = np.zeros(E, bool)
+    for (l, b, c) in runs:
+        if l == layer:
+            staged[b:b + c] = True
+    for e in range(E):
+        if staged[e]:
+            assert torch.equal(got[e], pool.key_record(layer * E + e)), e
+        else:
+            assert bool((got[e] == 0xA5).all()), e
+    assert staged.sum() > 0
