@@ -33,7 +33,7 @@ struct EnsureShared {
   int victim[SCR_MAX_QUERY_WIDTH];
   unsigned hist[256];
   int wave_tot[kWave + 1];
-  int nhit, nmiss, nsel, evict, npinned;
+  int nhit, nsel, evict, npinned;
   uint64_t prefix;
   unsigned rank;
   // batched calls: the chunk's query entries and their slots at its start,
