@@ -83,8 +83,8 @@ def calibrate_copy(steps: int):
 def main():
     args = _args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported on this build "
-              f"(multi-GPU sharding is described, not run)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library has no "
+              f"cross-GPU path (tensor- or expert-parallel sharding is not implemented)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
