@@ -374,6 +374,20 @@ def long_prefill(args) -> dict:
             reps.append((total, gu, dn))
     staged_bytes = sum(sp.staged_bytes(l) for l in layers)
     total = statistics.median(r[0] for r in reps)
+    # the staging copy alone, one layer's runs, by the copy kernel (what the
+    # pipeline uses) and by one hipMemcpyAsync per run (the pages' form)
+    copy_rates = {}
+    for name, fn in (("kernel", L.stage_rows_async), ("dma", L.stage_rows_dma_async)):
+        ts = []
+        for i in range(4):
+            t_a, t_b = L.Timer(), L.Timer()
+            torch.cuda.synchronize()
+            t_a.record(s)
+            fn(pool.desc, sp.runs, sp.n_runs, NL - 1, sp.staging[0], s, None, None)
+            t_b.record(s)
+            if i:
+                ts.append(t_a.elapsed_ms(t_b))
+        copy_rates[name] = round(sp.staged_bytes(NL - 1) / (statistics.median(ts) * 1e-3) / 1e9, 2)
     # grouped GEMM alone, data resident (the last staged layer's view), repeated
     b = bufs[-1]
     view = LY.make_view(layers[-1], E, k, H, I, L.SCR_W_NVFP4, E, sp.tables[(NL - 1) % 2], sc)
@@ -410,6 +424,7 @@ def long_prefill(args) -> dict:
         "layer_ms_staged": round(total / NL, 3),
         "staging_GBps": round(staged_bytes / (total * 1e-3) / 1e9, 2),
         "staging_frac_host_link_peak": round(staged_bytes / (total * 1e-3) / 1e9 / HOST_LINK_PEAK_GBS, 3),
+        "staging_copy_alone_GBps": copy_rates,
         "staged_bytes_per_layer": staged_bytes // NL,
         "gemm_tflops": round(tflops, 2),
         "gemm_frac_bf16_mfma_peak": round(tflops / 2500.0, 4),

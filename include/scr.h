@@ -425,6 +425,14 @@ int scr_stage_plan(const scr_bank_desc* bank, const scr_host_pool* pool, int lay
 int scr_stage_rows_async(const scr_host_pool* pool, const scr_run* runs, int n_runs, int layer,
                          void* dst_layer_buf, hipStream_t side, hipEvent_t wait_on,
                          hipEvent_t done);
+/* stage_rows_dma_async [P4 Prefill staging, in the pages' form: one
+ * hipMemcpyAsync per run from the pinned source on the side stream].  The
+ * same arguments, ordering and result as scr_stage_rows_async; each run's
+ * host records must be adjacent (scr_stage_plan builds runs so; SCR_EINVAL
+ * otherwise, nothing enqueued).  Uses key_rows_host. */
+int scr_stage_rows_dma_async(const scr_host_pool* pool, const scr_run* runs, int n_runs, int layer,
+                             void* dst_layer_buf, hipStream_t side, hipEvent_t wait_on,
+                             hipEvent_t done);
 
 /* ------------------------------------------------------------ helpers */
 

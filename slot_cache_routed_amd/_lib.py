@@ -31,7 +31,7 @@ EXPORTS = (
     "scr_align_capacity", "scr_align_workspace", "scr_align_blocks", "scr_tile_config",
     "scr_moe_workspace", "scr_grouped_moe_forward", "scr_quantize_mxfp8", "scr_stream_layer_async",
     "scr_stage_plan",
-    "scr_stage_rows_async", "scr_fill_row_table", "scr_fill_staged_rows", "scr_bank_rebuild_map",
+    "scr_stage_rows_async", "scr_stage_rows_dma_async", "scr_fill_row_table", "scr_fill_staged_rows", "scr_bank_rebuild_map",
     "scr_host_device_alias", "scr_prefill_on_demand", "scr_demand_capacity_ok", "scr_timer_create",
     "scr_timer_record", "scr_timer_elapsed_ms", "scr_timer_destroy", "scr_last_error", "scr_version",
 )
@@ -106,6 +106,7 @@ _SIGS = {
     "scr_stage_plan": (_I, [C.POINTER(BankDesc), C.POINTER(HostPoolDesc), _I, _I, _P, C.POINTER(Run), _I,
                             C.POINTER(_I), _P]),
     "scr_stage_rows_async": (_I, [C.POINTER(HostPoolDesc), C.POINTER(Run), _I, _I, _P, _P, _P, _P]),
+    "scr_stage_rows_dma_async": (_I, [C.POINTER(HostPoolDesc), C.POINTER(Run), _I, _I, _P, _P, _P, _P]),
     "scr_fill_row_table": (_I, [_P, _I, C.c_uint64, _P, _P]),
     "scr_fill_staged_rows": (_I, [C.POINTER(BankDesc), _I, _P, _P, _P]),
     "scr_bank_rebuild_map": (_I, [C.POINTER(BankDesc), _P]),
@@ -263,6 +264,11 @@ def stage_plan(bank: BankDesc, pool: HostPoolDesc, layer_begin, n_layers, host_m
 def stage_rows_async(pool: HostPoolDesc, runs, n_runs, layer, dst, side_stream, wait_on, done):
     _check("scr_stage_rows_async", load().scr_stage_rows_async(C.byref(pool), runs, n_runs, layer, _p(dst),
                                                                side_stream, wait_on, done))
+
+
+def stage_rows_dma_async(pool: HostPoolDesc, runs, n_runs, layer, dst, side_stream, wait_on, done):
+    _check("scr_stage_rows_dma_async", load().scr_stage_rows_dma_async(C.byref(pool), runs, n_runs, layer, _p(dst),
+                                                                       side_stream, wait_on, done))
 
 
 def fill_row_table(base, n, stride, bucket_rows, stream):

@@ -259,6 +259,38 @@ extern "C" int scr_stage_rows_async(const scr_host_pool* pool, const scr_run* ru
   return SCR_OK;
 }
 
+extern "C" int scr_stage_rows_dma_async(const scr_host_pool* pool, const scr_run* runs, int n_runs, int layer,
+                                        void* dst_layer_buf, hipStream_t side, hipEvent_t wait_on,
+                                        hipEvent_t done) {
+  int rc = scr::check_pool(pool);
+  if (rc) return rc;
+  SCR_CHECK_ARG(n_runs >= 0 && (n_runs == 0 || runs), "stage_rows_dma: bad runs");
+  SCR_CHECK_ARG(dst_layer_buf && pool->key_rows_host, "stage_rows_dma: null pointer");
+  SCR_CHECK_ARG(layer >= 0 && layer < pool->L, "stage_rows_dma: layer out of range");
+  for (int i = 0; i < n_runs; ++i)
+    SCR_CHECK_ARG(runs[i].e_begin >= 0 && runs[i].count >= 1 && runs[i].e_begin + runs[i].count <= pool->E,
+                  "stage_rows_dma: run %d out of the layer", i);
+  const uint64_t rec = pool->record_bytes;
+  for (int i = 0; i < n_runs; ++i) {  // a run's host records are adjacent (scr_stage_plan builds them so)
+    if (runs[i].layer != layer) continue;
+    const uint8_t* src0 = static_cast<const uint8_t*>(pool->key_rows_host[(size_t)layer * pool->E + runs[i].e_begin]);
+    for (int j = 1; j < runs[i].count; ++j)
+      SCR_CHECK_ARG(static_cast<const uint8_t*>(pool->key_rows_host[(size_t)layer * pool->E + runs[i].e_begin + j]) ==
+                        src0 + (uint64_t)j * rec,
+                    "stage_rows_dma: run %d is not contiguous in host memory", i);
+  }
+  if (wait_on) SCR_CHECK_HIP(hipStreamWaitEvent(side, wait_on, 0));
+  uint8_t* dst = static_cast<uint8_t*>(dst_layer_buf);
+  for (int i = 0; i < n_runs; ++i) {
+    if (runs[i].layer != layer) continue;
+    const uint8_t* src = static_cast<const uint8_t*>(pool->key_rows_host[(size_t)layer * pool->E + runs[i].e_begin]);
+    SCR_CHECK_HIP(hipMemcpyAsync(dst + (uint64_t)runs[i].e_begin * rec, src, (uint64_t)runs[i].count * rec,
+                                 hipMemcpyHostToDevice, side));
+  }
+  if (done) SCR_CHECK_HIP(hipEventRecord(done, side));
+  return SCR_OK;
+}
+
 extern "C" int scr_fill_row_table(const void* base, int n, uint64_t stride, const void** bucket_rows,
                                   hipStream_t stream) {
   SCR_CHECK_ARG(base && bucket_rows && n >= 1, "fill_row_table: bad arguments");

@@ -86,9 +86,11 @@ def test_staged_layers_equal_stream_and_oracle(T, n_layers, E, k, H, I, n_res, S
         assert err <= 5e-2
 
 
+@pytest.mark.parametrize("entry", ["kernel", "dma"])
 @pytest.mark.parametrize("pattern", ["alternating", "ragged"])
-def test_stage_rows_copies_every_run_across_launches(pattern):
-    """stage_rows_async moves each run of a layer's non-resident experts from
+def test_stage_rows_copies_every_run_across_launches(pattern, entry):
+    """stage_rows_async (the copy kernel) and stage_rows_dma_async (one
+    hipMemcpyAsync per run) move each run of a layer's non-resident experts from
     the pinned pool into the staging buffer at e * record_bytes and nothing
     else: 256 single-record runs (more than one launch's worth of run
     descriptors) or runs of mixed length, checked byte for byte against the
@@ -97,7 +99,7 @@ def test_stage_rows_copies_every_run_across_launches(pattern):
     import slot_cache_routed_amd.layer as LY
     NL, E, rec = 2, 512, 4096 + 256
     layer = 1
-    flush(f"stage_rows runs: {pattern}")
+    flush(f"stage_rows runs: {pattern}, {entry}")
     pool = LY.HostPool(NL, E, rec, NL * E)
     g = np.random.default_rng(17)
     pool.records.copy_(torch.from_numpy(g.integers(0, 256, NL * E * rec, dtype=np.uint8)))
@@ -114,7 +116,8 @@ def test_stage_rows_copies_every_run_across_launches(pattern):
     arr = (L.Run * len(runs))(*[L.Run(*r) for r in runs])
     dst = torch.full((E * rec,), 0xA5, dtype=torch.uint8, device="cuda")
     s = torch.cuda.current_stream().cuda_stream
-    L.stage_rows_async(pool.desc, arr, len(runs), layer, dst, s, None, None)
+    stage = L.stage_rows_async if entry == "kernel" else L.stage_rows_dma_async
+    stage(pool.desc, arr, len(runs), layer, dst, s, None, None)
     torch.cuda.synchronize()
     got = dst.cpu().view(E, rec)
     staged = np.zeros(E, bool)
