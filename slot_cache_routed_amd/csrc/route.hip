@@ -8,6 +8,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace scr {
 
 // float -> u32 with the same order (non-NaN inputs; -0 is first made +0, so
@@ -23,9 +25,11 @@ __device__ __forceinline__ float key_value(unsigned k) {
 // Lane l holds logits l, l+64, l+128, ... (VPL of them, E <= 64*VPL) as
 // ordered keys (every finite or infinite key is above 0, the "taken" mark).
 // Each of the k rounds takes every lane's best untaken key (lowest id on
-// ties), the wave's largest key, then among the lanes holding it the lowest
-// id, both as DPP reductions; the owning lane marks it taken.  Lane j keeps
-// the j-th selection.
+// ties: a tree of maxima, then the lowest slot holding the maximum), the
+// wave's largest key by a DPP reduction, then the lowest id among the lanes
+// holding it: a ballot of those lanes, and when there is more than one (equal
+// logits), a second reduction.  The owning lane marks the key taken.  Lane j
+// keeps the j-th selection.
 template <int VPL>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T, int E,
                                                     int k, int32_t* __restrict__ ids,
@@ -43,16 +47,28 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   unsigned my_key = 0u;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    unsigned lk = 0u;
-    unsigned li = 0xffffffffu;
+    unsigned bk[VPL];  // tree of maxima over the slots
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const bool better = key[i] > lk;  // strict: the lower id stays on ties
-      li = better ? (unsigned)(lane + kWave * i) : li;
-      lk = better ? key[i] : lk;
-    }
+    for (int i = 0; i < VPL; ++i) bk[i] = key[i];
+#pragma unroll
+    for (int st = 1; st < VPL; st *= 2)
+#pragma unroll
+      for (int m = 0; m + st < VPL; m += 2 * st) bk[m] = bk[m] > bk[m + st] ? bk[m] : bk[m + st];
+    const unsigned lk = bk[0];
+    // the lowest slot holding it (the lowest id of the lane)
+    typedef typename std::conditional<(VPL > 32), unsigned long long, unsigned>::type SlotMask;
+    SlotMask held = 0;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) held |= key[i] == lk ? (SlotMask)1 << i : (SlotMask)0;
+    const int slot = VPL > 32 ? __builtin_ctzll((unsigned long long)held) : __builtin_ctz((unsigned)held);
+    const unsigned li = lk ? (unsigned)lane + (unsigned)kWave * (unsigned)slot : 0xffffffffu;
     const unsigned gk = __reduce_max_sync(~0ull, lk);
-    const unsigned gi = __reduce_min_sync(~0ull, lk == gk ? li : 0xffffffffu);
+    const uint64_t holders = __ballot(lk == gk);
+    unsigned gi;
+    if (__popcll(holders) == 1)
+      gi = (unsigned)__builtin_amdgcn_readlane((int)li, __builtin_ctzll(holders));
+    else
+      gi = __reduce_min_sync(~0ull, lk == gk ? li : 0xffffffffu);
     if ((int)(gi & (kWave - 1)) == lane) {
 #pragma unroll
       for (int i = 0; i < VPL; ++i)
