@@ -246,3 +246,37 @@ def test_batched_admission_supersedes_re_evicted_entries():
     for sl in range(S):
         key = int(snap["slot_key"][sl])
         assert torch.equal(bank.slot_record(sl).cpu(), pool.key_record(key))
+
+
+def test_batched_admission_on_a_bank_past_the_prefetch_size():
+    """The batched planner reads every query entry's slot up front only for
+    banks of at most 65536 slots; a bank of 70000 slots takes the per-query
+    lookups.  Three chunks (300 distinct experts in queries of 128, then
+    overlapping ones) against the oracle, bank state bit-exact after each."""
+    import slot_cache_routed_amd._lib as L
+    S, NL, E = 70000, 2, 512
+    bank = _bank(S, NL, E)
+    st = SlotBankState(S, NL, E)
+    g = np.random.default_rng(70000)
+    s = _stream()
+    for chunk in range(3):
+        layer = chunk % NL
+        distinct = np.sort(g.choice(E, size=300, replace=False)).astype(np.int32)
+        flush(f"batched past prefetch: chunk {chunk}, layer {layer}")
+        d = torch.from_numpy(distinct).cuda()
+        ms = torch.full((300,), -9, dtype=torch.int32, device="cuda")
+        mk = torch.full((300,), -9, dtype=torch.int32, device="cuda")
+        nm = torch.zeros(3, dtype=torch.int32, device="cuda")
+        nt = torch.zeros(1, dtype=torch.int32, device="cuda")
+        L.ensure_slots_batched(bank.desc, layer, d, 300, 128, 1, ms, mk, nm, nt, s)
+        torch.cuda.synchronize()
+        splits, slots, keys = [], [], []
+        for q0 in range(0, 300, 128):
+            rs, rk = ensure_slots(st, layer, distinct[q0:q0 + 128], True)
+            splits.append(len(rs))
+            slots += rs
+            keys += rk
+        assert nm.cpu().numpy().tolist() == splits
+        n = int(nt.item())
+        assert ms.cpu().numpy()[:n].tolist() == slots and mk.cpu().numpy()[:n].tolist() == keys
+        _same_state(bank, st, f"chunk {chunk}")
