@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import workloads as W
-from helpers import ExpertSource, fill_pool
+from helpers import ExpertSource, fill_pool, flush
 
 pytestmark = pytest.mark.gpu
 
@@ -116,3 +116,82 @@ def test_captured_decode_step_of_all_layers_replays_bitwise(fused):
         assert np.array_equal(np.asarray(se[key]), np.asarray(sg[key])), key
     hits, misses, evictions, queries = [int(v) for v in sg["stats"]]
     assert evictions > 0 and hits > 0 and queries == steps * NL * step.bufs[0].n_queries
+
+
+def test_short_prefill_96_step_as_the_bench_times_it():
+    """The 96-token chunk over the 1100-slot bank exactly as the benchmark runs
+    it: route, the one-launch planner, the miss copy, the grouped GEMMs and a
+    bf16 combine, then the warm step captured once and replayed.  The cold step
+    admits 128 + 32 experts and matches the oracle; every replay equals the
+    eager warm step and the whole-layer stream bit for bit."""
+    import slot_cache_routed_amd._lib as L
+    import slot_cache_routed_amd.layer as LY
+    from oracle import moe_layer, route_topk_softmax
+    from oracle.mlp import bf16_bits_to_f64
+    from helpers import rel_max_err
+    cfg = W.C2
+    T, E, k, H, I, S, NL, Wd = cfg.T, cfg.shape.E, cfg.shape.k, cfg.shape.H, cfg.shape.I, cfg.S, cfg.L, cfg.W
+    lay = LY.record_layout(L.SCR_W_BF16, H, I)
+    src = ExpertSource(cfg.seed, H, I, "bf16")
+    pool = LY.HostPool(NL, E, lay.record_bytes, E, payload_of=lambda key: key % E)
+    fill_pool(pool, src, lay, range(E))
+    lg, _ = W.logits_with_chosen(cfg.seed, T, E, k, 160)
+    xb = W.f32_to_bf16_bits(W.activations_normal(cfg.seed, T, H))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    logits, x, sc = dev(lg), dev(xb.view(np.int16)), dev(np.ones(E, np.float32))
+    bank = LY.Bank(S, NL, E, L.SCR_W_BF16, lay.record_bytes)
+    bank.load_fill(W.bank_prefilled(cfg.seed, S, NL, E, 600, exclude_layer=0))
+    buf = LY.LayerBuffers(T, E, k, H, I, S, L.SCR_W_BF16, width=Wd, y_dtype=L.SCR_Y_BF16)
+    view = LY.make_view(0, E, k, H, I, L.SCR_W_BF16, S, bank.row_table, sc)
+
+    def step(s):
+        L.route(logits, T, E, k, buf["topk_ids"], buf["topk_w"], s)
+        assert L.plan_chunk(bank.desc, 0, buf["topk_ids"], buf.R, buf["distinct"], buf["n_distinct"], Wd, False,
+                            buf["miss_slot"], buf["miss_key"], buf["n_miss"], buf["n_total"], buf.cfg.block_m,
+                            buf["sorted_routes"], buf["block_bucket"], buf["n_post_pad"], buf["active_buckets"],
+                            buf["active_block_begin"], buf["n_active"], s)
+        L.copy_misses(bank.desc, pool.desc, buf["miss_slot"], buf["miss_key"], buf["n_total"], buf.lmax, s)
+        LY.forward(buf, view, x, stream=torch.cuda.current_stream())
+
+    flush("96-token step: cold")
+    step(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert buf["n_miss"].cpu().numpy().tolist() == [128, 32, 0, 0]
+    y_cold = buf["y"].clone()
+    # the same plan through the fp32-output mode: within the bf16 tolerance of
+    # the oracle, and the benchmarked bf16 output is exactly its rounding
+    buf32 = LY.LayerBuffers(T, E, k, H, I, S, L.SCR_W_BF16, width=Wd, y_dtype=L.SCR_Y_F32)
+    for key in ("topk_w", "sorted_routes", "active_buckets", "active_block_begin", "n_active"):
+        buf32[key].copy_(buf[key])
+    LY.forward(buf32, view, x)
+    torch.cuda.synchronize()
+    y32 = buf32["y"].clone()
+    assert torch.equal(y_cold, y32.to(torch.bfloat16))
+    ids, w = route_topk_softmax(lg, k)
+    y_ref = moe_layer(bf16_bits_to_f64(xb), ids, w, src.f64)
+    err = rel_max_err(y32.cpu().numpy(), y_ref)
+    flush(f"96-token step: rel max err {err:.3e} (fp32 output of the same plan)")
+    assert err <= 2e-2
+    flush("96-token step: warm, eager then captured")
+    step(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    y_warm = buf["y"].clone()
+    assert torch.equal(y_warm, y_cold) and buf["n_miss"].cpu().numpy().sum() == 0
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            step(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        buf["y"].zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(buf["y"], y_warm)
+        _ = (x.float() * 2).sum().item()      # eager work between replays
+    lb = LY.LayerStreamBuffer(E, lay.record_bytes)
+    st = LY.stream_layer(pool, 0, logits, x, sc, lb, L.SCR_W_BF16, y_dtype=L.SCR_Y_BF16, shape=(k, H, I))
+    torch.cuda.synchronize()
+    assert torch.equal(st["y"], y_warm), "slot path equals the whole-layer path bit for bit"
