@@ -1067,7 +1067,7 @@ __device__ __forceinline__ void load_row8(const bf16* p, float* v) {
   }
 }
 
-template <typename OT, bool BF16_OUT>
+template <typename OT, bool BF16_OUT, int G>
 __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ o,
                                                       const int32_t* __restrict__ flags, int T, int k,
                                                       int H, void* __restrict__ y) {
@@ -1077,21 +1077,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ o,
        i += (size_t)gridDim.x * blockDim.x) {
     const int t = (int)(i / h8), c8 = (int)(i % h8);
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // ranks in groups of four: every flag and row of a group is loaded
-    // unconditionally (clamped to the last rank), so the loads overlap; an
-    // unwritten route leaves the sum untouched (a select, not a branch)
-    for (int j0 = 0; j0 < k; j0 += 4) {
-      int fl[4];
-      float v[4][8];
+    // ranks in groups of G (G >= k up to 16: one round of loads): every flag
+    // and row of a group is loaded unconditionally (clamped to the last rank),
+    // so the loads overlap; an unwritten route leaves the sum untouched (a
+    // select, not a branch)
+    for (int j0 = 0; j0 < k; j0 += G) {
+      int fl[G];
+      float v[G][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < G; ++u) {
         const int r = t * k + min(j0 + u, k - 1);
         const int f = flags[r];
         fl[u] = j0 + u < k ? f : 0;
         load_row8(o + (size_t)r * H + 8 * c8, v[u]);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < G; ++u)
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = fl[u] ? acc[q] + v[u][q] : acc[q];
     }
@@ -1595,6 +1596,27 @@ static int run_gemms(const scr_tile_cfg& cfg, const GemmArgs& a, int max_active,
   return launch_gemms<WDT, 7, 2>(a, max_active, marks, s);
 }
 
+// the combine, its rank group the smallest of 4, 8, 12, 16 that holds k
+template <typename OT>
+static void launch_combine(const OT* o, const int32_t* flags, int T, int k, int H, void* y, bool bf16_out,
+                           int grid, hipStream_t s) {
+#define SCR_COMBINE(G)                                                                                       \
+  if (bf16_out)                                                                                              \
+    hipLaunchKernelGGL((combine_kernel<OT, true, G>), dim3(grid), dim3(256), 0, s, o, flags, T, k, H, y);   \
+  else                                                                                                       \
+    hipLaunchKernelGGL((combine_kernel<OT, false, G>), dim3(grid), dim3(256), 0, s, o, flags, T, k, H, y);
+  if (k <= 4) {
+    SCR_COMBINE(4)
+  } else if (k <= 8) {
+    SCR_COMBINE(8)
+  } else if (k <= 12) {
+    SCR_COMBINE(12)
+  } else {
+    SCR_COMBINE(16)
+  }
+#undef SCR_COMBINE
+}
+
 }  // namespace scr
 
 extern "C" int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_cfg* cfg) {
@@ -1716,19 +1738,10 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   const size_t total = (size_t)T * (H / 8);
   int cgrid = (int)((total + 255) / 256);
   if (cgrid > 4096) cgrid = 4096;
-  if (view->wdtype != SCR_W_BF16) {
-    const scr::bf16* o = static_cast<const scr::bf16*>(a.o);
-    if (y_dtype == SCR_Y_BF16)
-      hipLaunchKernelGGL((scr::combine_kernel<scr::bf16, true>), dim3(cgrid), dim3(256), 0, stream, o, a.flags, T, k, H, y);
-    else
-      hipLaunchKernelGGL((scr::combine_kernel<scr::bf16, false>), dim3(cgrid), dim3(256), 0, stream, o, a.flags, T, k, H, y);
-  } else {
-    const float* o = static_cast<const float*>(a.o);
-    if (y_dtype == SCR_Y_BF16)
-      hipLaunchKernelGGL((scr::combine_kernel<float, true>), dim3(cgrid), dim3(256), 0, stream, o, a.flags, T, k, H, y);
-    else
-      hipLaunchKernelGGL((scr::combine_kernel<float, false>), dim3(cgrid), dim3(256), 0, stream, o, a.flags, T, k, H, y);
-  }
+  if (view->wdtype != SCR_W_BF16)
+    scr::launch_combine(static_cast<const scr::bf16*>(a.o), a.flags, T, k, H, y, y_dtype == SCR_Y_BF16, cgrid, stream);
+  else
+    scr::launch_combine(static_cast<const float*>(a.o), a.flags, T, k, H, y, y_dtype == SCR_Y_BF16, cgrid, stream);
   SCR_CHECK_LAUNCH();
   if (marks && marks[4]) SCR_CHECK_HIP(hipEventRecord(marks[4], stream));
   return SCR_OK;
