@@ -369,14 +369,15 @@ def test_nvfp4_wide_gate_up_rows_of_every_magnitude(H):
     assert torch.equal(d["y"], st["y"])
 
 
-@pytest.mark.parametrize("wd", ["nvfp4", "fp8", "mxfp4", "mxfp4_a8"])
-def test_full_size_4096_token_layer_in_every_narrow_format(wd):
+@pytest.mark.parametrize("wd", ["bf16", "nvfp4", "fp8", "mxfp4", "mxfp4_a8"])
+def test_full_size_4096_token_layer_in_every_weight_format(wd):
     """The benchmark's 4096-token layer (512 experts, top-10, hidden 2048,
-    intermediate 512) in each narrow weight format through the demand path
+    intermediate 512) in each weight format through the demand path
     (every expert admitted into a 512-slot bank, 40,960 routes aligned by the
     multi-workgroup align, the wide GEMM kernels): bit-identical to the
     whole-layer stream path, and for the W4A16 formats sampled tokens within
-    the FP4 tolerance of the oracle.  Records alias 64 generated payloads."""
+    the oracle's tolerance (bf16 2e-2, the 4-bit and 8-bit formats 5e-2).
+    Records alias 64 generated payloads."""
     import slot_cache_routed_amd.layer as LY
     T, E, k, H, I, P, seed = 4096, 512, 10, 2048, 512, 64, 5
     code = wdtype_code(wd)
@@ -404,7 +405,7 @@ def test_full_size_4096_token_layer_in_every_narrow_format(wd):
     y_ref = moe_layer_tokens(bf16_bits_to_f64(xb), ids, w, lambda e: src.f64(e % P), toks)
     err = rel_max_err(_y(d)[toks], y_ref)
     flush(f"full-size layer {wd}: sampled rel max err = {err:.3e}")
-    assert err <= TOL_FP4
+    assert err <= (TOL_BF16 if wd == "bf16" else TOL_FP4)
     del bank, lb, pool
     torch.cuda.empty_cache()
 
