@@ -138,3 +138,39 @@ def test_lrfu_capacity_overflow_within_a_pinned_chunk():
         assert np.array_equal(np.asarray(snap[key]), np.asarray(_state(st)[key])), key
     assert snap["err"] == st.err == 1
     assert sorted(int(k) for k in snap["slot_key"]) == list(range(3, 13))   # the first ten admissions stay
+
+
+def test_lrfu_decode_stream_at_full_planner_scale():
+    """The decode stream's planner scale (48 layers x 512 experts, a 1650-slot
+    bank, 4-token steps, top-10 Zipf(1.1) routing) under LRFU with a half-life
+    of 16 queries: the bank state, every slot's value included, bit-exact
+    against the oracle after every layer-step of 4 steps.  Records are small
+    (hidden 128, intermediate 128): the GEMM sizes do not enter the planner."""
+    cfg = W.C4
+    E, k, S, NL, T = cfg.shape.E, cfg.shape.k, cfg.S, cfg.L, cfg.T
+    H = I = 128
+    L, LY, lay, pool = _setup(T=T, E=E, k=k, H=H, I=I, NL=NL, seed=cfg.seed)
+    D = _decay(16)
+    bank = LY.Bank(S, NL, E, L.SCR_W_BF16, lay.record_bytes, policy=L.SCR_POLICY_LRFU, lrfu_decay=D)
+    st = SlotBankState(S, NL, E)
+    st.policy, st.decay_q32 = POLICY_LRFU, D
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    sc = dev(np.ones(E, np.float32))
+    buf = LY.LayerBuffers(T, E, k, H, I, S, L.SCR_W_BF16, width=128)
+    for step in range(4):
+        flush(f"LRFU decode at full planner scale: step {step}")
+        for layer in range(NL):
+            lg = W.zipf_gumbel_logits(cfg.seed, layer, step, T, E)
+            xb = W.f32_to_bf16_bits(W.decode_activations(cfg.seed, layer, step, T, H))
+            LY.demand_layer(bank, pool, layer, dev(lg), dev(xb.view(np.int16)), sc, width=128, record_stats=True,
+                            buf=buf, shape=(k, H, I))
+            ids, _ = route_topk_softmax(lg, k)
+            distinct, _, _ = dedup_sorted(ids.reshape(-1), E)
+            ensure_slots(st, layer, distinct, True)
+            torch.cuda.synchronize()
+            snap = bank.snapshot()
+            for key in STATE:
+                assert np.array_equal(np.asarray(snap[key]), np.asarray(_state(st)[key])), (step, layer, key)
+    hits, misses, evictions, queries = [int(v) for v in bank.snapshot()["stats"]]
+    flush(f"LRFU decode at full planner scale: hits {hits} misses {misses} evictions {evictions}")
+    assert queries == 4 * NL and evictions > 0
