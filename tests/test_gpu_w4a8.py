@@ -21,7 +21,7 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 256), (128, 2048)])
+@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 256), (128, 2048), (4096, 2048)])
 def test_quantize_mxfp8_is_bit_exact(rows, cols):
     import slot_cache_routed_amd._lib as L
     g = np.random.default_rng(rows * 7 + cols)
