@@ -98,3 +98,21 @@ def test_route_signed_zeros_tie_and_minus_infinity():
     assert np.array_equal(ids, rid)
     assert ids[0].tolist() == [7, 0, 1, 3, 6]
     assert np.array_equal(w.view(np.int32), rw.view(np.int32))
+
+
+@pytest.mark.parametrize("E,k", [(512, 10), (4096, 32), (100, 7)])
+def test_route_with_many_equal_logits(E, k):
+    # logits from three values: equal keys within one lane's slots and across
+    # lanes in every round; rows of one value throughout choose ids 0..k-1
+    g = np.random.default_rng(E + k)
+    lg = g.integers(0, 3, size=(64, E)).astype(np.float32)
+    lg[5] = 1.0
+    lg[9] = -2.5
+    lg[11, : E // 2] = 0.0
+    lg[11, E // 2:] = 0.0 * -1.0
+    ids, w = _route_gpu(lg, k)
+    rid, rw = route_topk_softmax(lg, k)
+    assert np.array_equal(ids, rid)
+    assert ids[5].tolist() == list(range(k)) and ids[9].tolist() == list(range(k))
+    diff = np.abs(w.view(np.int32).astype(np.int64) - rw.view(np.int32).astype(np.int64))
+    assert diff.max() <= 1
