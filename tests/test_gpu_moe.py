@@ -410,6 +410,23 @@ def test_full_size_4096_token_layer_in_every_weight_format(wd):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("k", [24, 32])
+def test_top_k_past_sixteen(k):
+    """k above 16: the combine sums a token's ranks in groups of 16 (the second
+    group partly clamped), still in rank order; against the oracle and the
+    stream path."""
+    s = _setup(f"topk_{k}", S=96, W_=32, wdtype="bf16", T=40, E=48, k=k, H=256, I=128, NL=2)
+    bank = _bank_for(s)
+    sc = np.ones(s["E"], np.float32)
+    d = _run_demand(s, bank, sc)
+    y_ref, _, _ = _oracle(s)
+    err = rel_max_err(_y(d), y_ref)
+    flush(f"top-{k}: rel max err = {err:.3e}")
+    assert err <= TOL_BF16
+    st = _run_stream(s, sc)
+    assert torch.equal(d["y"], st["y"])
+
+
 def test_forward_with_no_tokens_launches_nothing():
     import slot_cache_routed_amd.layer as LY
     import slot_cache_routed_amd._lib as L
