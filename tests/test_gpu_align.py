@@ -122,3 +122,37 @@ def test_align_one_workgroup_table_and_walk_scatters(n, Nb, B):
     flush(f"align small n={n} Nb={Nb} B={B}")
     ids = W.uniform_ids(21, n, Nb + Nb // 10).copy()
     _compare(_align_gpu(ids, None, Nb, B), align_blocks(ids, None, Nb, B))
+
+
+@pytest.mark.parametrize("n,Nb,B", [(4 << 20, 2100, 16), (1 << 22, 512, 64)])
+def test_align_at_millions_of_routes_by_its_defining_properties(n, Nb, B):
+    """Millions of routes (chunks lengthened by the count-matrix budget): the
+    output is checked through the properties that fix it uniquely, since the
+    oracle's per-route loop is too slow at this size: every valid route once,
+    in the block range of its own bucket, ascending within the bucket, the
+    rest of each bucket's blocks padding, buckets in ascending order."""
+    flush(f"align properties n={n} Nb={Nb} B={B}")
+    ids = W.uniform_ids(17, n, Nb + Nb // 16)          # some ids past the buckets
+    got = _align_gpu(ids, None, Nb, B)
+    valid = ids < Nb
+    cnt = np.bincount(ids[valid], minlength=Nb)
+    blocks = -(-cnt // B)
+    act = np.nonzero(cnt)[0]
+    assert got["n_active"] == act.size and np.array_equal(got["active_buckets"], act)
+    begin = np.concatenate([[0], np.cumsum(blocks[act])])
+    assert np.array_equal(got["active_block_begin"], begin)
+    assert got["n_post_pad"] == B * int(begin[-1])
+    nb_used = int(begin[-1])
+    bb = got["block_bucket"][:nb_used]
+    assert np.array_equal(bb, np.repeat(act, blocks[act]))
+    sr = got["sorted_routes"][:B * nb_used]
+    real = sr != n
+    assert np.all((sr[real] >= 0) & (sr[real] < n))
+    slot_bucket = np.repeat(bb, B)
+    assert np.array_equal(ids[sr[real]], slot_bucket[real])                       # each in its own bucket
+    assert np.array_equal(np.sort(sr[real]), np.nonzero(valid)[0])                # every valid route once
+    # ascending within a bucket, and the real routes come first in its blocks
+    same = slot_bucket[1:] == slot_bucket[:-1]
+    assert np.all(sr[1:][same & real[1:] & real[:-1]] > sr[:-1][same & real[1:] & real[:-1]])
+    assert not np.any(same & real[1:] & ~real[:-1])
+    assert np.array_equal(np.bincount(slot_bucket[real], minlength=Nb), cnt)
