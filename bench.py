@@ -618,7 +618,8 @@ def align_bench() -> dict:
                            ("decode_step", 40, 1650, 16), ("uniform_1023", 960, 1023, 16),
                            ("uniform_2100", 960, 2100, 16), ("uniform_1023_block64", 960, 1023, 64),
                            ("uniform_2100_40960_block64", 40960, 2100, 64),
-                           ("bandwidth_655360x2100", 655360, 2100, 16)):
+                           ("bandwidth_655360x2100", 655360, 2100, 16),
+                           ("bandwidth_4194304x2100", 4194304, 2100, 16)):
         ids = torch.from_numpy(W.uniform_ids(4, n, nb)).cuda()
         cap = L.align_capacity(n, nb, B)
         m = min(n, nb)
