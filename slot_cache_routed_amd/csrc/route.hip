@@ -38,12 +38,17 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
   const float* row = logits + (size_t)t * E;
+  // every load is issued (lanes past E read the last logit and drop it), so
+  // that all VPL of them are in flight together
   unsigned key[VPL];
+  float v[VPL];
 #pragma unroll
   for (int i = 0; i < VPL; ++i) {
     const int e = lane + kWave * i;
-    key[i] = e < E ? ordered_key(row[e]) : 0u;
+    v[i] = row[e < E ? e : E - 1];
   }
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) key[i] = lane + kWave * i < E ? ordered_key(v[i]) : 0u;
   unsigned my_key = 0u;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
