@@ -402,9 +402,9 @@ int scr_quantize_mxfp8(const void* x, long long rows, int cols, uint8_t* codes, 
  * device-mapped view; about 57 GB/s over PCIe 5 against about 50 for DMA). */
 int scr_stream_layer_async(const scr_host_pool* pool, int layer, void* dst, hipStream_t stream);
 
-/* stage_plan [P4 Prefill staging: the placement tables only change in decode,
- * so at the first layer of a prefill step every layer's non-resident map is
- * read back once and turned into contiguous runs].  Reads key_to_slot of
+/* stage_plan [P4 Details, prefill staging: residency changes only during
+ * decode, so one read-back at the start of a prefill step serves all of its
+ * layers; absent experts are grouped into contiguous runs].  Reads key_to_slot of
  * layers [layer_begin, layer_begin + n_layers) into host_map (host i32
  * [n_layers * E]), synchronising `stream` (the step's one host sync), and
  * writes the runs of non-resident experts whose host records are adjacent
@@ -448,6 +448,19 @@ int scr_fill_staged_rows(const scr_bank_desc* bank, int layer, const void* stagi
 /* rebuilds key_to_slot from slot_key (all keys -1, then one entry per used
  * slot); use after writing an initial slot_key/slot_stamp/clock. */
 int scr_bank_rebuild_map(const scr_bank_desc* bank, hipStream_t stream);
+/* bank_init [P3 What: one bank of (layer, expert) keys shared by every layer;
+ * P1 Tests: the layer-view test starts from a bank that decode already filled
+ * with other layers' experts].  Sets the bank's replacement state from host
+ * arrays: slot_key <- host_slot_keys [S] (-1 = empty, else a key in [0, L*E)
+ * held by no other slot), slot_stamp <- host_stamps [S] (none above clock; 0
+ * for an empty slot), the clock <- clock; clears stats, decode_freq, err and,
+ * when present, slot_crf and chunk_start; rebuilds key_to_slot.  Slot records
+ * (rows) are left as they are.  An initialisation helper: the copies are
+ * enqueued on `stream`, which is synchronised before the call returns, so
+ * the host arrays may be freed at once.  A state that breaks the rules above
+ * returns SCR_EINVAL with nothing enqueued. */
+int scr_bank_init(const scr_bank_desc* bank, const int32_t* host_slot_keys, const uint64_t* host_stamps,
+                  uint64_t clock, hipStream_t stream);
 /* device-accessible alias of a pinned host address */
 int scr_host_device_alias(const void* host_ptr, void** dev_ptr);
 

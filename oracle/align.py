@@ -1,9 +1,10 @@
 """Align routes into fixed-size per-bucket blocks (oracle).
 
-Sources: FreeToken PR #676, "Solution" (a demand chunk aligns against the
-slot count, so the align must work past 1023 buckets) and "Tests" (at 1023
-and 2100 experts every route lands once, in a block of its expert);
-gdevenyi's comment there (the no-limit align is valid at 2100 and 4096);
+Sources: FreeToken PR #676, "Solution" (a demand chunk is aligned over the
+bank's slots, so bucket counts beyond 1023 must work) and "Tests" (the align
+test places each route exactly one time, inside a block owned by the route's
+expert, for 1023 and for 2100 experts); gdevenyi's comment there (an align
+without the one-block limit checked at 2100 and 4096 buckets);
 vLLM fork PR #48, "What" (align over logical experts ignoring invalid
 ones, then remap to physical rows).
 

@@ -1,9 +1,10 @@
 """Distinct-expert list (oracle).
 
-Source: FreeToken PR #676, "Solution" (the chunk's distinct experts are a
-sorted list of fixed length, so no host sync is needed) and gdevenyi's comment
-there (hand the LRU the unique ids, mapping each route back through the
-inverse of the unique).
+Source: FreeToken PR #676, "Solution" (the LRU receives the chunk's distinct
+experts as an ordered list whose length the host knows in advance, which is
+what spares a host synchronisation) and gdevenyi's comment there (the LRU
+gets unique ids only; routes find their entry again through the inverse
+index of the unique operation).
 
 Reading taken: the fixed length is min(n, E) (the largest possible distinct
 count, known to the host); unused tail entries hold the sentinel E; ids

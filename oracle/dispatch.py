@@ -3,8 +3,8 @@
 Sources: FreeToken PR #676, "Solution" and "Tests": a threshold N of 0 takes
 no chunk on demand; otherwise a chunk of at most N tokens takes the demand
 path (96 tokens do at N = 96, 97 tokens stream; N = 2 takes 1 and 2 tokens).
-Same page, author's reply: a layer never routes to more experts than the
-cache holds.  gdevenyi's PR #68, second commit: a layer needing more than
+Same page, author's reply: the expert set of one layer always fits in the
+cache (the capacity guard below).  gdevenyi's PR #68, second commit: a layer needing more than
 half the cache takes the whole-layer path.
 
 Parity: pinned (the page-printed threshold cases).

@@ -1,14 +1,16 @@
 """LRU slot bank keyed by (layer, expert) (oracle).
 
 Sources:
-  * FreeToken PR #676, "Problem" and "Solution": decode loads only the
-    experts its tokens route to through the slot cache; a prefill chunk hands
-    the LRU its distinct experts one fixed-width query at a time, copies each
-    query's misses before the next query runs, and keeps these admissions out
-    of the decode frequency and the LRU statistics.
-  * Same page, author's reply: the cache is LRU-only, earlier queries need no
-    pin because LRU evicts them last, and a layer never routes to more experts
-    than the cache holds.
+  * FreeToken PR #676, "Problem" and "Solution": in decode, only routed
+    experts are brought in through the slot cache; a short prefill chunk
+    feeds its distinct experts to the LRU in slices of fixed width, moves
+    every slice's misses in before the following slice is queried, and
+    records none of these admissions in the decode counters or the LRU
+    statistics.
+  * Same page, author's reply: eviction there is plain LRU, which never
+    picks a slice admitted earlier in the chunk while older slots remain,
+    so no pinning is needed; one layer's expert set always fits in the
+    cache.
   * vLLM fork PR #48, "What": one bank shared by all MoE layers, keyed
     (layer, expert), planned by an LRU over the bank.
 

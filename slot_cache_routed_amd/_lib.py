@@ -32,6 +32,7 @@ EXPORTS = (
     "scr_moe_workspace", "scr_grouped_moe_forward", "scr_quantize_mxfp8", "scr_stream_layer_async",
     "scr_stage_plan",
     "scr_stage_rows_async", "scr_stage_rows_dma_async", "scr_fill_row_table", "scr_fill_staged_rows", "scr_bank_rebuild_map",
+    "scr_bank_init",
     "scr_host_device_alias", "scr_prefill_on_demand", "scr_demand_capacity_ok", "scr_timer_create",
     "scr_timer_record", "scr_timer_elapsed_ms", "scr_timer_destroy", "scr_last_error", "scr_version",
 )
@@ -110,6 +111,7 @@ _SIGS = {
     "scr_fill_row_table": (_I, [_P, _I, C.c_uint64, _P, _P]),
     "scr_fill_staged_rows": (_I, [C.POINTER(BankDesc), _I, _P, _P, _P]),
     "scr_bank_rebuild_map": (_I, [C.POINTER(BankDesc), _P]),
+    "scr_bank_init": (_I, [C.POINTER(BankDesc), _P, _P, C.c_uint64, _P]),
     "scr_host_device_alias": (_I, [_P, C.POINTER(_P)]),
     "scr_prefill_on_demand": (_I, [_I, _I]),
     "scr_demand_capacity_ok": (_I, [_I, _I, _I, _I, _I]),
@@ -282,6 +284,14 @@ def fill_staged_rows(bank: BankDesc, layer, staging, bucket_rows, stream):
 
 def bank_rebuild_map(bank: BankDesc, stream):
     _check("scr_bank_rebuild_map", load().scr_bank_rebuild_map(C.byref(bank), stream))
+
+
+def bank_init(bank: BankDesc, slot_keys, stamps, clock: int, stream):
+    """slot_keys: host int32 [S], stamps: host uint64 [S] (numpy, C-contiguous)."""
+    import numpy as np
+    sk = np.ascontiguousarray(slot_keys, dtype=np.int32)
+    st = np.ascontiguousarray(stamps, dtype=np.uint64)
+    _check("scr_bank_init", load().scr_bank_init(C.byref(bank), sk.ctypes.data, st.ctypes.data, int(clock), stream))
 
 
 def host_device_alias(host_ptr: int) -> int:

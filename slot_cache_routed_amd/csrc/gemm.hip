@@ -1628,11 +1628,10 @@ extern "C" int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_c
   // rows per expert of the routed layer (never of the bank)
   const long long per_expert = ((long long)T * k + E_layer - 1) / E_layer;
   cfg->block_m = 16;
-  // few rows per expert: small M passes and narrow N tiles (more workgroups to
-  // stream weights); many rows: 128-row passes and wide N tiles (MFMA reuse)
+  // few rows per expert: 32-row passes and narrow N tiles (more workgroups to
+  // stream weights); many rows: 112-row passes (seven 16-row tiles, every
+  // weight format) and wide N tiles (MFMA reuse)
   const bool small = per_expert <= 16;
-  // NVFP4 passes hold 96 rows (the deeper weight ring of its wide kernel
-  // takes the registers of a seventh row tile), bf16 passes 112
   cfg->m_chunk = small ? 32 : 112;
   cfg->n_tile_gu = 4 * 8 * 2;    // h columns per workgroup
   cfg->n_tile_dn = 4 * 16 * 2;   // output columns per workgroup

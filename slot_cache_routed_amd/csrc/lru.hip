@@ -12,6 +12,8 @@
 // integer definition.
 #include "small_blocks.h"
 
+#include <vector>
+
 namespace scr {
 
 constexpr int kLruThreads = kPlanThreads;
@@ -502,5 +504,44 @@ extern "C" int scr_bank_rebuild_map(const scr_bank_desc* bank, hipStream_t strea
   hipLaunchKernelGGL(scr::rebuild_map_fill, dim3((bank->S + 255) / 256), dim3(256), 0, stream,
                      bank->slot_key, bank->S, n_keys, bank->key_to_slot);
   SCR_CHECK_LAUNCH();
+  return SCR_OK;
+}
+
+extern "C" int scr_bank_init(const scr_bank_desc* bank, const int32_t* host_slot_keys, const uint64_t* host_stamps,
+                             uint64_t clock, hipStream_t stream) {
+  int rc = scr::check_bank(bank);
+  if (rc) return rc;
+  SCR_CHECK_ARG(host_slot_keys && host_stamps, "bank_init: null host array");
+  const int S = bank->S;
+  const long long n_keys = (long long)bank->L * bank->E;
+  // the state must be one the planners can continue from: keys in range and
+  // each held by at most one slot, no stamp ahead of the clock, empty slots
+  // never stamped
+  std::vector<unsigned char> seen((size_t)n_keys, 0);
+  for (int s = 0; s < S; ++s) {
+    const int32_t key = host_slot_keys[s];
+    SCR_CHECK_ARG(key >= -1 && key < n_keys, "bank_init: slot %d holds key %d outside [-1, %lld)", s, key, n_keys);
+    SCR_CHECK_ARG(host_stamps[s] <= clock, "bank_init: slot %d is stamped after the clock", s);
+    if (key < 0) {
+      SCR_CHECK_ARG(host_stamps[s] == 0, "bank_init: empty slot %d has a non-zero stamp", s);
+      continue;
+    }
+    SCR_CHECK_ARG(!seen[key], "bank_init: key %d is held by more than one slot", key);
+    seen[key] = 1;
+  }
+  SCR_CHECK_HIP(hipMemcpyAsync(bank->slot_key, host_slot_keys, (size_t)S * sizeof(int32_t), hipMemcpyHostToDevice,
+                               stream));
+  SCR_CHECK_HIP(hipMemcpyAsync(bank->slot_stamp, host_stamps, (size_t)S * sizeof(uint64_t), hipMemcpyHostToDevice,
+                               stream));
+  SCR_CHECK_HIP(hipMemcpyAsync(bank->clock, &clock, sizeof(uint64_t), hipMemcpyHostToDevice, stream));
+  SCR_CHECK_HIP(hipMemsetAsync(bank->stats, 0, 4 * sizeof(uint64_t), stream));
+  SCR_CHECK_HIP(hipMemsetAsync(bank->decode_freq, 0, (size_t)n_keys * sizeof(uint32_t), stream));
+  SCR_CHECK_HIP(hipMemsetAsync(bank->err, 0, sizeof(uint32_t), stream));
+  if (bank->slot_crf) SCR_CHECK_HIP(hipMemsetAsync(bank->slot_crf, 0, (size_t)S * sizeof(uint32_t), stream));
+  if (bank->chunk_start) SCR_CHECK_HIP(hipMemsetAsync(bank->chunk_start, 0, sizeof(uint64_t), stream));
+  rc = scr_bank_rebuild_map(bank, stream);
+  if (rc) return rc;
+  // the host arrays (and `clock`, a local) are read by the copies above
+  SCR_CHECK_HIP(hipStreamSynchronize(stream));
   return SCR_OK;
 }

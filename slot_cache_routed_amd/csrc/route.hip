@@ -22,11 +22,34 @@ __device__ __forceinline__ float key_value(unsigned k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// One DPP move of x (lanes whose source lies outside the pattern, or whose
+// row is masked off, keep their own value, which max and min leave alone).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ unsigned dpp_mov(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+
+// Wave-wide max / min of an unsigned value by DPP: a shift-right ladder of
+// 1, 2, 4 and 8 lanes leaves each 16-lane row's result in its lane 15; a
+// broadcast of lane 15 into rows 1 and 3, then of lane 31 into rows 2 and 3,
+// folds the four rows into lane 63, which is read back to every lane.
+template <bool MAX>
+__device__ __forceinline__ unsigned wave_reduce_u32(unsigned x) {
+  auto op = [](unsigned a, unsigned b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  x = op(x, dpp_mov<0x111, 0xf>(x));  // row_shr:1
+  x = op(x, dpp_mov<0x112, 0xf>(x));  // row_shr:2
+  x = op(x, dpp_mov<0x114, 0xf>(x));  // row_shr:4
+  x = op(x, dpp_mov<0x118, 0xf>(x));  // row_shr:8
+  x = op(x, dpp_mov<0x142, 0xa>(x));  // row_bcast:15
+  x = op(x, dpp_mov<0x143, 0xc>(x));  // row_bcast:31
+  return (unsigned)__builtin_amdgcn_readlane((int)x, 63);
+}
+
 // Lane l holds logits l, l+64, l+128, ... (VPL of them, E <= 64*VPL) as
 // ordered keys (every finite or infinite key is above 0, the "taken" mark).
 // Each of the k rounds takes every lane's best untaken key (lowest id on
 // ties: a tree of maxima, then the lowest slot holding the maximum), the
-// wave's largest key by a DPP reduction, then the lowest id among the lanes
+// wave's largest key by a DPP reduction (wave_reduce_u32), then the lowest id among the lanes
 // holding it: a ballot of those lanes, and when there is more than one (equal
 // logits), a second reduction.  The owning lane marks the key taken.  Lane j
 // keeps the j-th selection.
@@ -67,13 +90,13 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     for (int i = 0; i < VPL; ++i) held |= key[i] == lk ? (SlotMask)1 << i : (SlotMask)0;
     const int slot = VPL > 32 ? __builtin_ctzll((unsigned long long)held) : __builtin_ctz((unsigned)held);
     const unsigned li = lk ? (unsigned)lane + (unsigned)kWave * (unsigned)slot : 0xffffffffu;
-    const unsigned gk = __reduce_max_sync(~0ull, lk);
+    const unsigned gk = wave_reduce_u32<true>(lk);
     const uint64_t holders = __ballot(lk == gk);
     unsigned gi;
     if (__popcll(holders) == 1)
       gi = (unsigned)__builtin_amdgcn_readlane((int)li, __builtin_ctzll(holders));
     else
-      gi = __reduce_min_sync(~0ull, lk == gk ? li : 0xffffffffu);
+      gi = wave_reduce_u32<false>(lk == gk ? li : 0xffffffffu);
     if ((int)(gi & (kWave - 1)) == lane) {
 #pragma unroll
       for (int i = 0; i < VPL; ++i)

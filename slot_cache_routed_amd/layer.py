@@ -151,16 +151,9 @@ class Bank:
         L.fill_row_table(self.rows, S, self.rec, self.row_table, _stream())
 
     def load_fill(self, fill, stream=None):
-        """Sets slot_key / slot_stamp / clock from a host BankFill and rebuilds key_to_slot."""
-        self.slot_key.copy_(torch.from_numpy(fill.slot_key.astype(np.int32)))
-        self.slot_stamp.copy_(torch.from_numpy(fill.slot_stamp.astype(np.int64)))
-        self.clock.fill_(int(fill.clock))
-        self.stats.zero_()
-        self.decode_freq.zero_()
-        self.err.zero_()
-        self.slot_crf.zero_()
-        self.chunk_start.zero_()
-        L.bank_rebuild_map(self.desc, _stream(stream))
+        """Sets slot_key / slot_stamp / clock from a host BankFill (scr_bank_init:
+        statistics cleared, key_to_slot rebuilt; synchronises the stream)."""
+        L.bank_init(self.desc, fill.slot_key, fill.slot_stamp, int(fill.clock), _stream(stream))
 
     def snapshot(self) -> dict:
         torch.cuda.synchronize()
@@ -414,9 +407,10 @@ def stream_layer(pool: HostPool, layer: int, logits, x, input_scale, layer_buf: 
 class StagedPrefill:
     """Prefill staging over consecutive layers.
 
-    Two device buffers, each the size of a whole layer, alternate by layer;
-    the non-resident map of every layer is read back once (scr_stage_plan,
-    the step's one host sync) and turned into runs; layer i+1's runs are
+    Layers take turns between a pair of device buffers that can each hold
+    one full layer (vLLM fork PR #51, Details: prefill staging).  One host
+    read-back per step (scr_stage_plan) fetches which experts of each layer
+    are absent from the bank and groups them into runs; layer i+1's runs are
     copied by a copy kernel on a side stream while layer i computes, ordered with events
     (the copy into a buffer waits for the layer that last read it).  Each
     layer then runs route, align over its experts and the grouped GEMM on a

@@ -66,7 +66,7 @@ def test_align_capacity_formula(lib):
     assert L.align_workspace(40960, 512) > 0
 
 
-@pytest.mark.parametrize("call", [
+BAD_CALLS = [
     lambda: L.route(0, 4, 8, 0, 0, 0, None),                 # k = 0
     lambda: L.route(0, 4, 8, 9, 0, 0, None),                 # k > E
     lambda: L.route(0, 4, 5000, 2, 0, 0, None),              # E too large
@@ -79,8 +79,11 @@ def test_align_capacity_formula(lib):
     lambda: L.align_blocks(1, 10, None, 0, 8, 16, 1, 1, 1, 1, 1, 1, 1, 4, None),         # tiny workspace
     lambda: L.tile_config(1, 0, 8, 0),
     lambda: L.tile_config(1, 1, 8, 7),
-    lambda: L.tile_config(1, 1, 8, 5),                        # no format 5
-])
+    lambda: L.tile_config(1, 1, 8, 9),                        # no format 9
+]
+
+
+@pytest.mark.parametrize("call", BAD_CALLS)
 def test_bad_arguments_are_rejected_before_any_launch(lib, call):
     with pytest.raises(L.ScrError) as ei:
         call()
@@ -128,3 +131,22 @@ def test_plan_chunk_validation(lib):
     assert call(bank, 0, n=5000) is False
     big = L.BankDesc(9000, 2, 8, 0, 1, 1, 1, 1, 1, 1, 1, 1, 16)
     assert call(big, 0) is False
+
+
+# bank states scr_bank_init must refuse (checked on the host, nothing enqueued):
+# (slot keys, stamps, clock) of a bank with S = 4 slots, L = 2 layers, E = 8
+BAD_BANK_STATES = [
+    ([3, 3, -1, -1], [1, 2, 0, 0], 2),      # one key in two slots
+    ([3, 16, -1, -1], [1, 2, 0, 0], 2),     # key beyond L * E
+    ([3, -2, -1, -1], [1, 0, 0, 0], 2),     # key below -1
+    ([3, 4, -1, -1], [1, 5, 0, 0], 4),      # a stamp after the clock
+    ([3, 4, -1, -1], [1, 2, 7, 0], 9),      # an empty slot with a stamp
+]
+
+
+@pytest.mark.parametrize("keys,stamps,clock", BAD_BANK_STATES)
+def test_bank_init_rejects_inconsistent_states(lib, keys, stamps, clock):
+    bank = L.BankDesc(4, 2, 8, 0, 1, 1, 1, 1, 1, 1, 1, 1, 16)
+    with pytest.raises(L.ScrError) as ei:
+        L.bank_init(bank, keys, stamps, clock, None)
+    assert ei.value.code == L.SCR_EINVAL

@@ -9,7 +9,7 @@ def test_threshold_cases_printed_on_the_page():
 
 
 def test_capacity_guard():
-    # a layer never routes to more experts than the cache holds
+    # the capacity guard: the layer's distinct experts must fit in the slots
     assert demand_capacity_ok(96, 10, 512, 1100)
     assert not demand_capacity_ok(96, 10, 512, 400)
     assert demand_capacity_ok(4096, 10, 512, 512)
