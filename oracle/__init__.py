@@ -17,6 +17,8 @@ from .dedup import dedup_sorted
 from .lru import SlotBankState, ensure_slots
 from .align import align_blocks, align_capacity
 from .nvfp4 import e2m1_value, e4m3_value, dequant_nvfp4
-from .lowbit import e8m0_value, dequant_fp8, dequant_mxfp4, e4m3_encode, quantize_mxfp8, dequant_mxfp8
-from .mlp import expert_mlp, moe_layer, moe_layer_tokens, moe_layer_w4a8
+from .lowbit import e8m0_value, dequant_fp8, dequant_mxfp4, e4m3_encode
+from .actquant import (layer_activation_scales, quantize_fp8_static, dequant_fp8_static, quantize_nvfp4_act,
+                       dequant_nvfp4_act, e2m1_encode_array)
+from .mlp import expert_mlp, moe_layer, moe_layer_tokens, moe_layer_w4a8, moe_layer_w4a4
 from .dispatch import prefill_on_demand, demand_capacity_ok

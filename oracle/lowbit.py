@@ -64,14 +64,9 @@ def dequant_mxfp4(q_packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return _E2M1_LUT[codes] * s_full
 
 
-# ---------------------------------------------------------------- MXFP8
-# Activations of the W4A8 path (MXFP4 weights times MXFP8 activations), as
-# the OCP MX specification defines the conversion of a block of 32 values:
-# shared exponent = floor(log2(max |v|)) - 8 (8 = the largest e4m3 exponent),
-# each element = v / 2^shared rounded to the nearest e4m3 value (ties to the
-# even code), values beyond the e4m3 range saturated to +-448.  Readings: the
-# shared exponent is clamped to the e8m0 range [-127, 127]; an all-zero block
-# gets scale code 0 (every element is 0 under any scale).
+# ---------------------------------------------------------------- E4M3 encode
+# Nearest E4M3FN code to a value, ties to the even code, magnitudes beyond the
+# format saturated to 448 (used by the activation quantisers, oracle/actquant.py).
 
 _E4M3_POS = np.array([e4m3_value(c) for c in range(0x7F)], dtype=np.float64)   # codes 0x00..0x7E, ascending
 
@@ -103,31 +98,3 @@ def _e4m3_encode_array(a: np.ndarray) -> np.ndarray:
     pick_lo = (dlo < dhi) | ((dlo == dhi) & (lo % 2 == 0))
     code = np.where(exact, hi, np.where(pick_lo, lo, hi)).astype(np.uint8)
     return sign | code
-
-
-def mx_shared_exponent(amax: float) -> int:
-    """floor(log2(amax)) - 8, clamped to [-127, 127]; -127 for an all-zero block."""
-    if amax == 0.0:
-        return -127
-    _, e = np.frexp(amax)                    # amax = f * 2^e, f in [0.5, 1)
-    return max(-127, min(127, int(e) - 1 - 8))
-
-
-def quantize_mxfp8(v: np.ndarray):
-    """MXFP8 codes and e8m0 scale codes of a [rows, cols] array (cols a
-    multiple of 32), blocks of 32 consecutive columns of a row.  Returns
-    (codes uint8 [rows, cols], scales uint8 [rows, cols/32])."""
-    v = np.asarray(v, dtype=np.float64)
-    rows, cols = v.shape
-    blocks = v.reshape(rows, cols // 32, 32)
-    amax = np.max(np.abs(blocks), axis=2)
-    shared = np.array([[mx_shared_exponent(float(a)) for a in row] for row in amax], dtype=np.int64)
-    scaled = np.ldexp(blocks, -shared[:, :, None])          # exact: powers of two
-    codes = _e4m3_encode_array(scaled).reshape(rows, cols)
-    return codes, (shared + 127).astype(np.uint8)
-
-
-def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """MXFP8 to fp64: e4m3(code) * 2^(scale - 127) per 32-column block."""
-    s = _E8M0_LUT[np.asarray(scales, dtype=np.uint8)]
-    return _E4M3_LUT[np.asarray(codes, dtype=np.uint8)] * np.repeat(s, 32, axis=1)

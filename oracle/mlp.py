@@ -11,19 +11,26 @@ W2_e is [H, I] and silu(z) = z / (1 + exp(-z)).  The sum over j runs in rank
 order.  Inputs are the exact values the device receives (bf16 or decoded
 NVFP4), widened to fp64; nothing is rounded on the way.
 
-W4A8 variant (moe_layer_w4a8): the expert input and the SwiGLU output h are
-each quantised to MXFP8 (oracle.lowbit.quantize_mxfp8, per 32 consecutive
-columns of a row) before their product with the weights; everything else as
-above, in fp64.
+Activation-quantising variants (FreeToken PR #676, Solution, fourth bullet:
+the W4A4 GEMM quantises its activations under the max of the routed layer's
+input scales): ``moe_layer_w4a8`` and ``moe_layer_w4a4`` quantise x (per
+token) under the max of the layer's gate/up input scales and each route's h
+(per route, after SwiGLU) under the max of its down input scales, with the
+rules of oracle/actquant.py (FP8 E4M3 per tensor for W4A8, NVFP4 with the
+layer scale as global scale for W4A4), then continue in fp64 as above.
 
 Parity: pinned (pure-Python scalar loops on tiny shapes, single-expert
-reduction with k = 1, zero up-projection gives zero output; the W4A8 variant
-equals the plain layer when every activation and h value is already an MXFP8
-value, and its quantiser is pinned in tests/test_oracle_lowbit.py).
+reduction with k = 1, zero up-projection gives zero output).  The quantising
+variants by: a hand-worked two-token layer (tests/golden/
+act_quant_layer_worked_example.txt), equality with the plain layer when x is
+representable and the up projection is zero, dependence on the input scales
+only through their maxima, token locality (y[t] depends on x[t] alone), and
+the quantisers' own pins.
 """
 import numpy as np
 
-from .lowbit import dequant_mxfp8, quantize_mxfp8
+from .actquant import (dequant_fp8_static, dequant_nvfp4_act, layer_activation_scales, quantize_fp8_static,
+                       quantize_nvfp4_act)
 
 
 def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -77,22 +84,27 @@ def moe_layer(x, ids, w, weights_of):
     return moe_layer_tokens(x, ids, w, weights_of, range(x.shape[0]))
 
 
-def expert_mlp_w4a8(xq: np.ndarray, w13: np.ndarray, w2: np.ndarray) -> np.ndarray:
-    """Like expert_mlp on MXFP8 inputs xq [m, H] (already quantised values),
-    with h quantised to MXFP8 before the down projection."""
-    I = w13.shape[0] // 2
-    g = xq @ w13[:I].T
-    u = xq @ w13[I:].T
-    h = (g / (1.0 + np.exp(-g))) * u
-    hq = dequant_mxfp8(*quantize_mxfp8(h))
-    return hq @ w2.T
+def _quantised(mode: str, v: np.ndarray, scale) -> np.ndarray:
+    """The values the GEMM sees for activations v [rows, cols] under a layer scale."""
+    if mode == "w4a8":
+        return dequant_fp8_static(quantize_fp8_static(v, scale), scale)
+    if mode == "w4a4":
+        return dequant_nvfp4_act(*quantize_nvfp4_act(v, scale), scale)
+    raise ValueError(mode)
 
 
-def moe_layer_w4a8(x: np.ndarray, ids: np.ndarray, w: np.ndarray, weights_of) -> np.ndarray:
-    """W4A8 routed layer for every token: x [T, H] fp64 is quantised to MXFP8
-    per token, each route's h to MXFP8 per route; rank-ordered combine."""
-    xq = dequant_mxfp8(*quantize_mxfp8(x))
+def moe_layer_act_quant(mode: str, x: np.ndarray, ids: np.ndarray, w: np.ndarray, weights_of, input_scale,
+                        down_input_scale) -> np.ndarray:
+    """Routed layer with quantised activations, every token: fp64 [T, H].
+
+    x [T, H] (the bf16 values, as fp64) is quantised per token under
+    a1 = max(input_scale); each route's h = silu(G xq) * (U xq), in fp64, is
+    quantised per route under a2 = max(down_input_scale); o = W2 hq; y[t] is
+    the rank-ordered sum of w[t, j] * o over the token's routes."""
+    a1, a2 = layer_activation_scales(input_scale, down_input_scale)
+    xq = _quantised(mode, x, a1)
     T, k = ids.shape
+    I = None
     outs = {}
     by_e = {}
     for t in range(T):
@@ -100,13 +112,28 @@ def moe_layer_w4a8(x: np.ndarray, ids: np.ndarray, w: np.ndarray, weights_of) ->
             by_e.setdefault(int(ids[t, j]), []).append((t, j))
     for e, routes in by_e.items():
         w13, w2 = weights_of(e)
-        o = expert_mlp_w4a8(np.stack([xq[t] for t, _ in routes]), w13, w2)
+        I = w13.shape[0] // 2
+        xs = np.stack([xq[t] for t, _ in routes])
+        g = xs @ w13[:I].T
+        u = xs @ w13[I:].T
+        h = (g / (1.0 + np.exp(-g))) * u                  # one row per route
+        o = _quantised(mode, h, a2) @ w2.T
         for (t, j), row in zip(routes, o):
             outs[(t, j)] = row
     y = np.zeros_like(x, dtype=np.float64)
     for t in range(T):
         acc = np.zeros(x.shape[1], dtype=np.float64)
-        for j in range(k):
+        for j in range(k):                                 # rank order
             acc = acc + float(w[t, j]) * outs[(t, j)]
         y[t] = acc
     return y
+
+
+def moe_layer_w4a8(x, ids, w, weights_of, input_scale, down_input_scale):
+    """W4A8: FP8 E4M3 activations (one scale per tensor) under the layer's scales."""
+    return moe_layer_act_quant("w4a8", x, ids, w, weights_of, input_scale, down_input_scale)
+
+
+def moe_layer_w4a4(x, ids, w, weights_of, input_scale, down_input_scale):
+    """W4A4: NVFP4 activations with the layer's scales as their global scales."""
+    return moe_layer_act_quant("w4a4", x, ids, w, weights_of, input_scale, down_input_scale)
