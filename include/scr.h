@@ -63,7 +63,8 @@ extern "C" {
 #define SCR_W_NVFP4 1 /* e2m1 codes + e4m3 per-16 block scales + fp32 global */
 #define SCR_W_FP8 2   /* e4m3 codes + one fp32 scale per tensor               */
 #define SCR_W_MXFP4 3 /* e2m1 codes + e8m0 per-32 block scales (OCP MX)       */
-#define SCR_W_MXFP4_A8 4 /* MXFP4 records; activations quantised to MXFP8 (W4A8) */
+#define SCR_W_MXFP4_A8 4 /* MXFP4 records; activations as FP8 E4M3 under the layer's scales (W4A8) */
+#define SCR_W_NVFP4_A4 5 /* NVFP4 records; activations as NVFP4 under the layer's scales (W4A4) */
 
 /* output dtypes of the layer */
 #define SCR_Y_F32 0
@@ -189,17 +190,21 @@ typedef struct scr_host_pool {
  * RoutedExperts [P1 Solution, fourth bullet]: the routed layer's expert count
  * and input scales travel beside the bucket range, so tiles and scales come
  * from the layer, never from the bank.
- *   bucket_rows  device [num_buckets]: record address of each bucket (a slot
- *                of the bank, an expert of a streamed layer buffer, or a row of
- *                a staging buffer); entries of buckets never routed to are
- *                not read.
- *   input_scale  device [num_experts]: the layer's per-expert input scales,
- *                indexed by logical expert.
+ *   bucket_rows       device [num_buckets]: record address of each bucket (a
+ *                     slot of the bank, an expert of a streamed layer buffer,
+ *                     or a row of a staging buffer); entries of buckets never
+ *                     routed to are not read.
+ *   input_scale       device [num_experts]: the layer's per-expert scales of
+ *                     the gate/up input x, indexed by logical expert.
+ *   down_input_scale  device [num_experts]: the same for the down input h;
+ *                     may be NULL except for the activation-quantising
+ *                     formats (SCR_W_MXFP4_A8, SCR_W_NVFP4_A4).
  */
 typedef struct scr_routed_experts {
   int32_t layer, num_experts, k, H, I, wdtype, num_buckets;
   const void* const* bucket_rows;
   const float* input_scale;
+  const float* down_input_scale;
 } scr_routed_experts;
 
 /* tile configuration of the grouped GEMM; a function of (T, k, E_layer,
@@ -333,9 +338,11 @@ int scr_align_blocks(const int32_t* ids, int n, const int32_t* id_to_bucket, int
  * layer's experts, never by the slot count]. */
 int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_cfg* cfg);
 /* workspace of scr_grouped_moe_forward: h [cap][I] bf16 + per-route rows [T*k][H]
- * (fp32 for bf16 weights, bf16 for the narrow formats) + per-route flags; for
- * SCR_W_MXFP4_A8 the MXFP8 codes and scales of x and of h in place of h; for
- * SCR_W_NVFP4 also an fp16 copy of x [T][H] and its row exponents [T] */
+ * (fp32 for bf16 weights, bf16 for the narrow formats) + per-route flags + the
+ * two activation scales; SCR_W_MXFP4_A8 holds the E4M3 codes of x [T][H] and
+ * of h [cap][I] in place of h; SCR_W_NVFP4_A4 the decoded NVFP4 values of x
+ * [T][H] and of h [cap][I] as fp16; SCR_W_NVFP4 also an fp16 copy of x [T][H]
+ * and its row exponents [T] */
 int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cfg* cfg,
                       size_t* bytes);
 
@@ -353,21 +360,32 @@ int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cf
  *   y           device [T][H], f32 or bf16 per y_dtype
  *   ws          device scratch of scr_moe_workspace(...) bytes
  *   cfg_out     host, nullable: receives the tile config used
- *   a_scale_out device f32 [1], nullable: max of the layer's input scales
- *               (what an activation-quantising GEMM would quantise under)
+ *   a_scale_out device f32 [2], nullable: the layer's activation scales, the
+ *               max of view->input_scale and the max of view->down_input_scale
+ *               (0 when that is NULL) [P1 Solution, fourth bullet]
  *   marks       host array of 5 events or NULL: recorded on `stream` before
- *               the launches, again before gate/up (which also clears the
- *               per-route flags and reports a_scale, so marks 0 and 1 bracket
- *               nothing), and after the gate/up, down and combine kernels
- *               (per-kernel timing on the launching stream); NULL entries
- *               are skipped
+ *               the launches, again before gate/up (marks 0 and 1 bracket the
+ *               activation quantisation of the A8/A4 formats and nothing
+ *               otherwise: the gate/up kernel itself clears the per-route
+ *               flags and reports a_scale), and after the gate/up, down and
+ *               combine kernels (per-kernel timing on the launching stream);
+ *               NULL entries are skipped
  * H % 128 == 0, I % 128 == 0, 128 <= H, I <= 16384 (the GEMM's K block is 128).
- * SCR_W_MXFP4_A8 (W4A8, FreeToken PR #676 Known limits names activation-
- * quantising GEMMs; the MX pairing is this library's reading): x is quantised
- * to MXFP8 per row (scr_quantize_mxfp8, between marks 0 and 1), each route's
- * h to MXFP8 per 32-column block in the gate/up epilogue, and both GEMMs run
- * on the block-scaled fp8 x fp4 MFMA; needs H and I multiples of 512, at most
- * 4096 (SCR_ENOTSUP otherwise, nothing launched).
+ * Activation-quantising formats [P1 Solution, fourth bullet; Tests, fourth
+ * bullet: the activations are quantised under the max of the routed layer's
+ * input scales, never the bank's]: a1 = max(input_scale[0..E)),
+ * a2 = max(down_input_scale[0..E)).
+ *   SCR_W_MXFP4_A8 (W4A8): x as E4M3 codes of x / a1 (scr_quantize_fp8's rule),
+ *     each route's h as E4M3 codes of h / a2 (computed from the fp32
+ *     accumulators), both GEMMs on the block-scaled fp8 x fp4 MFMA with unit
+ *     activation scales and a1 (a2) applied to the fp32 accumulators.
+ *   SCR_W_NVFP4_A4 (W4A4): x and h as NVFP4 with a1 (a2) as global scale
+ *     (scr_quantize_nvfp4's rule; h per route and 16 columns); activation and
+ *     weight codes times their block scales are exact fp16 values, so both
+ *     GEMMs run on the fp16 MFMA over exact operands, the global scales applied
+ *     to the fp32 accumulators.
+ *   Both need down_input_scale and H, I multiples of 512 (SCR_ENOTSUP
+ *   otherwise, nothing launched).
  * SCR_W_NVFP4 with many rows per expert (the wide kernels: cfg.m_chunk 112,
  * H and I multiples of 512): the gate/up runs on the fp16 MFMA.  Between
  * marks 1 and 2 (so inside the gate/up time) each row of x is copied to
@@ -383,15 +401,26 @@ int scr_grouped_moe_forward(const scr_routed_experts* view, const void* x, int T
                             size_t ws_bytes, scr_tile_cfg* cfg_out, float* a_scale_out,
                             hipEvent_t* marks, hipStream_t stream);
 
-/* quantize_mxfp8 (the W4A8 activations; OCP Microscaling Formats, MXFP8
- * E4M3): x device bf16 [rows][cols], cols a multiple of 32; per row and block
- * of 32 consecutive columns, shared = floor(log2(max |x|)) - 8 clamped to
- * [-127, 127] (-127 for an all-zero block), scales[row][block] = shared + 127
- * (e8m0), codes[row][col] = e4m3 of x * 2^-shared rounded to nearest even,
- * saturated to +-448.  codes device [rows][cols], scales device [rows][cols/32].
- * Inputs must be finite. */
-int scr_quantize_mxfp8(const void* x, long long rows, int cols, uint8_t* codes, uint8_t* scales,
-                       hipStream_t stream);
+/* quantize_fp8 [P1 Solution, fourth bullet: activations quantised under the
+ * max of the layer's input scales; the static FP8 activation encoding is a
+ * reading]: with a = max(scales[0..n_scales)) (device f32), codes[i] = the
+ * OCP E4M3FN code of x[i] / a (an IEEE fp32 division), rounded to nearest
+ * even and saturated to +-448.  x device bf16 [rows][cols], codes device u8
+ * [rows][cols].  Inputs finite, a > 0. */
+int scr_quantize_fp8(const void* x, long long rows, int cols, const float* scales, int n_scales,
+                     uint8_t* codes, hipStream_t stream);
+
+/* quantize_nvfp4 [same passage; NVFP4 activations with the layer scale as
+ * their global scale]: with a = max(scales[0..n_scales)), per row and block
+ * of 16 consecutive columns: block = E4M3 code of amax / (6 * a) (fp32
+ * product and division, nearest even, saturated to 448), then per element
+ * the E2M1 code of x / (e4m3(block) * a) (nearest, ties to even, saturated
+ * to +-6; sign bit set for every negative input); a block whose scale is
+ * zero gets zero codes.  x device bf16 [rows][cols], cols a multiple of 16;
+ * codes device u8 [rows][cols / 2] (low nibble = even column); block_scales
+ * device u8 [rows][cols / 16].  Inputs finite, a > 0. */
+int scr_quantize_nvfp4(const void* x, long long rows, int cols, const float* scales, int n_scales,
+                       uint8_t* codes, uint8_t* block_scales, hipStream_t stream);
 
 /* ------------------------------------------------ whole-layer / staging */
 

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libscr.so")
 
 SCR_OK, SCR_EINVAL, SCR_ENOTSUP, SCR_ECAPACITY, SCR_EHIP = 0, -1, -2, -3, -4
 SCR_ERR_CAPACITY = 1
-SCR_W_BF16, SCR_W_NVFP4, SCR_W_FP8, SCR_W_MXFP4, SCR_W_MXFP4_A8 = 0, 1, 2, 3, 4
+SCR_W_BF16, SCR_W_NVFP4, SCR_W_FP8, SCR_W_MXFP4, SCR_W_MXFP4_A8, SCR_W_NVFP4_A4 = 0, 1, 2, 3, 4, 5
 SCR_Y_F32, SCR_Y_BF16 = 0, 1
 SCR_POLICY_LRU, SCR_POLICY_LRFU = 0, 1
 SCR_MAX_TOPK = 32
@@ -29,7 +29,7 @@ EXPORTS = (
     "scr_record_layout_of", "scr_route", "scr_dedup", "scr_ensure_slots", "scr_ensure_slots_batched",
     "scr_copy_misses", "scr_plan_chunk",
     "scr_align_capacity", "scr_align_workspace", "scr_align_blocks", "scr_tile_config",
-    "scr_moe_workspace", "scr_grouped_moe_forward", "scr_quantize_mxfp8", "scr_stream_layer_async",
+    "scr_moe_workspace", "scr_grouped_moe_forward", "scr_quantize_fp8", "scr_quantize_nvfp4", "scr_stream_layer_async",
     "scr_stage_plan",
     "scr_stage_rows_async", "scr_stage_rows_dma_async", "scr_fill_row_table", "scr_fill_staged_rows", "scr_bank_rebuild_map",
     "scr_bank_init",
@@ -67,7 +67,7 @@ class HostPoolDesc(C.Structure):
 class RoutedExperts(C.Structure):
     _fields_ = [("layer", C.c_int32), ("num_experts", C.c_int32), ("k", C.c_int32), ("H", C.c_int32),
                 ("I", C.c_int32), ("wdtype", C.c_int32), ("num_buckets", C.c_int32),
-                ("bucket_rows", C.c_void_p), ("input_scale", C.c_void_p)]
+                ("bucket_rows", C.c_void_p), ("input_scale", C.c_void_p), ("down_input_scale", C.c_void_p)]
 
 
 class TileCfg(C.Structure):
@@ -102,7 +102,8 @@ _SIGS = {
     "scr_moe_workspace": (_I, [_I, _I, _I, _I, _I, C.POINTER(TileCfg), C.POINTER(_SZ)]),
     "scr_grouped_moe_forward": (_I, [C.POINTER(RoutedExperts), _P, _I, _P, _P, _P, _P, _P, _P, _I, _P,
                                      _SZ, C.POINTER(TileCfg), _P, _P, _P]),
-    "scr_quantize_mxfp8": (_I, [_P, C.c_longlong, _I, _P, _P, _P]),
+    "scr_quantize_fp8": (_I, [_P, C.c_longlong, _I, _P, _I, _P, _P]),
+    "scr_quantize_nvfp4": (_I, [_P, C.c_longlong, _I, _P, _I, _P, _P, _P]),
     "scr_stream_layer_async": (_I, [C.POINTER(HostPoolDesc), _I, _P, _P]),
     "scr_stage_plan": (_I, [C.POINTER(BankDesc), C.POINTER(HostPoolDesc), _I, _I, _P, C.POINTER(Run), _I,
                             C.POINTER(_I), _P]),
@@ -248,8 +249,13 @@ def grouped_moe_forward(view: RoutedExperts, x, T, topk_w, sorted_routes, active
     return cfg
 
 
-def quantize_mxfp8(x, rows, cols, codes, scales, stream):
-    _check("scr_quantize_mxfp8", load().scr_quantize_mxfp8(_p(x), rows, cols, _p(codes), _p(scales), stream))
+def quantize_fp8(x, rows, cols, scales, n_scales, codes, stream):
+    _check("scr_quantize_fp8", load().scr_quantize_fp8(_p(x), rows, cols, _p(scales), n_scales, _p(codes), stream))
+
+
+def quantize_nvfp4(x, rows, cols, scales, n_scales, codes, block_scales, stream):
+    _check("scr_quantize_nvfp4", load().scr_quantize_nvfp4(_p(x), rows, cols, _p(scales), n_scales, _p(codes),
+                                                           _p(block_scales), stream))
 
 
 def stream_layer_async(pool: HostPoolDesc, layer, dst, stream):

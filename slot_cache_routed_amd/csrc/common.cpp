@@ -41,7 +41,7 @@ extern "C" int scr_record_layout_of(int wdtype, int H, int I, scr_record_layout*
     SCR_CHECK_ARG(out->record_bytes % 16 == 0, "record_layout: bf16 record not 16-byte sized");
     return SCR_OK;
   }
-  if (wdtype == SCR_W_NVFP4) {
+  if (wdtype == SCR_W_NVFP4 || wdtype == SCR_W_NVFP4_A4) {
     out->w13_off = 0;
     out->w13_scale_off = out->w13_off + 2 * i * h / 2;
     out->w2_off = out->w13_scale_off + 2 * i * h / 16;

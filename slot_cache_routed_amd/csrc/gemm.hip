@@ -73,6 +73,41 @@ __device__ __forceinline__ float e4m3_to_f32(unsigned c) {
   return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
 }
 
+// ------------------------------------------- activation codes (A8 / A4)
+// OCP E4M3FN code of v, rounded to nearest even, saturated to +-448 (the
+// hardware conversion rounds to nearest even; the clamp makes it saturate)
+__device__ __forceinline__ unsigned e4m3_code_sat(float v) {
+  const float c = fminf(fmaxf(v, -448.0f), 448.0f);
+  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+// E2M1 magnitude code (0..7) of a magnitude: nearest of 0, 0.5, 1, 1.5, 2, 3,
+// 4, 6, ties to the even code, saturated to 6
+__device__ __forceinline__ int e2m1_mag_code(float m) {
+  return (int)(m > 0.25f) + (int)(m >= 0.75f) + (int)(m > 1.25f) + (int)(m >= 1.75f) + (int)(m > 2.5f) +
+         (int)(m >= 3.5f) + (int)(m > 5.0f);
+}
+__device__ __forceinline__ float e2m1_mag_value(int c) {
+  return c < 2 ? 0.5f * (float)c : __builtin_amdgcn_ldexpf((c & 1) ? 1.5f : 1.0f, (c >> 1) - 1);
+}
+// NVFP4 activation block under the layer scale s: the block scale code of a
+// block whose largest magnitude is amax (fp32 product and IEEE division)
+__device__ __forceinline__ unsigned nvfp4_block_code(float amax, float s) {
+  return e4m3_code_sat(amax / (6.0f * s));
+}
+// the element's E2M1 code (sign in bit 3, set for every negative v) under a
+// block scale value bv (> 0) and the layer scale s
+__device__ __forceinline__ int nvfp4_elem_code(float v, float bv, float s) {
+  const int mag = bv > 0.0f ? e2m1_mag_code(fabsf(v / (bv * s))) : 0;
+  return mag | (v < 0.0f ? 8 : 0);
+}
+// the element's decoded value without the layer scale, e2m1 * block, as fp16
+// bits (exact: at most 5 significant bits, magnitude in [2^-10, 2688])
+__device__ __forceinline__ uint16_t nvfp4_elem_f16(int code, float bv) {
+  const float m = e2m1_mag_value(code & 7) * bv;
+  const _Float16 h = (_Float16)((code & 8) ? -m : m);
+  return __builtin_bit_cast(uint16_t, h);
+}
+
 // Weight formats: bytes of one tile-block (16 rows x 128 columns) of codes
 // and of its block scales, whether the record carries a per-tensor scale,
 // and the per-route row type: fp32 for bf16 weights (their output tolerance
@@ -104,6 +139,9 @@ struct WFmt<SCR_W_MXFP4> {
   static constexpr bool gscale = false;
   typedef __bf16 row_t;
 };
+// W4A4 reads NVFP4 records
+template <>
+struct WFmt<SCR_W_NVFP4_A4> : WFmt<SCR_W_NVFP4> {};
 template <int WDT>
 struct RowT {
   typedef typename WFmt<WDT>::row_t type;
@@ -121,32 +159,46 @@ struct GemmArgs {
   bf16* h;              // [h_rows][I]
   void* o;              // [R][H] per-route weighted expert outputs (RowT<WDT>)
   int32_t* flags;       // [R]
-  const float* input_scale;  // [E] the layer's activation scales
-  float* a_scale_out;        // nullable, device
-  // W4A8 only: MXFP8 activations (e4m3 codes, e8m0 scale per 32 columns)
+  const float* input_scale;       // [E] the layer's scales of the gate/up input
+  const float* down_input_scale;  // [E] the layer's scales of the down input, or null
+  float* a_scale_out;             // nullable, device [2]
+  // A8 / A4 formats: the layer's activation scales (max of each array),
+  // written by the activation quantisation before the GEMMs
+  const float* act_scale;  // [2]
+  // W4A8 only: E4M3 codes of x / a1 and of h / a2
   const uint8_t* xq;  // [T][H]
-  const uint8_t* xs;  // [T][H/32]
   uint8_t* hq;        // [h_rows][I]
-  uint8_t* hs;        // [h_rows][I/32]
-  // NVFP4 wide gate/up: x as fp16, row t scaled by 2^xe[t]
+  // NVFP4 wide gate/up: x as fp16, row t scaled by 2^xe[t]; W4A4: the decoded
+  // NVFP4 values of x (xe unused)
   const uint16_t* x16;  // [T][H]
   const int32_t* xe;    // [T]
   int T, k, R, H, I, B, h_rows, E;
 };
 
+// max of n layer scales over one wave (every lane gets it; -inf for n = 0)
+__device__ __forceinline__ float wave_scale_max(const float* s, int n, int lane) {
+  float m = -INFINITY;
+  for (int e = lane; e < n; e += 64) m = fmaxf(m, s[e]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  return m;
+}
+
 // Work that must precede the down GEMM, done by the gate/up workgroups before
 // anything else (so that it costs no launch of its own): clear the per-route
-// written flags that down sets, and report the layer's activation scale
-// (the max of its input scales) from the first wave of workgroup 0.
+// written flags that down sets, and report the layer's activation scales
+// (the max of each array of its input scales) from the first wave of
+// workgroup 0.  (The A8/A4 formats report them from their quantisation.)
 __device__ __forceinline__ void gateup_prologue(const GemmArgs& a) {
   const int nthreads = gridDim.x * blockDim.x;
   for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < a.R; r += nthreads) a.flags[r] = 0;
-  if (a.a_scale_out && blockIdx.x == 0 && threadIdx.x < 64) {
-    float m = -INFINITY;
-    for (int e = threadIdx.x; e < a.E; e += 64) m = fmaxf(m, a.input_scale[e]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if (threadIdx.x == 0) *a.a_scale_out = m;
+  if (a.a_scale_out && !a.act_scale && blockIdx.x == 0 && threadIdx.x < 64) {
+    const float m1 = wave_scale_max(a.input_scale, a.E, threadIdx.x);
+    const float m2 = a.down_input_scale ? wave_scale_max(a.down_input_scale, a.E, threadIdx.x) : 0.0f;
+    if (threadIdx.x == 0) {
+      a.a_scale_out[0] = m1;
+      a.a_scale_out[1] = m2;
+    }
   }
 }
 
@@ -358,6 +410,10 @@ struct BFrag<SCR_W_MXFP4, NT> {
   }
   __device__ __forceinline__ bf16x8 get_hw(int t, int st) const { return get(t, st); }
 };
+
+// W4A4 reads NVFP4 records
+template <int NT>
+struct BFrag<SCR_W_NVFP4_A4, NT> : BFrag<SCR_W_NVFP4, NT> {};
 
 struct PassCtx {
   int tid, lane, wave, col, grp, rows, m0, nkb, ncol0, tx;
@@ -633,9 +689,10 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
 
 // the NVFP4 wide gate/up runs on fp16 (half the decode work of bf16: see
 // BFrag<SCR_W_NVFP4>::get_f16); every other wide pass on bf16
+// (W4A4: both GEMMs, whose activations are exact fp16 values)
 template <int WDT, bool GATEUP>
 struct WideF16A {
-  static constexpr bool value = WDT == SCR_W_NVFP4 && GATEUP;
+  static constexpr bool value = (WDT == SCR_W_NVFP4 && GATEUP) || WDT == SCR_W_NVFP4_A4;
 };
 
 // x as fp16 for the F16A gate/up, one wave per token: the row is scaled by
@@ -805,24 +862,43 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
       for (int mt = 0; mt < MTC; ++mt) {
         // rows i and i + 1 of a lane converted as one bf16 pair, stored as halves
         uint16_t* sh16 = reinterpret_cast<uint16_t*>(sh);
+        if constexpr (WDT == SCR_W_NVFP4_A4) {
+          // W4A4: h quantised to NVFP4 under the layer's down scale a2, per
+          // row and 16 columns (one gate tile t: its 16 columns sit in the 16
+          // lanes of a row group), stored as the exact fp16 value e2m1 * block
+          // for the down GEMM's fp16 operand (a2 goes to its accumulators)
+          const float a2 = a.act_scale[1];
 #pragma unroll
-        for (int i = 0; i < 4; i += 2)
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int t = 0; t < NTW / 2; ++t) {
-            unsigned p;
-            if constexpr (F16A) {
-              // the row's power of two comes off after the global scale, as
-              // exact multiplies (gs * acc is then the bf16 path's value)
-              const float s0 = row_rs[mt * 16 + grp * 4 + i], s1 = row_rs[mt * 16 + grp * 4 + i + 1];
-              p = pack_bf16(silu_mul(gs * acc[mt][t][i] * s0, gs * acc[mt][t + NTW / 2][i] * s0),
-                            silu_mul(gs * acc[mt][t][i + 1] * s1, gs * acc[mt][t + NTW / 2][i + 1] * s1));
-            } else {
-              p = pack_bf16(silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]),
-                            silu_mul(gs * acc[mt][t][i + 1], gs * acc[mt][t + NTW / 2][i + 1]));
+            for (int t = 0; t < NTW / 2; ++t) {
+              const float hv = silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]);
+              float m = fabsf(hv);
+#pragma unroll
+              for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+              const float bv = __builtin_amdgcn_cvt_f32_fp8((int)nvfp4_block_code(m, a2), 0);
+              sh16[(grp * 4 + i) * HC + 16 * t + col] = nvfp4_elem_f16(nvfp4_elem_code(hv, bv, a2), bv);
             }
-            sh16[(grp * 4 + i) * HC + 16 * t + col] = (uint16_t)p;
-            sh16[(grp * 4 + i + 1) * HC + 16 * t + col] = (uint16_t)(p >> 16);
-          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; i += 2)
+#pragma unroll
+            for (int t = 0; t < NTW / 2; ++t) {
+              unsigned p;
+              if constexpr (F16A) {
+                // the row's power of two comes off after the global scale, as
+                // exact multiplies (gs * acc is then the bf16 path's value)
+                const float s0 = row_rs[mt * 16 + grp * 4 + i], s1 = row_rs[mt * 16 + grp * 4 + i + 1];
+                p = pack_bf16(silu_mul(gs * acc[mt][t][i] * s0, gs * acc[mt][t + NTW / 2][i] * s0),
+                              silu_mul(gs * acc[mt][t][i + 1] * s1, gs * acc[mt][t + NTW / 2][i + 1] * s1));
+              } else {
+                p = pack_bf16(silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]),
+                              silu_mul(gs * acc[mt][t][i + 1], gs * acc[mt][t + NTW / 2][i + 1]));
+              }
+              sh16[(grp * 4 + i) * HC + 16 * t + col] = (uint16_t)p;
+              sh16[(grp * 4 + i + 1) * HC + 16 * t + col] = (uint16_t)(p >> 16);
+            }
+        }
 #pragma unroll
         for (int rd = 0; rd < ROUNDS; ++rd) {
           const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
@@ -1001,9 +1077,10 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
     toff0[t] = (int)(GATEUP ? a.lay.w13_off : a.lay.w2_off) + tb * tile_bytes;
     soff0[t] = (int)(GATEUP ? a.lay.w13_scale_off : a.lay.w2_scale_off) + tb * stile_bytes;
   }
-  const float gs = WFmt<WDT>::gscale
-                       ? *reinterpret_cast<const float*>(rec + (GATEUP ? a.lay.g13_off : a.lay.g2_off))
-                       : 1.0f;
+  float gs = WFmt<WDT>::gscale ? *reinterpret_cast<const float*>(rec + (GATEUP ? a.lay.g13_off : a.lay.g2_off))
+                               : 1.0f;
+  // W4A4: the layer's activation scale joins the record's global scale
+  if constexpr (WDT == SCR_W_NVFP4_A4) gs *= a.act_scale[GATEUP ? 0 : 1];
   for (int m0 = p0; m0 < p1; m0 += MT * 16) {
     const int rows = min(MT * 16, p1 - m0);
     for (int i = tid; i < MT * 16; i += kThreads) {
@@ -1017,9 +1094,11 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
         }
       }
       src_row[i] = off;
-      if constexpr (WideF16A<WDT, GATEUP>::value) {
+      if constexpr (WideF16A<WDT, GATEUP>::value && WDT == SCR_W_NVFP4) {
         const int r = i < rows ? a.sorted_routes[m0 + i] : -1;
         row_rs[i] = (r >= 0 && r < a.R) ? __builtin_ldexpf(1.0f, -a.xe[r / a.k]) : 1.0f;
+      } else if constexpr (WideF16A<WDT, GATEUP>::value) {
+        row_rs[i] = 1.0f;
       }
       if (!GATEUP) {
         const int r = i < rows ? a.sorted_routes[m0 + i] : -1;
@@ -1113,78 +1192,138 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ o,
   }
 }
 
-// ------------------------------------------------ W4A8: MXFP4 x MXFP8
+// ------------------------------------- activations under the layer's scales
 //
-// Activations quantised to MXFP8 (OCP MX: e4m3 elements, one e8m0 scale per
-// 32 consecutive columns of a row) against MXFP4 weights, multiplied by the
-// gfx950 block-scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4 (A fp8, B fp4):
-// one instruction per 16x16 output tile and 128-wide K block, the scales
-// applied inside the instruction, no dequantisation.  Operand layout per lane
-// l, g = l / 16 (measured on the device with one-hot operands):
+// The A8 and A4 formats quantise each GEMM's input under the largest of the
+// routed layer's input scales for that GEMM (FreeToken PR #676, Solution,
+// fourth bullet): a1 = max(input_scale), a2 = max(down_input_scale).  x is
+// quantised here, before the GEMMs, one thread per 16 consecutive elements of
+// a row; h in the gate/up epilogue.  MODE:
+//   kActFp8      E4M3 codes of x / a1 (W4A8, and scr_quantize_fp8)
+//   kActNvfp4    NVFP4 codes (packed, low nibble = even column) and block
+//                scale codes (scr_quantize_nvfp4)
+//   kActNvfp4F16 the decoded NVFP4 values e2m1 * block as fp16 (the W4A4
+//                GEMM's operand; a1 goes to its accumulators)
+// Every workgroup reduces the scale arrays itself (at most 4096 floats);
+// workgroup 0 also stores a1, a2 for the GEMMs and for the caller.
+constexpr int kActFp8 = 0, kActNvfp4 = 1, kActNvfp4F16 = 2;
+constexpr int kActMaxGrid = 1024;
+
+template <int MODE>
+__global__ __launch_bounds__(256) void act_quant_kernel(const bf16* __restrict__ x, long long nblk,
+                                                        const float* __restrict__ s1, const float* __restrict__ s2,
+                                                        int n_scales, uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ bs, uint16_t* __restrict__ f16,
+                                                        float* __restrict__ act_scale, float* __restrict__ a_out) {
+  __shared__ float sm;
+  if (threadIdx.x < 64) {
+    const float m1 = wave_scale_max(s1, n_scales, threadIdx.x);
+    const float m2 = s2 ? wave_scale_max(s2, n_scales, threadIdx.x) : 0.0f;
+    if (threadIdx.x == 0) {
+      sm = m1;
+      if (blockIdx.x == 0) {
+        if (act_scale) {
+          act_scale[0] = m1;
+          act_scale[1] = m2;
+        }
+        if (a_out) {
+          a_out[0] = m1;
+          a_out[1] = m2;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const float a1 = sm;
+  for (long long b = blockIdx.x * 256ll + threadIdx.x; b < nblk; b += (long long)gridDim.x * 256) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 16);
+    const u32x4 v0 = ldg<u32x4>(src), v1 = ldg<u32x4>(src + 1);
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(v0[i]);
+      f[2 * i + 1] = bf16_hi(v0[i]);
+      f[8 + 2 * i] = bf16_lo(v1[i]);
+      f[8 + 2 * i + 1] = bf16_hi(v1[i]);
+    }
+    if constexpr (MODE == kActFp8) {
+      u32x4 out;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        out[i] = e4m3_code_sat(f[4 * i] / a1) | (e4m3_code_sat(f[4 * i + 1] / a1) << 8) |
+                 (e4m3_code_sat(f[4 * i + 2] / a1) << 16) | (e4m3_code_sat(f[4 * i + 3] / a1) << 24);
+      reinterpret_cast<u32x4*>(q + b * 16)[0] = out;
+    } else {
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      const unsigned bc = nvfp4_block_code(amax, a1);
+      const float bv = __builtin_amdgcn_cvt_f32_fp8((int)bc, 0);
+      int c[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = nvfp4_elem_code(f[i], bv, a1);
+      if constexpr (MODE == kActNvfp4) {
+        u32x2 out;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          unsigned d = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) d |= (unsigned)c[8 * w + i] << (4 * i);
+          out[w] = d;
+        }
+        reinterpret_cast<u32x2*>(q + b * 8)[0] = out;
+        bs[b] = (uint8_t)bc;
+      } else {
+        u32x4 out[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          out[i / 4][i % 4] = (unsigned)nvfp4_elem_f16(c[2 * i], bv) | ((unsigned)nvfp4_elem_f16(c[2 * i + 1], bv) << 16);
+        u32x4* dst = reinterpret_cast<u32x4*>(f16 + b * 16);
+        dst[0] = out[0];
+        dst[1] = out[1];
+      }
+    }
+  }
+}
+
+template <int MODE>
+static int launch_act_quant(const bf16* x, long long rows, int cols, const float* s1, const float* s2, int n_scales,
+                            uint8_t* q, uint8_t* bs, uint16_t* f16, float* act_scale, float* a_out, hipStream_t s) {
+  const long long nblk = rows * (cols / 16);
+  long long grid = (nblk + 255) / 256;
+  if (grid > kActMaxGrid) grid = kActMaxGrid;
+  if (grid < 1) grid = 1;  // the scales are still reduced and reported
+  hipLaunchKernelGGL((act_quant_kernel<MODE>), dim3((unsigned)grid), dim3(256), 0, s, x, nblk, s1, s2, n_scales, q,
+                     bs, f16, act_scale, a_out);
+  SCR_CHECK_LAUNCH();
+  return SCR_OK;
+}
+
+// ------------------------------------------------ W4A8: MXFP4 x FP8
+//
+// FP8 activations (E4M3 codes of x / a1, h / a2) against MXFP4 weights,
+// multiplied by the gfx950 block-scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4
+// (A fp8, B fp4): one instruction per 16x16 output tile and 128-wide K block,
+// the weights' e8m0 scales applied inside the instruction, the activations'
+// scale 1 (code 127) there and the layer scale applied to the fp32
+// accumulators.  No dequantisation.  Operand layout per lane l, g = l / 16
+// (measured on the device with one-hot operands):
 //   A (16 x 128 fp8): row l % 16; bytes 0..15 hold k = 16 g .. 16 g + 15,
 //                     bytes 16..31 hold k = 64 + 16 g .. 64 + 16 g + 15
 //   B (128 x 16 fp4): column l % 16; nibbles 0..31 (low first) hold
 //                     k = 32 g .. 32 g + 31: exactly one MXFP4 tile-block load
 //   scales: lane l gives the e8m0 code of row (A) / column (B) l % 16 for the
 //           32-column block l / 16: the MXFP4 tile-block's scale byte `lane`
-// x is quantised by a separate pass; h is quantised in the gate/up epilogue,
-// per row and 32-column block (one wave's 32 h columns), and read by down the
-// way gate/up reads x.
-
-constexpr int kMxScaleCols = 128;  // e8m0 scales per staged activation row (K <= 4096)
-
-// Shared exponent of an MX block: floor(log2(amax)) - 8 (8 = the largest e4m3
-// exponent), clamped to the e8m0 range; -127 (code 0) for an all-zero block.
-__device__ __forceinline__ int mx_shared_exp(float amax) {
-  if (!(amax > 0.0f)) return -127;
-  const int e = __builtin_amdgcn_frexp_expf(amax) - 1 - 8;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-// two values as e4m3 codes (low byte = a) under a block's shared exponent:
-// v * 2^-shared is exact, saturated to +-448, then rounded to nearest even
-__device__ __forceinline__ unsigned mx_fp8_pair(float a, float b, int shared) {
-  const float va = fminf(fmaxf(__builtin_amdgcn_ldexpf(a, -shared), -448.0f), 448.0f);
-  const float vb = fminf(fmaxf(__builtin_amdgcn_ldexpf(b, -shared), -448.0f), 448.0f);
-  return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(va, vb, 0, false) & 0xFFFFu;
-}
-
-// one thread per 32-element block of a row-major [rows][cols] bf16 array
-__global__ __launch_bounds__(256) void mxfp8_quant_kernel(const bf16* __restrict__ x, long long nblocks,
-                                                          uint8_t* __restrict__ q, uint8_t* __restrict__ s) {
-  for (long long b = blockIdx.x * 256ll + threadIdx.x; b < nblocks; b += (long long)gridDim.x * 256) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 32);
-    u32x4 v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = ldg<u32x4>(src + i);
-    float f[32];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const unsigned w = v[i / 4][i % 4];
-      f[2 * i] = __uint_as_float(w << 16);
-      f[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u);
-      amax = fmaxf(amax, fmaxf(fabsf(f[2 * i]), fabsf(f[2 * i + 1])));
-    }
-    const int shared = mx_shared_exp(amax);
-    u32x4 out[2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      out[i / 4][i % 4] = mx_fp8_pair(f[4 * i], f[4 * i + 1], shared) | (mx_fp8_pair(f[4 * i + 2], f[4 * i + 3], shared) << 16);
-    u32x4* dst = reinterpret_cast<u32x4*>(q + b * 32);
-    dst[0] = out[0];
-    dst[1] = out[1];
-    s[b] = (uint8_t)(shared + 127);
-  }
-}
+// h is quantised in the gate/up epilogue and read by down the way gate/up
+// reads x.
+constexpr int kUnitScale = 127;  // e8m0 code of 2^0
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // RES: down with K = I = kWideBufs blocks keeps the bucket's whole h block
 // resident in LDS (a compile-time choice: the run-time one spills registers)
 template <int MT, bool GATEUP, int EW, int NTW, int MTC, bool RES>
-__device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row, const uint8_t* asc,
-                                          const int* row_route, const float* row_w, uint8_t* As0, uint8_t* As1,
+__device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row, const int* row_route, const float* row_w, uint8_t* As0, uint8_t* As1,
                                           uint8_t* As2, uint8_t* As3, uint32_t* stg, int m0,
                                           __amdgpu_buffer_rsrc_t wrsrc, const int* toff0, const int* soff0,
                                           int nkb, int c_begin, int c_end) {
@@ -1244,26 +1383,18 @@ __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row,
   uint32_t* const wst = stg + wave * (kWideStage / 4);
   auto epilogue = [&](int ch) {
     if (GATEUP) {
-      // h = silu(g) * u for this wave's 32 h columns (one MX block per row),
-      // quantised per row: block max across the 16 lanes of a row group
+      // h = silu(g) * u for this wave's 32 h columns, g and u the accumulators
+      // times a1, as E4M3 codes of h / a2
+      const float a1 = a.act_scale[0], a2 = a.act_scale[1];
       uint8_t* sh = reinterpret_cast<uint8_t*>(wst);
 #pragma unroll
       for (int mt = 0; mt < MTC; ++mt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float h0 = silu_mul(acc[mt][0][i], acc[mt][NTW / 2][i]);
-          const float h1 = silu_mul(acc[mt][1][i], acc[mt][NTW / 2 + 1][i]);
-          float m = fmaxf(fabsf(h0), fabsf(h1));
-#pragma unroll
-          for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
-          const int shared = mx_shared_exp(m);
-          const unsigned p = mx_fp8_pair(h0, h1, shared);
-          sh[(grp * 4 + i) * 32 + col] = (uint8_t)(p & 0xFF);
-          sh[(grp * 4 + i) * 32 + 16 + col] = (uint8_t)(p >> 8);
-          if (col == 0) {
-            const int pos = m0 + mt * 16 + grp * 4 + i;
-            a.hs[(size_t)pos * (a.I / 32) + ch * EW + wave] = (uint8_t)(shared + 127);
-          }
+          const float h0 = silu_mul(a1 * acc[mt][0][i], a1 * acc[mt][NTW / 2][i]);
+          const float h1 = silu_mul(a1 * acc[mt][1][i], a1 * acc[mt][NTW / 2 + 1][i]);
+          sh[(grp * 4 + i) * 32 + col] = (uint8_t)e4m3_code_sat(h0 / a2);
+          sh[(grp * 4 + i) * 32 + 16 + col] = (uint8_t)e4m3_code_sat(h1 / a2);
         }
         // 16 rows x 32 bytes = 32 lanes x 16 bytes
         if (lane < 32) {
@@ -1341,12 +1472,11 @@ __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row,
 #pragma unroll
         for (int mt = 0; mt < MTC; ++mt) {
           const i32x8 af = read_a(buf, mt);
-          const int sa = asc[(mt * 16 + col) * kMxScaleCols + 4 * kb + grp];
 #pragma unroll
           for (int t = 0; t < NTW; ++t) {
             const u32x4 c4 = bc.codes[t];
             const i32x8 bf = {(int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3], 0, 0, 0, 0};
-            acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[mt][t], 0, 4, 0, sa, 0,
+            acc[mt][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf, acc[mt][t], 0, 4, 0, kUnitScale, 0,
                                                                             (int)(bc.sc[t] & 0xFFu));
           }
         }
@@ -1370,7 +1500,6 @@ __global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int group
   __shared__ __attribute__((aligned(1024))) uint8_t As1[MT * 16 * kKB];
   __shared__ __attribute__((aligned(1024))) uint8_t As2[MT * 16 * kKB];
   __shared__ __attribute__((aligned(1024))) uint8_t As3[MT * 16 * kKB];
-  __shared__ __attribute__((aligned(16))) uint8_t asc[MT * 16 * kMxScaleCols];  // e8m0 scales of the pass rows
   __shared__ int src_row[MT * 16];
   __shared__ int row_route[GATEUP ? 1 : MT * 16];
   __shared__ float row_w[GATEUP ? 1 : MT * 16];
@@ -1386,7 +1515,6 @@ __global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int group
   const int tid = threadIdx.x, wave = tid >> 6;
   const int K = GATEUP ? a.H : a.I;
   const int nkb = K / kKB;
-  const int nsc = K / 32;
   const int nchunks = GATEUP ? a.I / (8 * NTW * EW) : a.H / (16 * NTW * EW);
   const int c_begin = g * nchunks / groups, c_end = (g + 1) * nchunks / groups;
   if (c_begin >= c_end) return;
@@ -1420,21 +1548,14 @@ __global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int group
       if (!GATEUP) {
         const bool valid = r >= 0 && r < a.R;
         row_route[i] = valid ? r : -1;
-        row_w[i] = valid ? a.topk_w[r] : 0.0f;
+        row_w[i] = valid ? a.topk_w[r] * a.act_scale[1] : 0.0f;  // the layer's h scale folded in
       }
-    }
-    __syncthreads();
-    // the scales of the pass rows (padding rows: those of row 0 of the source)
-    for (int e = tid; e < MT * 16 * nsc; e += kThreads) {
-      const int i = e / nsc, c = e - i * nsc;
-      const int off = src_row[i] >= 0 ? src_row[i] : 0;
-      asc[i * kMxScaleCols + c] = GATEUP ? a.xs[off / 32 + c] : a.hs[off / 32 + c];
     }
     __syncthreads();
 #define SCR_W4A8_PASS(n)                                                                                     \
   case n:                                                                                                    \
     if constexpr (MT >= n)                                                                                   \
-      w4a8_pass<MT, GATEUP, EW, NTW, n, RES>(a, src_row, asc, row_route, row_w, As0, As1, As2, As3, stg, m0,   \
+      w4a8_pass<MT, GATEUP, EW, NTW, n, RES>(a, src_row, row_route, row_w, As0, As1, As2, As3, stg, m0,   \
                                              wrsrc, toff0, soff0, nkb, c_begin, c_end);                        \
     break;
     switch (rows / 16) {
@@ -1453,9 +1574,9 @@ __global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int group
 }
 
 struct WsLayout {
-  size_t h_off, o_off, flags_off, bytes;
-  size_t xq_off, xs_off, hs_off;  // W4A8 only (h_off then holds the MXFP8 codes of h)
-  size_t x16_off, xe_off;         // NVFP4 only: x as fp16 and its row exponents
+  size_t h_off, o_off, flags_off, act_off, bytes;
+  size_t xq_off;          // W4A8: E4M3 codes of x (h_off then holds those of h)
+  size_t x16_off, xe_off;  // NVFP4: x as fp16 and its row exponents; W4A4: x's decoded NVFP4 values
   int h_rows;
 };
 
@@ -1468,24 +1589,23 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
   long long rows = R + m * (B - 1);
   rows = (rows + B - 1) / B * B;
   w.h_rows = (int)rows;
-  w.xq_off = w.xs_off = w.hs_off = 0;
+  w.xq_off = 0;
   w.h_off = 0;
   size_t end;
   if (wdtype == SCR_W_MXFP4_A8) {
     w.xq_off = 0;
-    w.xs_off = align256((size_t)T * H);
-    w.h_off = align256(w.xs_off + (size_t)T * (H / 32));
-    w.hs_off = align256(w.h_off + (size_t)rows * I);
-    end = w.hs_off + (size_t)rows * (I / 32);
+    w.h_off = align256((size_t)T * H);
+    end = w.h_off + (size_t)rows * I;
   } else {
     end = w.h_off + (size_t)rows * I * sizeof(uint16_t);
   }
   w.o_off = align256(end);
   const size_t row_bytes = wdtype == SCR_W_BF16 ? sizeof(float) : sizeof(uint16_t);
   w.flags_off = align256(w.o_off + (size_t)R * H * row_bytes);
-  w.bytes = align256(w.flags_off + (size_t)R * sizeof(int32_t));
+  w.act_off = align256(w.flags_off + (size_t)R * sizeof(int32_t));
+  w.bytes = align256(w.act_off + 2 * sizeof(float));
   w.x16_off = w.xe_off = 0;
-  if (wdtype == SCR_W_NVFP4) {
+  if (wdtype == SCR_W_NVFP4 || wdtype == SCR_W_NVFP4_A4) {
     w.x16_off = w.bytes;
     w.xe_off = align256(w.x16_off + (size_t)T * H * sizeof(uint16_t));
     w.bytes = align256(w.xe_off + (size_t)T * sizeof(int32_t));
@@ -1518,7 +1638,7 @@ static int launch_wide_gemms(const GemmArgs& a, int max_active, hipEvent_t* mark
   const int g_gu = a.I / (8 * NTW * kWideWaves);
   const int nch_dn = a.H / (16 * NTW * kWideWaves);
   const int g_dn = nch_dn >= 2 ? nch_dn / 2 : 1;  // two chunks per workgroup
-  if constexpr (WideF16A<WDT, true>::value) {
+  if constexpr (WDT == SCR_W_NVFP4) {
     const int rc = launch_x_to_f16(a, s);
     if (rc) return rc;
   }
@@ -1549,10 +1669,10 @@ static int launch_gemms(const GemmArgs& a, int max_active, hipEvent_t* marks, hi
   return SCR_OK;
 }
 
-// W4A8: the block-scaled kernels for every row count (their 16-row passes
+// W4A8 and W4A4: the wide kernels for every row count (their 16-row passes
 // serve few rows per expert as well); the shape must fit the wide tiling
-static bool w4a8_fits(const GemmArgs& a) {
-  return wide_gemms_fit<SCR_W_MXFP4>(a) && a.H / 32 <= kMxScaleCols && a.I / 32 <= kMxScaleCols;
+static bool act_quant_fits(const GemmArgs& a, int wdtype) {
+  return wdtype == SCR_W_MXFP4_A8 ? wide_gemms_fit<SCR_W_MXFP4>(a) : wide_gemms_fit<SCR_W_NVFP4_A4>(a);
 }
 
 static int launch_w4a8(const GemmArgs& a, int max_active, hipEvent_t* marks, hipStream_t s) {
@@ -1573,16 +1693,6 @@ static int launch_w4a8(const GemmArgs& a, int max_active, hipEvent_t* marks, hip
                        dim3(64 * kWideWaves), 0, s, a, g_dn);
   SCR_CHECK_LAUNCH();
   if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
-  return SCR_OK;
-}
-
-static int launch_mxfp8_quant(const bf16* x, long long rows, int cols, uint8_t* q, uint8_t* sc, hipStream_t s) {
-  const long long nb = rows * (cols / 32);
-  if (nb == 0) return SCR_OK;
-  long long grid = (nb + 255) / 256;
-  if (grid > 8192) grid = 8192;
-  hipLaunchKernelGGL(mxfp8_quant_kernel, dim3((unsigned)grid), dim3(256), 0, s, x, nb, q, sc);
-  SCR_CHECK_LAUNCH();
   return SCR_OK;
 }
 
@@ -1623,7 +1733,7 @@ extern "C" int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_c
   SCR_CHECK_ARG(cfg != nullptr, "tile_config: cfg is null");
   SCR_CHECK_ARG(T >= 0 && k >= 1 && E_layer >= 1, "tile_config: bad T, k or E");
   SCR_CHECK_ARG(wdtype == SCR_W_BF16 || wdtype == SCR_W_NVFP4 || wdtype == SCR_W_FP8 || wdtype == SCR_W_MXFP4 ||
-                    wdtype == SCR_W_MXFP4_A8,
+                    wdtype == SCR_W_MXFP4_A8 || wdtype == SCR_W_NVFP4_A4,
                 "tile_config: unknown wdtype");
   // rows per expert of the routed layer (never of the bank)
   const long long per_expert = ((long long)T * k + E_layer - 1) / E_layer;
@@ -1659,8 +1769,11 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   SCR_CHECK_ARG(I >= 128 && I % 128 == 0 && I <= 16384, "forward: I must be a multiple of 128 in [128, 16384]");
   SCR_CHECK_ARG(view->num_buckets >= 1 && view->bucket_rows && view->input_scale, "forward: bad view");
   SCR_CHECK_ARG(view->wdtype == SCR_W_BF16 || view->wdtype == SCR_W_NVFP4 || view->wdtype == SCR_W_FP8 ||
-                    view->wdtype == SCR_W_MXFP4 || view->wdtype == SCR_W_MXFP4_A8,
+                    view->wdtype == SCR_W_MXFP4 || view->wdtype == SCR_W_MXFP4_A8 || view->wdtype == SCR_W_NVFP4_A4,
                 "forward: unknown wdtype");
+  const bool act_quant = view->wdtype == SCR_W_MXFP4_A8 || view->wdtype == SCR_W_NVFP4_A4;
+  SCR_CHECK_ARG(!act_quant || view->down_input_scale,
+                "forward: the activation-quantising formats need the layer's down input scales");
   SCR_CHECK_ARG(y_dtype == SCR_Y_F32 || y_dtype == SCR_Y_BF16, "forward: unknown y dtype");
   SCR_CHECK_ARG(T >= 0 && (long long)T * k < (1ll << 30) && (long long)T * H < (1ll << 31),
                 "forward: T out of range");
@@ -1691,9 +1804,7 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   uint8_t* wsb = static_cast<uint8_t*>(ws);
   a.h = reinterpret_cast<scr::bf16*>(wsb + wl.h_off);
   a.xq = wsb + wl.xq_off;
-  a.xs = wsb + wl.xs_off;
   a.hq = wsb + wl.h_off;
-  a.hs = wsb + wl.hs_off;
   a.x16 = reinterpret_cast<const uint16_t*>(wsb + wl.x16_off);
   a.xe = reinterpret_cast<const int32_t*>(wsb + wl.xe_off);
   a.o = wsb + wl.o_off;
@@ -1707,18 +1818,27 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   a.h_rows = wl.h_rows;
 
   a.input_scale = view->input_scale;
+  a.down_input_scale = view->down_input_scale;
   a.a_scale_out = a_scale_out;
+  a.act_scale = act_quant ? reinterpret_cast<const float*>(wsb + wl.act_off) : nullptr;
   a.E = E;
   // marks[0] and marks[1] bracket the prologue (the activation quantisation
-  // of W4A8; otherwise empty: the gate/up kernel clears the flags and reports
-  // the activation scale itself)
-  if (view->wdtype == SCR_W_MXFP4_A8 && !scr::w4a8_fits(a)) {
-    scr::set_error("forward: W4A8 needs H a multiple of 512 and I of 512, both at most 4096 (H=%d I=%d)", H, I);
+  // of the A8/A4 formats; otherwise empty: the gate/up kernel clears the
+  // flags and reports the activation scales itself)
+  if (act_quant && !scr::act_quant_fits(a, view->wdtype)) {
+    scr::set_error("forward: W4A8 and W4A4 need H and I multiples of 512 (H=%d I=%d)", H, I);
     return SCR_ENOTSUP;
   }
   if (marks && marks[0]) SCR_CHECK_HIP(hipEventRecord(marks[0], stream));
   if (view->wdtype == SCR_W_MXFP4_A8) {
-    rc = scr::launch_mxfp8_quant(a.x, T, H, wsb + wl.xq_off, wsb + wl.xs_off, stream);
+    rc = scr::launch_act_quant<scr::kActFp8>(a.x, T, H, view->input_scale, view->down_input_scale, E,
+                                             wsb + wl.xq_off, nullptr, nullptr,
+                                             reinterpret_cast<float*>(wsb + wl.act_off), a_scale_out, stream);
+    if (rc) return rc;
+  } else if (view->wdtype == SCR_W_NVFP4_A4) {
+    rc = scr::launch_act_quant<scr::kActNvfp4F16>(a.x, T, H, view->input_scale, view->down_input_scale, E, nullptr,
+                                                  nullptr, reinterpret_cast<uint16_t*>(wsb + wl.x16_off),
+                                                  reinterpret_cast<float*>(wsb + wl.act_off), a_scale_out, stream);
     if (rc) return rc;
   }
   if (marks && marks[1]) SCR_CHECK_HIP(hipEventRecord(marks[1], stream));
@@ -1730,6 +1850,7 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
     case SCR_W_NVFP4: rc = scr::run_gemms<SCR_W_NVFP4>(cfg, a, max_active, marks, stream); break;
     case SCR_W_FP8: rc = scr::run_gemms<SCR_W_FP8>(cfg, a, max_active, marks, stream); break;
     case SCR_W_MXFP4: rc = scr::run_gemms<SCR_W_MXFP4>(cfg, a, max_active, marks, stream); break;
+    case SCR_W_NVFP4_A4: rc = scr::launch_wide_gemms<SCR_W_NVFP4_A4, 7>(a, max_active, marks, stream); break;
     default: rc = scr::launch_w4a8(a, max_active, marks, stream); break;
   }
   if (rc) return rc;
@@ -1746,10 +1867,24 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   return SCR_OK;
 }
 
-extern "C" int scr_quantize_mxfp8(const void* x, long long rows, int cols, uint8_t* codes, uint8_t* scales,
-                                  hipStream_t stream) {
-  SCR_CHECK_ARG(rows >= 0 && cols >= 32 && cols % 32 == 0, "quantize_mxfp8: cols must be a positive multiple of 32");
+extern "C" int scr_quantize_fp8(const void* x, long long rows, int cols, const float* scales, int n_scales,
+                                uint8_t* codes, hipStream_t stream) {
+  SCR_CHECK_ARG(rows >= 0 && cols >= 16 && cols % 16 == 0, "quantize_fp8: cols must be a positive multiple of 16");
+  SCR_CHECK_ARG(n_scales >= 1 && n_scales <= SCR_MAX_EXPERTS, "quantize_fp8: n_scales must be in [1, %d]",
+                SCR_MAX_EXPERTS);
   if (rows == 0) return SCR_OK;
-  SCR_CHECK_ARG(x && codes && scales, "quantize_mxfp8: null pointer");
-  return scr::launch_mxfp8_quant(static_cast<const scr::bf16*>(x), rows, cols, codes, scales, stream);
+  SCR_CHECK_ARG(x && codes && scales, "quantize_fp8: null pointer");
+  return scr::launch_act_quant<scr::kActFp8>(static_cast<const scr::bf16*>(x), rows, cols, scales, nullptr, n_scales,
+                                             codes, nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+extern "C" int scr_quantize_nvfp4(const void* x, long long rows, int cols, const float* scales, int n_scales,
+                                  uint8_t* codes, uint8_t* block_scales, hipStream_t stream) {
+  SCR_CHECK_ARG(rows >= 0 && cols >= 16 && cols % 16 == 0, "quantize_nvfp4: cols must be a positive multiple of 16");
+  SCR_CHECK_ARG(n_scales >= 1 && n_scales <= SCR_MAX_EXPERTS, "quantize_nvfp4: n_scales must be in [1, %d]",
+                SCR_MAX_EXPERTS);
+  if (rows == 0) return SCR_OK;
+  SCR_CHECK_ARG(x && codes && block_scales && scales, "quantize_nvfp4: null pointer");
+  return scr::launch_act_quant<scr::kActNvfp4>(static_cast<const scr::bf16*>(x), rows, cols, scales, nullptr,
+                                               n_scales, codes, block_scales, nullptr, nullptr, nullptr, stream);
 }

@@ -235,7 +235,7 @@ class LayerBuffers:
             "align_ws": torch.empty(L.align_workspace(R, self.num_buckets), dtype=torch.uint8, device=_DEV),
             "moe_ws": torch.empty(L.moe_workspace(self.T, self.k, self.E, self.H, self.I, self.cfg),
                                   dtype=torch.uint8, device=_DEV),
-            "a_scale": torch.zeros(1, dtype=torch.float32, device=_DEV),
+            "a_scale": torch.zeros(2, dtype=torch.float32, device=_DEV),
             "y": torch.empty((self.T, self.H), dtype=torch.float32 if self.y_dtype == L.SCR_Y_F32 else torch.bfloat16,
                              device=_DEV),
         }
@@ -245,8 +245,14 @@ class LayerBuffers:
         return self.t[k]
 
 
-def make_view(layer, E, k, H, I, wdtype, num_buckets, bucket_rows: torch.Tensor, input_scale: torch.Tensor):
-    return L.RoutedExperts(layer, E, k, H, I, wdtype, num_buckets, bucket_rows.data_ptr(), input_scale.data_ptr())
+def make_view(layer, E, k, H, I, wdtype, num_buckets, bucket_rows: torch.Tensor, input_scale: torch.Tensor,
+              down_input_scale: torch.Tensor | None = None):
+    """The routed layer's view: bucket rows plus the layer's per-expert input
+    scales (gate/up input, and down input for the activation-quantising
+    formats; by default the same array serves both)."""
+    ds = input_scale if down_input_scale is None else down_input_scale
+    return L.RoutedExperts(layer, E, k, H, I, wdtype, num_buckets, bucket_rows.data_ptr(), input_scale.data_ptr(),
+                           ds.data_ptr())
 
 
 # ------------------------------------------------------------------ steps
@@ -313,7 +319,7 @@ def forward(buf: LayerBuffers, view: L.RoutedExperts, x: torch.Tensor, stream=No
 
 def demand_layer(bank: Bank, pool: HostPool, layer: int, logits, x, input_scale, width=128, record_stats=False,
                  y_dtype=L.SCR_Y_F32, buf: LayerBuffers | None = None, stream=None, shape=None, batched=False,
-                 fused=False):
+                 fused=False, down_input_scale=None):
     """Demand (slot) path of one layer: route, dedup, per-query ensure + miss copy,
     align over the bank's slots through key_to_slot, grouped GEMM at the slots.
     fused=True plans the chunk (dedup, queries, align) in one launch when it fits."""
@@ -332,7 +338,7 @@ def demand_layer(bank: Bank, pool: HostPool, layer: int, logits, x, input_scale,
         route_dedup(buf, logits, stream)
         admit(buf, bank, pool, layer, record_stats, stream, batched=batched)
         align(buf, bank.key_to_slot.data_ptr() + layer * E * 4, E, stream)
-    view = make_view(layer, E, k, H, I, bank.wdtype, bank.S, bank.row_table, input_scale)
+    view = make_view(layer, E, k, H, I, bank.wdtype, bank.S, bank.row_table, input_scale, down_input_scale)
     buf.cfg_used = forward(buf, view, x, stream)
     return buf
 
@@ -385,7 +391,8 @@ class LayerStreamBuffer:
 
 
 def stream_layer(pool: HostPool, layer: int, logits, x, input_scale, layer_buf: LayerStreamBuffer, wdtype,
-                 y_dtype=L.SCR_Y_F32, buf: LayerBuffers | None = None, stream=None, shape=None, copy=True):
+                 y_dtype=L.SCR_Y_F32, buf: LayerBuffers | None = None, stream=None, shape=None, copy=True,
+                 down_input_scale=None):
     """Whole-layer path: copy every expert of the layer, align over its experts,
     same grouped GEMM."""
     T, E = logits.shape
@@ -397,7 +404,7 @@ def stream_layer(pool: HostPool, layer: int, logits, x, input_scale, layer_buf: 
     if copy:
         L.stream_layer_async(pool.desc, layer, layer_buf.data, s)
     align(buf, None, 0, stream)
-    view = make_view(layer, E, k, H, I, wdtype, E, layer_buf.row_table, input_scale)
+    view = make_view(layer, E, k, H, I, wdtype, E, layer_buf.row_table, input_scale, down_input_scale)
     buf.cfg_used = forward(buf, view, x, stream)
     return buf
 

@@ -30,6 +30,8 @@ class ExpertSource:
     """Generator-side expert weights of one workload, by payload id."""
 
     def __init__(self, seed, H, I, wdtype):
+        # the activation-quantising formats read the records of their weight format
+        wdtype = {"mxfp4_a8": "mxfp4", "nvfp4_a4": "nvfp4"}.get(wdtype, wdtype)
         self.seed, self.H, self.I, self.wdtype = seed, H, I, wdtype
         self._cache = {}
 
@@ -38,7 +40,7 @@ class ExpertSource:
             return W.expert_nvfp4(self.seed, payload, self.H, self.I)
         if self.wdtype == "fp8":
             return W.expert_fp8(self.seed, payload, self.H, self.I)
-        if self.wdtype in ("mxfp4", "mxfp4_a8"):
+        if self.wdtype == "mxfp4":
             return W.expert_mxfp4(self.seed, payload, self.H, self.I)
         if self.wdtype == "fp32":
             w13, w2 = W.expert_f32(self.seed, payload, self.H, self.I)
@@ -54,7 +56,7 @@ class ExpertSource:
             out = (dequant_nvfp4(r["w13_q"], r["w13_s"], r["g13"]), dequant_nvfp4(r["w2_q"], r["w2_s"], r["g2"]))
         elif self.wdtype == "fp8":
             out = (dequant_fp8(r["w13_q"], r["g13"]), dequant_fp8(r["w2_q"], r["g2"]))
-        elif self.wdtype in ("mxfp4", "mxfp4_a8"):
+        elif self.wdtype == "mxfp4":
             out = (dequant_mxfp4(r["w13_q"], r["w13_s"]), dequant_mxfp4(r["w2_q"], r["w2_s"]))
         else:
             out = (bf16_bits_to_f64(r[0]), bf16_bits_to_f64(r[1]))
@@ -75,7 +77,7 @@ def fill_pool(pool, src: ExpertSource, lay, payloads):
             rec = LY.pack_record_nvfp4(lay, r)
         elif src.wdtype == "fp8":
             rec = LY.pack_record_fp8(lay, r)
-        elif src.wdtype in ("mxfp4", "mxfp4_a8"):
+        elif src.wdtype == "mxfp4":
             rec = LY.pack_record_mxfp4(lay, r)
         else:
             rec = LY.pack_record_bf16(lay, r[0], r[1])
@@ -88,7 +90,7 @@ def fill_pool(pool, src: ExpertSource, lay, payloads):
 def wdtype_code(wd):
     import slot_cache_routed_amd._lib as L
     return {"nvfp4": L.SCR_W_NVFP4, "fp8": L.SCR_W_FP8, "mxfp4": L.SCR_W_MXFP4,
-            "mxfp4_a8": L.SCR_W_MXFP4_A8}.get(wd, L.SCR_W_BF16)
+            "mxfp4_a8": L.SCR_W_MXFP4_A8, "nvfp4_a4": L.SCR_W_NVFP4_A4}.get(wd, L.SCR_W_BF16)
 
 
 def rms(a):
