@@ -127,7 +127,13 @@ def _ws(mode, buf, T, H, I):
     return x16, h
 
 
-def _check_layer(mode, env, T, E, k, H, I, sc, sc2):
+def _check_layer(mode, env, T, E, k, H, I, sc, sc2, end_to_end=True):
+    """end_to_end=False: y is asserted against the oracle with the device's
+    side of the near-tie h decisions only (each one checked valid above); the
+    plain oracle distance is reported.  At millions of h values a few land
+    within the GEMM's fp32 rounding of an e2m1 decision point, and one such
+    flip moves an output element by up to about a third of its block's
+    magnitude through W2."""
     d = env["d"]
     src = env["src"]
     y = d["y"].float().cpu().numpy()
@@ -207,7 +213,8 @@ def _check_layer(mode, env, T, E, k, H, I, sc, sc2):
     err, err_dn = rel_max_err(y, y_ref), rel_max_err(y, y_dn)
     flush(f"{mode} {T}x{E}: rel max err vs the oracle = {err:.3e}, with the device's near-tie h = {err_dn:.3e}")
     assert err_dn <= TOL_FP4
-    assert err <= TOL_FP4
+    if end_to_end:
+        assert err <= TOL_FP4
     assert torch.equal(d["y"], env["st"]["y"]), "slot path equals the whole-layer path bit for bit"
     return y, y_ref
 

@@ -9,7 +9,7 @@ import torch
 
 import workloads as W
 from helpers import ExpertSource, fill_pool, flush, rel_max_err, wdtype_code
-from oracle import moe_layer, moe_layer_tokens, moe_layer_w4a4, moe_layer_w4a8, route_topk_softmax
+from oracle import moe_layer, moe_layer_tokens, route_topk_softmax
 from oracle.mlp import bf16_bits_to_f64
 
 pytestmark = pytest.mark.gpu
@@ -405,12 +405,19 @@ def test_full_size_4096_token_layer_in_every_weight_format(wd):
     x = bf16_bits_to_f64(xb)
     wf = lambda e: src.f64(e % P)
     flush(f"full-size layer {wd}: oracle over all {T} tokens")
-    if wd == "mxfp4_a8":
-        y_ref = moe_layer_w4a8(x, ids, w, wf, sc_h, sc_h)
-    elif wd == "nvfp4_a4":
-        y_ref = moe_layer_w4a4(x, ids, w, wf, sc_h, sc_h)
-    else:
-        y_ref = moe_layer(x, ids, w, wf)
+    if wd in ("mxfp4_a8", "nvfp4_a4"):
+        # x's codes bit-exact, every h value valid, y against the oracle with
+        # the device's side of the near-tie h decisions (the plain distance,
+        # which a handful of those flips among 21M h values dominates, is
+        # reported)
+        import test_gpu_actquant as A
+
+        class _Src:
+            f64 = staticmethod(wf)
+        A._check_layer("w4a8" if wd == "mxfp4_a8" else "w4a4", dict(src=_Src, lg=lg, xb=xb, d=d, st=st),
+                       T, E, k, H, I, sc_h, sc_h, end_to_end=False)
+        return
+    y_ref = moe_layer(x, ids, w, wf)
     err = rel_max_err(_y(d), y_ref)
     flush(f"full-size layer {wd}: rel max err over every element = {err:.3e}")
     assert err <= (TOL_BF16 if wd == "bf16" else TOL_FP4)
