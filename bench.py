@@ -16,7 +16,9 @@ timed region holds no PCIe transfer.  The timed steps are replays of the
 step captured once as a HIP graph (checked bitwise against the eager step);
 the eager step's times are reported beside it.  The cold step (bank reset to
 its pre-filled state, 160 misses copied from pinned host memory) is reported
-under "cold".
+as "layer_ms_cold" (PCIe-inclusive, never `value`), and the warm replay timed
+one step at a time after a 512 MB write that flushes the memory-side cache as
+"layer_ms_mall_flushed_median".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Prints one JSON line.
@@ -54,7 +56,11 @@ def _args():
     p.add_argument("--long-layers", type=int, default=8)
     p.add_argument("--long-reps", type=int, default=3)
     p.add_argument("--no-decode", action="store_true", help="skip the decode-stream measurement")
-    p.add_argument("--decode-steps", type=int, default=48)
+    p.add_argument("--decode-steps", type=int, default=256)
+    p.add_argument("--decode-warm-steps", type=int, default=32,
+                   help="decode steps counted as the cold start (the rest is the steady state)")
+    p.add_argument("--decode-side-steps", type=int, default=64,
+                   help="steps of the graph-replayed and LRFU decode passes")
     p.add_argument("--no-align", action="store_true", help="skip the align measurements")
     p.add_argument("--no-formats", action="store_true",
                    help="skip the 4096-token grouped GEMM in every weight format (bf16, NVFP4, FP8, MXFP4)")
@@ -202,6 +208,7 @@ def main():
     # the same warm step captured once as a HIP graph and replayed (the path
     # holds no host sync, so the whole step is capturable)
     graph_ms = None
+    flushed_ms = None
     try:
         y_eager = buf["y"].clone()
         side = torch.cuda.Stream()
@@ -220,7 +227,20 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
-        del g
+        # the same replays one at a time, each after a 512 MB write that flushes
+        # the 256 MB memory-side cache, timed by events around the replay alone
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        fl = []
+        for i in range(args.steps + 5):
+            flush_buf.fill_(i & 0xFF)
+            t_a, t_b = L.Timer(), L.Timer()
+            t_a.record(s)
+            g.replay()
+            t_b.record(s)
+            if i >= 5:
+                fl.append(t_a.elapsed_ms(t_b))
+        flushed_ms = statistics.median(fl)
+        del g, flush_buf
     except Exception as e:  # capture is an extra measurement; report why it is missing
         graph_ms = f"unavailable: {type(e).__name__}: {e}"
     gu_ms = [m[1].elapsed_ms(m[2]) for m in marks]
@@ -267,6 +287,8 @@ def main():
                    "distinct": n_active, "query_width": Wd},
         "step_mode": step_mode,
         "layer_ms": round(step_ms, 4),
+        "layer_ms_cold": round(cold_ms, 3),
+        "layer_ms_mall_flushed_median": None if flushed_ms is None else round(flushed_ms, 4),
         "ms_per_step_eager_with_timing_events": round(ms_per_step, 4),
         "ms_per_step_eager": round(ms_no_events, 4),
         "ms_per_step_hip_graph": graph_ms if not isinstance(graph_ms, float) else round(graph_ms, 4),
@@ -455,19 +477,22 @@ def formats_4096() -> dict:
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     lg = dev(W.logits_normal(cfg.seed, 0, T, E))
     x = dev(W.f32_to_bf16_bits(W.activations_normal(cfg.seed, T, H)).view(np.int16))
-    sc = dev(np.ones(E, np.float32))
+    sc = dev(W.c3_input_scales(E))        # the layer's input scales (2.0 / 3.0; used by W4A8 and W4A4)
     s = torch.cuda.current_stream().cuda_stream
     fmts = (("bf16", L.SCR_W_BF16, lambda lay, p: LY.pack_record_bf16(lay, *W.expert_bf16(cfg.seed, p, H, I))),
             ("nvfp4", L.SCR_W_NVFP4, lambda lay, p: LY.pack_record_nvfp4(lay, W.expert_nvfp4(cfg.seed, p, H, I))),
             ("fp8", L.SCR_W_FP8, lambda lay, p: LY.pack_record_fp8(lay, W.expert_fp8(cfg.seed, p, H, I))),
             ("mxfp4", L.SCR_W_MXFP4, lambda lay, p: LY.pack_record_mxfp4(lay, W.expert_mxfp4(cfg.seed, p, H, I))),
             ("mxfp4_w4a8", L.SCR_W_MXFP4_A8,
-             lambda lay, p: LY.pack_record_mxfp4(lay, W.expert_mxfp4(cfg.seed, p, H, I))))
+             lambda lay, p: LY.pack_record_mxfp4(lay, W.expert_mxfp4(cfg.seed, p, H, I))),
+            ("nvfp4_w4a4", L.SCR_W_NVFP4_A4,
+             lambda lay, p: LY.pack_record_nvfp4(lay, W.expert_nvfp4(cfg.seed, p, H, I))))
     out = {"workload": "4096 tokens, 512 experts resident, top-10, hidden 2048, intermediate 512; "
                        "TFLOP/s = 6*R*H*I / (gate/up + down); nvfp4's gate/up time includes its fp16 copy of x; "
-                       "mxfp4_w4a8 quantises the activations to MXFP8 (activation_quant_us, added to its GEMM time) "
-                       "and runs the fp8 x fp4 block-scaled MFMA, whose dense peak is 5 PFLOP/s "
-                       "(frac_bf16_mfma_peak stays against 2.5)"}
+                       "mxfp4_w4a8 quantises x to FP8 E4M3 under the layer's max input scale (activation_quant_us, "
+                       "added to its GEMM time) and runs the fp8 x fp4 block-scaled MFMA, whose dense peak is 5 "
+                       "PFLOP/s; nvfp4_w4a4 quantises x to NVFP4 under the same scale (also added) and runs the fp16 "
+                       "MFMA on the exact decoded operands (frac_bf16_mfma_peak stays against 2.5)"}
     flops = 6.0 * R * H * I
     for name, code, pack in fmts:
         lay = LY.record_layout(code, H, I)
@@ -492,10 +517,10 @@ def formats_4096() -> dict:
                 gus.append(tm[1].elapsed_ms(tm[2]))
                 dns.append(tm[2].elapsed_ms(tm[3]))
         gu, dn, q = statistics.mean(gus), statistics.mean(dns), statistics.mean(qs)
-        # W4A8's activation quantisation is part of its GEMM work; the other
-        # formats have nothing between marks 0 and 1 (NVFP4's fp16 copy of x
+        # W4A8's and W4A4's activation quantisation is part of their GEMM work;
+        # the other formats have nothing between marks 0 and 1 (NVFP4's fp16 copy of x
         # is inside its gate/up time)
-        t = gu + dn + (q if code == L.SCR_W_MXFP4_A8 else 0.0)
+        t = gu + dn + (q if code in (L.SCR_W_MXFP4_A8, L.SCR_W_NVFP4_A4) else 0.0)
         wbytes = E * rec
         out[name] = {"gate_up_us": round(gu * 1e3, 1), "down_us": round(dn * 1e3, 1),
                      "activation_quant_us": round(q * 1e3, 1),
@@ -510,8 +535,9 @@ def formats_4096() -> dict:
 
 def decode_stream(args) -> dict:
     """48 layers x 512 experts (bf16) over a 1650-slot bank, 4-token steps with
-    Zipf(1.1) routing, decode statistics on, from an empty bank.  Keys alias
-    512 host records (bounded pinned memory)."""
+    Zipf(1.1) routing, decode statistics on, from an empty bank: 256 steps, the
+    first 32 reported as the cold start and the rest as the steady state.  Keys
+    alias 512 host records (bounded pinned memory)."""
     import numpy as np
     import torch
     from concurrent.futures import ThreadPoolExecutor
@@ -533,60 +559,96 @@ def decode_stream(args) -> dict:
 
     with ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
         list(ex.map(one, range(P)))
-    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     steps = args.decode_steps
-    logits = [[dev(W.zipf_gumbel_logits(cfg.seed, l, st, T, E)) for l in range(NL)] for st in range(steps)]
-    xs = [[dev(W.f32_to_bf16_bits(W.decode_activations(cfg.seed, l, st, T, H)).view(np.int16)) for l in range(NL)]
-          for st in range(steps)]
-    sc = dev(np.ones(E, np.float32))
+    warm = min(args.decode_warm_steps, steps - 1)
+    side = min(args.decode_side_steps, steps)
+    t0 = time.time()
+
+    def step_inputs(st):
+        lg = np.stack([W.zipf_gumbel_logits(cfg.seed, l, st, T, E) for l in range(NL)])
+        xs = np.stack([W.f32_to_bf16_bits(W.decode_activations(cfg.seed, l, st, T, H)) for l in range(NL)])
+        return lg, xs
+
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
+        host = list(ex.map(step_inputs, range(steps)))
+    logits = torch.from_numpy(np.stack([h[0] for h in host])).cuda()                 # [steps, NL, T, E]
+    xs = torch.from_numpy(np.stack([h[1] for h in host]).view(np.int16)).cuda()     # [steps, NL, T, H]
+    del host
+    _log(f"decode: inputs of {steps} steps ready in {time.time() - t0:.1f}s")
+    sc = torch.ones(E, dtype=torch.float32, device="cuda")
     bank = LY.Bank(S, NL, E, L.SCR_W_BF16, rec)
     buf = LY.LayerBuffers(T, E, k, H, I, S, L.SCR_W_BF16, width=128, y_dtype=L.SCR_Y_BF16)
     s = torch.cuda.current_stream().cuda_stream
+    # every step timed on the stream; the statistics read after each step
+    marks = [L.Timer() for _ in range(steps + 1)]
+    per_step_stats = []
+    torch.cuda.synchronize()
+    marks[0].record(s)
+    for st in range(steps):
+        for l in range(NL):
+            LY.demand_layer(bank, pool, l, logits[st, l], xs[st, l], sc, width=128, record_stats=True, buf=buf,
+                            batched=True, shape=(k, H, I))
+        marks[st + 1].record(s)
+        per_step_stats.append(bank.stats.clone())
+    torch.cuda.synchronize()
+    step_ms = [marks[i].elapsed_ms(marks[i + 1]) for i in range(steps)]
+    stats = torch.stack(per_step_stats).cpu().numpy().astype(np.int64)               # cumulative [steps, 4]
+    snap = bank.snapshot()
+    hits, misses, evictions, queries = [int(v) for v in snap["stats"]]
+
+    def window(a, b):
+        d = stats[b - 1] - (stats[a - 1] if a > 0 else 0)
+        h, m, ev = int(d[0]), int(d[1]), int(d[2])
+        ms = float(np.sum(step_ms[a:b]))
+        return {"steps": b - a, "step_ms": round(ms / (b - a), 3), "step_ms_median": round(float(np.median(step_ms[a:b])), 3),
+                "hit_rate": round(h / max(1, h + m), 4), "misses_per_step": round(m / (b - a), 1),
+                "evictions_per_step": round(ev / (b - a), 1),
+                "miss_copy_GBps_effective": round(m * rec / (ms * 1e-3) / 1e9, 2)}
+    del bank, buf
+    torch.cuda.empty_cache()
+    # the first `side` steps from an empty bank, each step one replay of a graph
+    # holding every layer (inputs copied into the graph's static tensors first);
+    # the bank state must equal that of the eager steps at the same point
+    bank_e = LY.Bank(S, NL, E, L.SCR_W_BF16, rec)
+    buf = LY.LayerBuffers(T, E, k, H, I, S, L.SCR_W_BF16, width=128, y_dtype=L.SCR_Y_BF16)
+    for st in range(side):
+        for l in range(NL):
+            LY.demand_layer(bank_e, pool, l, logits[st, l], xs[st, l], sc, width=128, record_stats=True, buf=buf,
+                            batched=True, shape=(k, H, I))
+    snap_e = bank_e.snapshot()
+    del bank_e, buf
+    torch.cuda.empty_cache()
+    bank_g = LY.Bank(S, NL, E, L.SCR_W_BF16, rec)
+    graph = LY.DecodeStepGraph(bank_g, pool, range(NL), T, E, (k, H, I), sc, width=128, record_stats=True,
+                               y_dtype=L.SCR_Y_BF16)
     t_a, t_b = L.Timer(), L.Timer()
     torch.cuda.synchronize()
     t_a.record(s)
-    for st in range(steps):
-        for l in range(NL):
-            LY.demand_layer(bank, pool, l, logits[st][l], xs[st][l], sc, width=128, record_stats=True, buf=buf, batched=True,
-                            shape=(k, H, I))
-    t_b.record(s)
-    total = t_a.elapsed_ms(t_b)
-    snap = bank.snapshot()
-    hits, misses, evictions, queries = [int(v) for v in snap["stats"]]
-    del bank, buf
-    torch.cuda.empty_cache()
-    # the same steps from an empty bank, each step one replay of a graph holding
-    # every layer (inputs copied into the graph's static tensors first)
-    bank_g = LY.Bank(S, NL, E, L.SCR_W_BF16, rec)
-    step = LY.DecodeStepGraph(bank_g, pool, range(NL), T, E, (k, H, I), sc, width=128, record_stats=True,
-                              y_dtype=L.SCR_Y_BF16)
-    torch.cuda.synchronize()
-    t_a.record(s)
-    for st in range(steps):
-        for l in range(NL):
-            step.logits[l].copy_(logits[st][l])
-            step.x[l].copy_(xs[st][l])
-        step.replay()
+    for st in range(side):
+        graph.logits.copy_(logits[st])
+        graph.x.copy_(xs[st])
+        graph.replay()
     t_b.record(s)
     total_g = t_a.elapsed_ms(t_b)
     snap_g = bank_g.snapshot()
-    del step
+    del graph
     torch.cuda.empty_cache()
-    # the same steps under scored (LRFU) eviction, half-life 16 queries
+    # the same first steps under scored (LRFU) eviction, half-life 16 queries
     lrfu_decay = int(2 ** 32 * 2 ** (-1.0 / 16))
     bank_f = LY.Bank(S, NL, E, L.SCR_W_BF16, rec, policy=L.SCR_POLICY_LRFU, lrfu_decay=lrfu_decay)
     buf = LY.LayerBuffers(T, E, k, H, I, S, L.SCR_W_BF16, width=128, y_dtype=L.SCR_Y_BF16)
     torch.cuda.synchronize()
     t_a.record(s)
-    for st in range(steps):
+    for st in range(side):
         for l in range(NL):
-            LY.demand_layer(bank_f, pool, l, logits[st][l], xs[st][l], sc, width=128, record_stats=True, buf=buf,
+            LY.demand_layer(bank_f, pool, l, logits[st, l], xs[st, l], sc, width=128, record_stats=True, buf=buf,
                             batched=True, shape=(k, H, I))
     t_b.record(s)
     total_f = t_a.elapsed_ms(t_b)
     hf, mf = [int(v) for v in bank_f.snapshot()["stats"][:2]]
-    same = all(np.array_equal(np.asarray(snap[key]), np.asarray(snap_g[key]))
+    same = all(np.array_equal(np.asarray(snap_e[key]), np.asarray(snap_g[key]))
                for key in ("slot_key", "key_to_slot", "slot_stamp", "stats", "decode_freq", "clock"))
+    total = float(np.sum(step_ms))
     return {
         "workload": f"decode_stream: {NL} layers x {E} experts, top-{k}, bf16, {S}-slot bank, {steps} steps of {T} "
                     f"tokens, Zipf(1.1) routing, from an empty bank",
@@ -595,12 +657,16 @@ def decode_stream(args) -> dict:
         "hit_rate": round(hits / max(1, hits + misses), 4),
         "misses": misses, "evictions": evictions, "queries": queries,
         "miss_copy_GBps_effective": round(misses * rec / (total * 1e-3) / 1e9, 2),
-        "step_ms_hip_graph": round(total_g / steps, 3),
+        "cold_start": window(0, warm),
+        "steady_state": window(warm, steps),
+        "step_ms_hip_graph": round(total_g / side, 3),
+        "hip_graph_steps": side,
         "hip_graph_bank_identical": bool(same),
-        "lrfu_half_life_16": {"step_ms": round(total_f / steps, 3), "hit_rate": round(hf / max(1, hf + mf), 4),
-                              "misses": mf},
-        "note": "wall time of all layer-steps on the compute stream, PCIe-inclusive; step_ms_hip_graph replays "
-                "one graph per step holding every layer, from an empty bank, inputs copied in before each replay",
+        f"lrfu_half_life_16_first_{side}_steps": {"step_ms": round(total_f / side, 3),
+                                                  "hit_rate": round(hf / max(1, hf + mf), 4), "misses": mf},
+        "note": "per-step times by stream events, PCIe-inclusive (misses are copied from pinned host memory); "
+                "cold_start = the first steps from an empty bank, steady_state = the rest; step_ms_hip_graph "
+                "replays one graph per step holding every layer, inputs copied in before each replay",
     }
 
 
@@ -708,11 +774,25 @@ def cpu_baseline(budget_s: float) -> dict:
                               "ms_per_chunk": round(s1 / p1 * 1e3, 1)}
     except ImportError:
         out["single_core"] = None
+    out["nproc"] = os.cpu_count()
     try:
-        with open("/proc/cpuinfo") as f:
-            out["cpu_model"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
-    except OSError:
-        out["cpu_model"] = None
+        out["cpus_usable"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        out["cpus_usable"] = None
+    out["cpu_model"] = None
+    try:
+        import subprocess
+        r = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10)
+        out["cpu_model"] = next((l.split(":", 1)[1].strip() for l in r.stdout.splitlines()
+                                 if l.strip().startswith("Model name")), None)
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if not out["cpu_model"]:
+        try:
+            with open("/proc/cpuinfo") as f:
+                out["cpu_model"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+        except OSError:
+            pass
     return out
 
 

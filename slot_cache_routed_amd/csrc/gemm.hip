@@ -175,13 +175,34 @@ struct GemmArgs {
   int T, k, R, H, I, B, h_rows, E;
 };
 
-// max of n layer scales over one wave (every lane gets it; -inf for n = 0)
-__device__ __forceinline__ float wave_scale_max(const float* s, int n, int lane) {
-  float m = -INFINITY;
-  for (int e = lane; e < n; e += 64) m = fmaxf(m, s[e]);
+// maxima of the layer's two scale arrays (n >= 1 each; s2 may be null, its
+// maximum then 0) over one wave, every lane getting them.  Loads go out in
+// rounds of 8 per lane per array, clamped to the last entry (a repeat cannot
+// change a maximum), so a round costs one memory latency.
+__device__ __forceinline__ void wave_scale_max2(const float* s1, const float* s2, int n, int lane, float& m1,
+                                                float& m2) {
+  float a = -INFINITY, b = s2 ? -INFINITY : 0.0f;
+  for (int e0 = 0; e0 < n; e0 += 64 * 8) {
+    float v[8], w[8];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  return m;
+    for (int u = 0; u < 8; ++u) {
+      const int e = min(e0 + 64 * u + lane, n - 1);
+      v[u] = s1[e];
+      w[u] = s2 ? s2[e] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a = fmaxf(a, v[u]);
+      b = fmaxf(b, w[u]);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    a = fmaxf(a, __shfl_xor(a, off, 64));
+    b = fmaxf(b, __shfl_xor(b, off, 64));
+  }
+  m1 = a;
+  m2 = b;
 }
 
 // Work that must precede the down GEMM, done by the gate/up workgroups before
@@ -193,8 +214,8 @@ __device__ __forceinline__ void gateup_prologue(const GemmArgs& a) {
   const int nthreads = gridDim.x * blockDim.x;
   for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < a.R; r += nthreads) a.flags[r] = 0;
   if (a.a_scale_out && !a.act_scale && blockIdx.x == 0 && threadIdx.x < 64) {
-    const float m1 = wave_scale_max(a.input_scale, a.E, threadIdx.x);
-    const float m2 = a.down_input_scale ? wave_scale_max(a.down_input_scale, a.E, threadIdx.x) : 0.0f;
+    float m1, m2;
+    wave_scale_max2(a.input_scale, a.down_input_scale, a.E, threadIdx.x, m1, m2);
     if (threadIdx.x == 0) {
       a.a_scale_out[0] = m1;
       a.a_scale_out[1] = m2;
@@ -864,21 +885,45 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
         uint16_t* sh16 = reinterpret_cast<uint16_t*>(sh);
         if constexpr (WDT == SCR_W_NVFP4_A4) {
           // W4A4: h quantised to NVFP4 under the layer's down scale a2, per
-          // row and 16 columns (one gate tile t: its 16 columns sit in the 16
-          // lanes of a row group), stored as the exact fp16 value e2m1 * block
-          // for the down GEMM's fp16 operand (a2 goes to its accumulators)
-          const float a2 = a.act_scale[1];
+          // row and 16 columns.  The wave's 16 x HC block of h goes through
+          // its LDS tile as fp32; lane l < 2 * 16 then owns row l / 2,
+          // columns 16 (l % 2) .. + 15 (one NVFP4 block), and writes them as
+          // the exact fp16 values e2m1 * block (the down GEMM's fp16 operand;
+          // a2 goes to its accumulators)
+          static_assert(HC == 32, "one wave's h row holds two NVFP4 blocks");
+          float* shf = reinterpret_cast<float*>(wst);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int t = 0; t < NTW / 2; ++t) {
-              const float hv = silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]);
-              float m = fabsf(hv);
+            for (int t = 0; t < NTW / 2; ++t)
+              shf[(grp * 4 + i) * HC + 16 * t + col] = silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]);
+          if (lane < 32) {
+            // the block's largest magnitude, then its values again in two
+            // halves of 8 (few registers live beside the accumulators)
+            const float a2 = a.act_scale[1];
+            const float4* src = reinterpret_cast<const float4*>(shf + (lane >> 1) * HC + 16 * (lane & 1));
+            float amax = 0.0f;
 #pragma unroll
-              for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
-              const float bv = __builtin_amdgcn_cvt_f32_fp8((int)nvfp4_block_code(m, a2), 0);
-              sh16[(grp * 4 + i) * HC + 16 * t + col] = nvfp4_elem_f16(nvfp4_elem_code(hv, bv, a2), bv);
+            for (int c = 0; c < 4; ++c) {
+              const float4 q = src[c];
+              amax = fmaxf(fmaxf(amax, fmaxf(fabsf(q.x), fabsf(q.y))), fmaxf(fabsf(q.z), fabsf(q.w)));
             }
+            const float bv = __builtin_amdgcn_cvt_f32_fp8((int)nvfp4_block_code(amax, a2), 0);
+            const int pos = m0 + mt * 16 + (lane >> 1);
+            const int hc = ch * (HC * EW) + wave * HC + 16 * (lane & 1);
+            u32x4* dst = reinterpret_cast<u32x4*>(a.h + (size_t)pos * a.I + hc);
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const float4 q0 = src[2 * half], q1 = src[2 * half + 1];
+              const float v[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+              u32x4 out;
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                out[c] = (unsigned)nvfp4_elem_f16(nvfp4_elem_code(v[2 * c], bv, a2), bv) |
+                         ((unsigned)nvfp4_elem_f16(nvfp4_elem_code(v[2 * c + 1], bv, a2), bv) << 16);
+              dst[half] = out;
+            }
+          }
         } else {
 #pragma unroll
           for (int i = 0; i < 4; i += 2)
@@ -899,14 +944,16 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
               sh16[(grp * 4 + i + 1) * HC + 16 * t + col] = (uint16_t)(p >> 16);
             }
         }
+        if constexpr (WDT != SCR_W_NVFP4_A4) {
 #pragma unroll
-        for (int rd = 0; rd < ROUNDS; ++rd) {
-          const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
-          if (q < 16 * PPR) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(sh + rr * HC + pc * 8);
-            const int pos = m0 + mt * 16 + rr;
-            const int hc = ch * (HC * EW) + wave * HC + pc * 8;
-            *reinterpret_cast<u32x4*>(a.h + (size_t)pos * a.I + hc) = v;
+          for (int rd = 0; rd < ROUNDS; ++rd) {
+            const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
+            if (q < 16 * PPR) {
+              const u32x4 v = *reinterpret_cast<const u32x4*>(sh + rr * HC + pc * 8);
+              const int pos = m0 + mt * 16 + rr;
+              const int hc = ch * (HC * EW) + wave * HC + pc * 8;
+              *reinterpret_cast<u32x4*>(a.h + (size_t)pos * a.I + hc) = v;
+            }
           }
         }
       }
@@ -1217,8 +1264,8 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const bf16* __restrict__
                                                         float* __restrict__ act_scale, float* __restrict__ a_out) {
   __shared__ float sm;
   if (threadIdx.x < 64) {
-    const float m1 = wave_scale_max(s1, n_scales, threadIdx.x);
-    const float m2 = s2 ? wave_scale_max(s2, n_scales, threadIdx.x) : 0.0f;
+    float m1, m2;
+    wave_scale_max2(s1, s2, n_scales, threadIdx.x, m1, m2);
     if (threadIdx.x == 0) {
       sm = m1;
       if (blockIdx.x == 0) {
