@@ -333,6 +333,21 @@ int scr_align_blocks(const int32_t* ids, int n, const int32_t* id_to_bucket, int
                      int32_t* block_bucket, int32_t* n_post_pad, int32_t* active_buckets,
                      int32_t* active_block_begin, int32_t* n_active, void* ws, size_t ws_bytes,
                      hipStream_t stream);
+/* align_blocks_noalloc: for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  scr_align_blocks with the same arguments except the
+ * workspace, and the same outputs.  Its scratch is a file-scope device array
+ * of the library, 4,325,632 bytes on each GPU it runs on, held until the
+ * process ends; the call allocates nothing.  All calls on one GPU share that
+ * GPU's array, so calls that overlap on one GPU (several streams or threads)
+ * race: the caller serialises them.  Every scratch entry a call reads is
+ * written earlier in the same call, so nothing carries over between calls.
+ * SCR_ECAPACITY if a shape needs more scratch than the array holds (none
+ * with num_buckets <= SCR_MAX_BUCKETS does). */
+int scr_align_blocks_noalloc(const int32_t* ids, int n, const int32_t* id_to_bucket, int num_ids,
+                             int num_buckets, int block_size, int32_t* sorted_routes,
+                             int32_t* block_bucket, int32_t* n_post_pad, int32_t* active_buckets,
+                             int32_t* active_block_begin, int32_t* n_active, hipStream_t stream);
 
 /* tile config [P1 Solution fourth bullet, Tests: tiles sized by the routed
  * layer's experts, never by the slot count]. */

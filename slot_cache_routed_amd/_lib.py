@@ -28,7 +28,7 @@ SCR_MAX_BUCKETS = 16384
 EXPORTS = (
     "scr_record_layout_of", "scr_route", "scr_dedup", "scr_ensure_slots", "scr_ensure_slots_batched",
     "scr_copy_misses", "scr_plan_chunk",
-    "scr_align_capacity", "scr_align_workspace", "scr_align_blocks", "scr_tile_config",
+    "scr_align_capacity", "scr_align_workspace", "scr_align_blocks", "scr_align_blocks_noalloc", "scr_tile_config",
     "scr_moe_workspace", "scr_grouped_moe_forward", "scr_quantize_fp8", "scr_quantize_nvfp4", "scr_stream_layer_async",
     "scr_stage_plan",
     "scr_stage_rows_async", "scr_stage_rows_dma_async", "scr_fill_row_table", "scr_fill_staged_rows", "scr_bank_rebuild_map",
@@ -98,6 +98,7 @@ _SIGS = {
     "scr_align_capacity": (_SZ, [_I, _I, _I]),
     "scr_align_workspace": (_I, [_I, _I, C.POINTER(_SZ)]),
     "scr_align_blocks": (_I, [_P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "scr_align_blocks_noalloc": (_I, [_P, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "scr_tile_config": (_I, [_I, _I, _I, _I, C.POINTER(TileCfg)]),
     "scr_moe_workspace": (_I, [_I, _I, _I, _I, _I, C.POINTER(TileCfg), C.POINTER(_SZ)]),
     "scr_grouped_moe_forward": (_I, [C.POINTER(RoutedExperts), _P, _I, _P, _P, _P, _P, _P, _P, _I, _P,
@@ -221,6 +222,13 @@ def align_blocks(ids, n, id_to_bucket, num_ids, num_buckets, block_size, sorted_
     _check("scr_align_blocks", load().scr_align_blocks(
         _p(ids), n, _p(id_to_bucket), num_ids, num_buckets, block_size, _p(sorted_routes), _p(block_bucket),
         _p(n_post_pad), _p(active_buckets), _p(active_block_begin), _p(n_active), _p(ws), ws_bytes, stream))
+
+
+def align_blocks_noalloc(ids, n, id_to_bucket, num_ids, num_buckets, block_size, sorted_routes, block_bucket,
+                         n_post_pad, active_buckets, active_block_begin, n_active, stream):
+    _check("scr_align_blocks_noalloc", load().scr_align_blocks_noalloc(
+        _p(ids), n, _p(id_to_bucket), num_ids, num_buckets, block_size, _p(sorted_routes), _p(block_bucket),
+        _p(n_post_pad), _p(active_buckets), _p(active_block_begin), _p(n_active), stream))
 
 
 def tile_config(T, k, E_layer, wdtype) -> TileCfg:

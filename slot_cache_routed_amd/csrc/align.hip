@@ -12,6 +12,8 @@
 // need no workgroup barrier (wave ballots rank equal buckets of a batch).
 #include "small_blocks.h"
 
+#include <mutex>
+
 namespace scr {
 
 constexpr int kAlignMatrixBudget = 1 << 20;  // entries of the chunk x bucket count matrix (4 MiB)
@@ -329,11 +331,12 @@ extern "C" int scr_align_workspace(int n, int num_buckets, size_t* bytes) {
   return SCR_OK;
 }
 
-extern "C" int scr_align_blocks(const int32_t* ids, int n, const int32_t* id_to_bucket, int num_ids,
-                                int num_buckets, int block_size, int32_t* sorted_routes,
-                                int32_t* block_bucket, int32_t* n_post_pad, int32_t* active_buckets,
-                                int32_t* active_block_begin, int32_t* n_active, void* ws,
-                                size_t ws_bytes, hipStream_t stream) {
+namespace scr {
+
+static int align_blocks_impl(const int32_t* ids, int n, const int32_t* id_to_bucket, int num_ids, int num_buckets,
+                             int block_size, int32_t* sorted_routes, int32_t* block_bucket, int32_t* n_post_pad,
+                             int32_t* active_buckets, int32_t* active_block_begin, int32_t* n_active, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
   SCR_CHECK_ARG(n >= 0 && n < (1 << 30), "align: n out of range");
   SCR_CHECK_ARG(num_buckets >= 1 && num_buckets <= SCR_MAX_BUCKETS, "align: num_buckets must be in [1, %d]",
                 SCR_MAX_BUCKETS);
@@ -377,4 +380,75 @@ extern "C" int scr_align_blocks(const int32_t* ids, int n, const int32_t* id_to_
                      bucket_off, n_post_pad, nblocks, block_bucket, sorted_routes);
   SCR_CHECK_LAUNCH();
   return SCR_OK;
+}
+
+// Scratch of the entry point that allocates nothing: the largest workspace an
+// align call can need (the count matrix is capped at kAlignMatrixBudget
+// entries, plus two ints per bucket), resident on every GPU the library runs
+// on until the process ends.  Host code never uses the array's name as an
+// address: each device's copy is looked up once with hipGetSymbolAddress (on
+// the first call made with that device current) and that address is what
+// the kernels receive.  Every entry of it that an align call reads is written
+// by the same call first (counts, then totals and offsets), so nothing needs
+// clearing between calls.
+constexpr size_t kAlignScratchBytes = ((size_t)kAlignMatrixBudget + 2 * (size_t)SCR_MAX_BUCKETS) * sizeof(int32_t) + 256;
+static __device__ __align__(256) unsigned char scratch[kAlignScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mutex;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int scratch_for_current_device(void** out) {
+  int dev = -1;
+  SCR_CHECK_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("align_blocks_noalloc: device %d beyond the %d the library tracks", dev, kMaxDevices);
+    return SCR_ENOTSUP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    SCR_CHECK_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) {
+      set_error("align_blocks_noalloc: no device address for the scratch array on device %d", dev);
+      return SCR_EHIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SCR_OK;
+}
+
+}  // namespace scr
+
+extern "C" int scr_align_blocks(const int32_t* ids, int n, const int32_t* id_to_bucket, int num_ids,
+                                int num_buckets, int block_size, int32_t* sorted_routes,
+                                int32_t* block_bucket, int32_t* n_post_pad, int32_t* active_buckets,
+                                int32_t* active_block_begin, int32_t* n_active, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  return scr::align_blocks_impl(ids, n, id_to_bucket, num_ids, num_buckets, block_size, sorted_routes, block_bucket,
+                                n_post_pad, active_buckets, active_block_begin, n_active, ws, ws_bytes, stream);
+}
+
+extern "C" int scr_align_blocks_noalloc(const int32_t* ids, int n, const int32_t* id_to_bucket, int num_ids,
+                                        int num_buckets, int block_size, int32_t* sorted_routes,
+                                        int32_t* block_bucket, int32_t* n_post_pad, int32_t* active_buckets,
+                                        int32_t* active_block_begin, int32_t* n_active, hipStream_t stream) {
+  SCR_CHECK_ARG(n >= 0 && n < (1 << 30), "align_noalloc: n out of range");
+  SCR_CHECK_ARG(num_buckets >= 1 && num_buckets <= SCR_MAX_BUCKETS, "align_noalloc: num_buckets must be in [1, %d]",
+                SCR_MAX_BUCKETS);
+  size_t need = 0;
+  int rc = scr_align_workspace(n, num_buckets, &need);
+  if (rc) return rc;
+  if (need > scr::kAlignScratchBytes) {
+    scr::set_error("align_noalloc: %zu bytes of scratch needed, the library holds %zu", need,
+                   scr::kAlignScratchBytes);
+    return SCR_ECAPACITY;
+  }
+  void* ws = nullptr;
+  rc = scr::scratch_for_current_device(&ws);
+  if (rc) return rc;
+  return scr::align_blocks_impl(ids, n, id_to_bucket, num_ids, num_buckets, block_size, sorted_routes, block_bucket,
+                                n_post_pad, active_buckets, active_block_begin, n_active, ws, scr::kAlignScratchBytes,
+                                stream);
 }
