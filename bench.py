@@ -17,7 +17,7 @@ step captured once as a HIP graph (checked bitwise against the eager step);
 the eager step's times are reported beside it.  The cold step (bank reset to
 its pre-filled state, 160 misses copied from pinned host memory) is reported
 as "layer_ms_cold" (PCIe-inclusive, never `value`), and the warm replay timed
-one step at a time after a 512 MB write that flushes the memory-side cache as
+one step at a time after a 512 MB read that flushes the memory-side cache as
 "layer_ms_mall_flushed_median".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -227,12 +227,13 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
-        # the same replays one at a time, each after a 512 MB write that flushes
-        # the 256 MB memory-side cache, timed by events around the replay alone
-        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        # the same replays one at a time, each after a 512 MB read that flushes
+        # the 256 MB memory-side cache (a read leaves no dirty lines to write
+        # back during the step), timed by events around the replay alone
+        flush_buf = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
         fl = []
         for i in range(args.steps + 5):
-            flush_buf.fill_(i & 0xFF)
+            flush_buf.sum()
             t_a, t_b = L.Timer(), L.Timer()
             t_a.record(s)
             g.replay()
