@@ -418,9 +418,9 @@ int scr_grouped_moe_forward(const scr_routed_experts* view, const void* x, int T
 
 /* quantize_fp8 [P1 Solution, fourth bullet: activations quantised under the
  * max of the layer's input scales; the static FP8 activation encoding is a
- * reading]: with a = max(scales[0..n_scales)) (device f32), codes[i] = the
- * OCP E4M3FN code of x[i] / a (an IEEE fp32 division), rounded to nearest
- * even and saturated to +-448.  x device bf16 [rows][cols], codes device u8
+ * reading]: with a = max(scales[0..n_scales)) (device f32) and r = 1 / a (an
+ * IEEE fp32 division), codes[i] = the OCP E4M3FN code of the fp32 product
+ * x[i] * r, rounded to nearest even and saturated to +-448.  x device bf16 [rows][cols], codes device u8
  * [rows][cols].  Inputs finite, a > 0. */
 int scr_quantize_fp8(const void* x, long long rows, int cols, const float* scales, int n_scales,
                      uint8_t* codes, hipStream_t stream);
@@ -429,9 +429,10 @@ int scr_quantize_fp8(const void* x, long long rows, int cols, const float* scale
  * their global scale]: with a = max(scales[0..n_scales)), per row and block
  * of 16 consecutive columns: block = E4M3 code of amax / (6 * a) (fp32
  * product and division, nearest even, saturated to 448), then per element
- * the E2M1 code of x / (e4m3(block) * a) (nearest, ties to even, saturated
- * to +-6; sign bit set for every negative input); a block whose scale is
- * zero gets zero codes.  x device bf16 [rows][cols], cols a multiple of 16;
+ * the E2M1 code of the fp32 product x * r, r = 1 / (e4m3(block) * a) (one
+ * IEEE division per block; nearest, ties to even, saturated to +-6; sign bit
+ * set for every negative input); a block whose scale is zero gets zero
+ * codes.  x device bf16 [rows][cols], cols a multiple of 16;
  * codes device u8 [rows][cols / 2] (low nibble = even column); block_scales
  * device u8 [rows][cols / 16].  Inputs finite, a > 0. */
 int scr_quantize_nvfp4(const void* x, long long rows, int cols, const float* scales, int n_scales,

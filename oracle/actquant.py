@@ -10,22 +10,26 @@ input scales, and over the slot cache it must take the routed layer's scales
   the routed layer's per-expert input scales for that GEMM.  A layer carries
   one array for the gate/up input x and one for the down input h (each
   quantised linear layer of a checkpoint has its own input scale; reading).
-* W4A8 (``quantize_fp8_static``): FP8 E4M3 codes of v / scale, one scale per
-  tensor, rounded to nearest even and saturated to +-448 (the static FP8
-  activation scheme).  Decoded value = e4m3(code) * scale.
+* W4A8 (``quantize_fp8_static``): FP8 E4M3 codes of v times the reciprocal
+  of the scale, one scale per tensor, rounded to nearest even and saturated
+  to +-448 (the static FP8 activation scheme).  Decoded value = e4m3(code) *
+  scale.
 * W4A4 (``quantize_nvfp4_act``): NVFP4 activations with the layer scale as
   the second-level (global) scale: per 16 consecutive columns of a row the
   block scale is the e4m3 code of amax / (6 * scale) (6 = the largest e2m1
-  value), and each element the e2m1 code of v / (block * scale); decoded
-  value = e2m1(code) * e4m3(block) * scale.  A block whose scale rounds to
-  zero gets zero codes.
+  value), and each element the e2m1 code of v times the reciprocal of
+  (block * scale); decoded value = e2m1(code) * e4m3(block) * scale.  A
+  block whose scale rounds to zero gets zero codes.
 
-Where these decisions are made in floating point (a division, then a
-rounding to a code), they are made in fp32, the precision the kernels use:
-v and the scale are fp32 values, 6 * scale and block * scale are fp32
-products and each quotient is an IEEE fp32 division.  The roundings to codes
-are exact operations on those fp32 values.  Everything after the codes
-(decoding, the GEMMs) is fp64.
+Where these decisions are made in floating point (a quotient or a product,
+then a rounding to a code), they are made in fp32, the precision the kernels
+use: v and the scale are fp32 values; 6 * scale and block * scale are fp32
+products; amax / (6 * scale) is an IEEE fp32 division; the reciprocals 1 /
+scale (once per tensor) and 1 / (block * scale) (once per block) are IEEE
+fp32 divisions, and each element is multiplied by its reciprocal in fp32 (a
+quantiser multiplies by the inverse scale rather than dividing every
+element).  The roundings to codes are exact operations on those fp32 values.
+Everything after the codes (decoding, the GEMMs) is fp64.
 
 e2m1 rounding: to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the
 even code (0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4,
@@ -60,8 +64,8 @@ def layer_activation_scales(input_scale, down_input_scale):
 # ----------------------------------------------------------------- W4A8
 
 def quantize_fp8_static(v: np.ndarray, scale) -> np.ndarray:
-    """E4M3 codes (uint8, same shape) of fp32(v) / fp32(scale)."""
-    q = np.asarray(v, dtype=np.float32) / np.float32(scale)
+    """E4M3 codes (uint8, same shape) of fp32(v) * fp32(1 / fp32(scale))."""
+    q = np.asarray(v, dtype=np.float32) * (np.float32(1.0) / np.float32(scale))
     return _e4m3_encode_array(q.astype(np.float64)).reshape(np.shape(v))
 
 
@@ -95,7 +99,8 @@ def quantize_nvfp4_act(v: np.ndarray, scale):
     sv = _E4M3_LUT[sc].astype(np.float32)                                   # exact in fp32
     den = sv * s                                                            # fp32 product
     live = (sv > 0)[:, :, None]
-    q = blocks / np.where(live, den[:, :, None], np.float32(1.0))           # fp32 quotients
+    rcp = np.float32(1.0) / np.where(live, den[:, :, None], np.float32(1.0))  # fp32 reciprocal per block
+    q = blocks * rcp                                                        # fp32 products
     codes = e2m1_encode_array(q)
     # a zero block scale keeps only the signs (every element rounds to zero)
     codes = np.where(live, codes, np.where(blocks < 0, 8, 0)).astype(np.uint8)

@@ -80,32 +80,34 @@ __device__ __forceinline__ unsigned e4m3_code_sat(float v) {
   const float c = fminf(fmaxf(v, -448.0f), 448.0f);
   return (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
 }
-// E2M1 magnitude code (0..7) of a magnitude: nearest of 0, 0.5, 1, 1.5, 2, 3,
-// 4, 6, ties to the even code, saturated to 6
-__device__ __forceinline__ int e2m1_mag_code(float m) {
-  return (int)(m > 0.25f) + (int)(m >= 0.75f) + (int)(m > 1.25f) + (int)(m >= 1.75f) + (int)(m > 2.5f) +
-         (int)(m >= 3.5f) + (int)(m > 5.0f);
-}
-__device__ __forceinline__ float e2m1_mag_value(int c) {
-  return c < 2 ? 0.5f * (float)c : __builtin_amdgcn_ldexpf((c & 1) ? 1.5f : 1.0f, (c >> 1) - 1);
-}
 // NVFP4 activation block under the layer scale s: the block scale code of a
 // block whose largest magnitude is amax (fp32 product and IEEE division)
 __device__ __forceinline__ unsigned nvfp4_block_code(float amax, float s) {
   return e4m3_code_sat(amax / (6.0f * s));
 }
-// the element's E2M1 code (sign in bit 3, set for every negative v) under a
-// block scale value bv (> 0) and the layer scale s
-__device__ __forceinline__ int nvfp4_elem_code(float v, float bv, float s) {
-  const int mag = bv > 0.0f ? e2m1_mag_code(fabsf(v / (bv * s))) : 0;
-  return mag | (v < 0.0f ? 8 : 0);
+// the reciprocal an NVFP4 block's elements are multiplied by: 1 / (block
+// scale value * layer scale), an IEEE division once per block (0 for a zero
+// block scale, whose elements all get zero codes)
+__device__ __forceinline__ float nvfp4_block_rcp(float bv, float s) {
+  return bv > 0.0f ? 1.0f / (bv * s) : 0.0f;
 }
-// the element's decoded value without the layer scale, e2m1 * block, as fp16
-// bits (exact: at most 5 significant bits, magnitude in [2^-10, 2688])
-__device__ __forceinline__ uint16_t nvfp4_elem_f16(int code, float bv) {
-  const float m = e2m1_mag_value(code & 7) * bv;
-  const _Float16 h = (_Float16)((code & 8) ? -m : m);
-  return __builtin_bit_cast(uint16_t, h);
+// E2M1 codes of two values times their block's reciprocal, v0 in the low
+// nibble: the magnitudes from the gfx950 conversion (nearest of 0, 0.5, 1,
+// 1.5, 2, 3, 4, 6, ties to the even code, saturated to 6: the rule, checked
+// on every midpoint and its neighbours), the sign bit from the input (set
+// for every negative v, also where the magnitude rounds to 0)
+__device__ __forceinline__ unsigned nvfp4_pair_codes(float v0, float v1, float rcp) {
+  const unsigned m = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, fabsf(v0 * rcp), fabsf(v1 * rcp), 1.0f, 0) & 0xFFu;
+  return m | (v0 < 0.0f ? 0x8u : 0u) | (v1 < 0.0f ? 0x80u : 0u);
+}
+// the pair's decoded values without the layer scale, e2m1 * block, as two
+// fp16 (exact: at most 5 significant bits, magnitude in [2^-10, 2688])
+__device__ __forceinline__ unsigned nvfp4_pair_f16(unsigned codes, float bv) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+  const _Float16 b = (_Float16)bv;
+  const h2 bb = {b, b};
+  return __builtin_bit_cast(unsigned, e * bb);
 }
 
 // Weight formats: bytes of one tile-block (16 rows x 128 columns) of codes
@@ -886,10 +888,11 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
         if constexpr (WDT == SCR_W_NVFP4_A4) {
           // W4A4: h quantised to NVFP4 under the layer's down scale a2, per
           // row and 16 columns.  The wave's 16 x HC block of h goes through
-          // its LDS tile as fp32; lane l < 2 * 16 then owns row l / 2,
-          // columns 16 (l % 2) .. + 15 (one NVFP4 block), and writes them as
-          // the exact fp16 values e2m1 * block (the down GEMM's fp16 operand;
-          // a2 goes to its accumulators)
+          // its LDS tile as fp32; then lane l takes row l / 4, the 8 columns
+          // 8 (l % 4) .. + 7 (half of one NVFP4 block: lanes l and l ^ 1
+          // share a block and its largest magnitude), and writes them as the
+          // exact fp16 values e2m1 * block (the down GEMM's fp16 operand; a2
+          // goes to its accumulators)
           static_assert(HC == 32, "one wave's h row holds two NVFP4 blocks");
           float* shf = reinterpret_cast<float*>(wst);
 #pragma unroll
@@ -897,33 +900,27 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
 #pragma unroll
             for (int t = 0; t < NTW / 2; ++t)
               shf[(grp * 4 + i) * HC + 16 * t + col] = silu_mul(gs * acc[mt][t][i], gs * acc[mt][t + NTW / 2][i]);
-          if (lane < 32) {
-            // the block's largest magnitude, then its values again in two
-            // halves of 8 (few registers live beside the accumulators)
+          {
             const float a2 = a.act_scale[1];
-            const float4* src = reinterpret_cast<const float4*>(shf + (lane >> 1) * HC + 16 * (lane & 1));
+            const float4* src = reinterpret_cast<const float4*>(shf + (lane >> 2) * HC + 8 * (lane & 3));
+            const float4 q0 = src[0], q1 = src[1];
+            const float v[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
             float amax = 0.0f;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float4 q = src[c];
-              amax = fmaxf(fmaxf(amax, fmaxf(fabsf(q.x), fabsf(q.y))), fmaxf(fabsf(q.z), fabsf(q.w)));
-            }
+            for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(v[c]));
+            amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
             const float bv = __builtin_amdgcn_cvt_f32_fp8((int)nvfp4_block_code(amax, a2), 0);
-            const int pos = m0 + mt * 16 + (lane >> 1);
-            const int hc = ch * (HC * EW) + wave * HC + 16 * (lane & 1);
-            u32x4* dst = reinterpret_cast<u32x4*>(a.h + (size_t)pos * a.I + hc);
+            const float rcp = nvfp4_block_rcp(bv, a2);
+            u32x4 out;
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-              const float4 q0 = src[2 * half], q1 = src[2 * half + 1];
-              const float v[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-              u32x4 out;
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                out[c] = (unsigned)nvfp4_elem_f16(nvfp4_elem_code(v[2 * c], bv, a2), bv) |
-                         ((unsigned)nvfp4_elem_f16(nvfp4_elem_code(v[2 * c + 1], bv, a2), bv) << 16);
-              dst[half] = out;
-            }
+            for (int c = 0; c < 4; ++c) out[c] = nvfp4_pair_f16(nvfp4_pair_codes(v[2 * c], v[2 * c + 1], rcp), bv);
+            const int pos = m0 + mt * 16 + (lane >> 2);
+            const int hc = ch * (HC * EW) + wave * HC + 8 * (lane & 3);
+            *reinterpret_cast<u32x4*>(a.h + (size_t)pos * a.I + hc) = out;
           }
+          // one row tile at a time (interleaving the tiles' divisions would
+          // hold more registers than the accumulators leave)
+          __builtin_amdgcn_sched_barrier(0);
         } else {
 #pragma unroll
           for (int i = 0; i < 4; i += 2)
@@ -1282,6 +1279,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const bf16* __restrict__
   }
   __syncthreads();
   const float a1 = sm;
+  const float r1 = 1.0f / a1;  // FP8: codes of x times the reciprocal of the layer scale
   for (long long b = blockIdx.x * 256ll + threadIdx.x; b < nblk; b += (long long)gridDim.x * 256) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + b * 16);
     const u32x4 v0 = ldg<u32x4>(src), v1 = ldg<u32x4>(src + 1);
@@ -1297,8 +1295,8 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const bf16* __restrict__
       u32x4 out;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        out[i] = e4m3_code_sat(f[4 * i] / a1) | (e4m3_code_sat(f[4 * i + 1] / a1) << 8) |
-                 (e4m3_code_sat(f[4 * i + 2] / a1) << 16) | (e4m3_code_sat(f[4 * i + 3] / a1) << 24);
+        out[i] = e4m3_code_sat(f[4 * i] * r1) | (e4m3_code_sat(f[4 * i + 1] * r1) << 8) |
+                 (e4m3_code_sat(f[4 * i + 2] * r1) << 16) | (e4m3_code_sat(f[4 * i + 3] * r1) << 24);
       reinterpret_cast<u32x4*>(q + b * 16)[0] = out;
     } else {
       float amax = 0.0f;
@@ -1306,25 +1304,20 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const bf16* __restrict__
       for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
       const unsigned bc = nvfp4_block_code(amax, a1);
       const float bv = __builtin_amdgcn_cvt_f32_fp8((int)bc, 0);
-      int c[16];
+      const float rcp = nvfp4_block_rcp(bv, a1);
+      unsigned c[8];  // code pairs, the even element in the low nibble
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = nvfp4_elem_code(f[i], bv, a1);
+      for (int i = 0; i < 8; ++i) c[i] = nvfp4_pair_codes(f[2 * i], f[2 * i + 1], rcp);
       if constexpr (MODE == kActNvfp4) {
         u32x2 out;
 #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          unsigned d = 0;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) d |= (unsigned)c[8 * w + i] << (4 * i);
-          out[w] = d;
-        }
+        for (int w = 0; w < 2; ++w) out[w] = c[4 * w] | (c[4 * w + 1] << 8) | (c[4 * w + 2] << 16) | (c[4 * w + 3] << 24);
         reinterpret_cast<u32x2*>(q + b * 8)[0] = out;
         bs[b] = (uint8_t)bc;
       } else {
         u32x4 out[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          out[i / 4][i % 4] = (unsigned)nvfp4_elem_f16(c[2 * i], bv) | ((unsigned)nvfp4_elem_f16(c[2 * i + 1], bv) << 16);
+        for (int i = 0; i < 8; ++i) out[i / 4][i % 4] = nvfp4_pair_f16(c[i], bv);
         u32x4* dst = reinterpret_cast<u32x4*>(f16 + b * 16);
         dst[0] = out[0];
         dst[1] = out[1];
@@ -1431,8 +1424,8 @@ __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row,
   auto epilogue = [&](int ch) {
     if (GATEUP) {
       // h = silu(g) * u for this wave's 32 h columns, g and u the accumulators
-      // times a1, as E4M3 codes of h / a2
-      const float a1 = a.act_scale[0], a2 = a.act_scale[1];
+      // times a1, as E4M3 codes of h times the reciprocal of a2
+      const float a1 = a.act_scale[0], r2 = 1.0f / a.act_scale[1];
       uint8_t* sh = reinterpret_cast<uint8_t*>(wst);
 #pragma unroll
       for (int mt = 0; mt < MTC; ++mt) {
@@ -1440,8 +1433,8 @@ __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row,
         for (int i = 0; i < 4; ++i) {
           const float h0 = silu_mul(a1 * acc[mt][0][i], a1 * acc[mt][NTW / 2][i]);
           const float h1 = silu_mul(a1 * acc[mt][1][i], a1 * acc[mt][NTW / 2 + 1][i]);
-          sh[(grp * 4 + i) * 32 + col] = (uint8_t)e4m3_code_sat(h0 / a2);
-          sh[(grp * 4 + i) * 32 + 16 + col] = (uint8_t)e4m3_code_sat(h1 / a2);
+          sh[(grp * 4 + i) * 32 + col] = (uint8_t)e4m3_code_sat(h0 * r2);
+          sh[(grp * 4 + i) * 32 + 16 + col] = (uint8_t)e4m3_code_sat(h1 * r2);
         }
         // 16 rows x 32 bytes = 32 lanes x 16 bytes
         if (lane < 32) {
