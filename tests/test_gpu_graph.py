@@ -185,11 +185,35 @@ def test_short_prefill_96_step_as_the_bench_times_it():
             step(side.cuda_stream)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    for _ in range(3):
+    # every launch of the step is in the graph: the route's and the planner's
+    # outputs are cleared before each replay and come back, and the bank's
+    # clock advances by one eager step's queries per replay
+    plan_keys = ("topk_ids", "topk_w", "sorted_routes", "n_post_pad", "active_buckets", "active_block_begin",
+                 "n_active")
+
+    def plan_outputs():     # the defined parts of the route's and the planner's outputs
+        n, npp = int(buf["n_active"][0]), int(buf["n_post_pad"][0])
+        return [buf["topk_ids"].clone(), buf["topk_w"].clone(), buf["n_active"].clone(), buf["n_post_pad"].clone(),
+                buf["active_buckets"][:n].clone(), buf["active_block_begin"][:n + 1].clone(),
+                buf["sorted_routes"][:npp].clone()]
+
+    plan_warm = plan_outputs()
+    clock0 = bank.snapshot()["clock"]
+    step(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    per_step = bank.snapshot()["clock"] - clock0
+    assert per_step > 0
+    for rep in range(3):
         buf["y"].zero_()
+        for key in plan_keys:
+            buf[key].fill_(-3)
+        clock0 = bank.snapshot()["clock"]
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(buf["y"], y_warm)
+        for i, (a, b) in enumerate(zip(plan_outputs(), plan_warm)):
+            assert torch.equal(a, b), (rep, i)
+        assert bank.snapshot()["clock"] - clock0 == per_step, rep
         _ = (x.float() * 2).sum().item()      # eager work between replays
     lb = LY.LayerStreamBuffer(E, lay.record_bytes)
     st = LY.stream_layer(pool, 0, logits, x, sc, lb, L.SCR_W_BF16, y_dtype=L.SCR_Y_BF16, shape=(k, H, I))
