@@ -696,13 +696,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
 // other.
 //
 // Activations reach LDS by direct global-to-LDS loads (no register staging):
-// two K-block buffers, each a [rows][128] bf16 tile whose 16-byte chunks are
-// XOR-swizzled by (row mod 16), so the fragment reads hit distinct banks.
+// K-block buffers, each a [rows][128] bf16 tile whose 16-byte chunks are
+// XOR-swizzled by a function of (row mod 16) (wide_swz), so the fragment
+// reads hit distinct banks.
 // The buffers are separate arrays so that the compiler can tell a read of one
 // from the direct loads still in flight into the other.
 constexpr int kWideBufs = 4;  // activation K-block buffers in LDS (loaded kWideBufs - 1 blocks ahead)
 constexpr int kWideRing = 2;  // NVFP4 weight ring depth in K blocks (deeper measured slower)
 constexpr int kWideStage = 4096;  // bytes of LDS per wave for the epilogue tile (16 rows x 64 fp32)
+
+// The chunk swizzle of activation row r: physical chunk = logical ^ wide_swz(r).
+// A 16-lane group of a fragment read takes 16 rows; the bf16 order (lane
+// group g reads logical chunk 4 s + g) is conflict-free with r mod 16 itself,
+// while the block-scaled formats' order (chunk 4 g + s) needs the two 2-bit
+// halves of r mod 16 swapped: with r mod 16 every 128-bit read of the
+// latter took a two-way bank conflict on gfx950 (measured with the LDS
+// conflict counter), with the swap none, for every step and row tile.
+template <int WDT>
+__device__ __forceinline__ int wide_swz(int r) {
+  return WDT == SCR_W_BF16 ? (r & 15) : (((r & 3) << 2) | ((r >> 2) & 3));
+}
 
 // s_waitcnt immediate that waits until at most n vector memory operations are
 // outstanding (gfx9 encoding; the LDS and export counters are left alone)
@@ -828,7 +841,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
   // the last instruction: the same bytes to the same place), so that the
   // waits below can count them.  Instruction j fills LDS chunk q = 64 j +
   // lane of a buffer, i.e. row q / 16, physical chunk q % 16, which holds
-  // logical chunk (q % 16) ^ (row % 16).
+  // logical chunk (q % 16) ^ wide_swz(row).
   constexpr int NA = (4 * MTC + EW - 1) / EW;
   int aoff[NA];  // byte offsets
   int adst[NA];  // LDS element offsets of the wave's 1 KB destinations
@@ -836,7 +849,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
   for (int u = 0; u < NA; ++u) {
     const int j = min(u * EW + wave, 4 * MTC - 1);
     const int q = j * 64 + lane;
-    const int r = q >> 4, c = (q & 15) ^ (r & 15);
+    const int r = q >> 4, c = (q & 15) ^ wide_swz<WDT>(r);
     const int off = src_row[r];
     aoff[u] = 2 * (off >= 0 ? off : 0) + 16 * c;  // padding rows read row 0 (their outputs are dropped)
     adst[u] = j * 512;
@@ -863,7 +876,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
     const int c = kcol<WDT>(grp, st) >> 3;
 #pragma unroll
     for (int mt = 0; mt < MTC; ++mt)
-      af[mt] = *reinterpret_cast<const bf16x8*>(buf + (mt * 16 + col) * kKB + ((c ^ col) << 3));
+      af[mt] = *reinterpret_cast<const bf16x8*>(buf + (mt * 16 + col) * kKB + ((c ^ wide_swz<WDT>(col)) << 3));
   };
 
 
