@@ -155,15 +155,7 @@ __global__ __launch_bounds__(kLayoutThreads) void align_layout_kernel(const int3
     pad_sum += (cnt[i] + B - 1) / B * B;
     act_sum += cnt[i] > 0;
   }
-  int s0 = pad_sum, s1 = act_sum;  // inclusive scans over the wave
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o0 = __shfl_up(s0, off, kWave), o1 = __shfl_up(s1, off, kWave);
-    if (lane >= off) {
-      s0 += o0;
-      s1 += o1;
-    }
-  }
+  const int s0 = wave_incl_sum(pad_sum), s1 = wave_incl_sum(act_sum);  // inclusive scans over the wave
   if (lane == kWave - 1) {
     wave_tot[0][wv] = s0;
     wave_tot[1][wv] = s1;

@@ -119,7 +119,7 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
   }
 
   // lookup: one query entry per thread (width <= blockDim)
-  int my_key = -1, is_miss = 0;
+  int my_key = -1, is_miss = 0, is_hit = 0;
   if (tid < width) {
     const int e = qe;
     if (e >= 0 && e < E) {
@@ -133,31 +133,25 @@ __device__ int ensure_query(EnsureShared& sh, const BankRefs& bk, uint64_t now, 
         }
         bk.slot_stamp[s] = now;  // touch the hit
         atomicOr(&sh.hit_bits[s >> 5], 1u << (s & 31));
-        atomicAdd(&sh.nhit, 1);
+        is_hit = 1;
       } else {
         is_miss = 1;
       }
     }
   }
+  {  // the hits counted per wave: one LDS atomic per wave instead of one per hit
+    const uint64_t hits = __ballot(is_hit);
+    if (lane_id() == 0 && hits) atomicAdd(&sh.nhit, (int)__popcll(hits));
+  }
   const int m = __syncthreads_count(is_miss);
   // misses keep query order: exclusive scan of the miss flags
   if (m > 0) {
     const int lane = lane_id(), wv = tid / kWave, nw = blockDim.x / kWave;
-    int v = is_miss;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(v, off, kWave);
-      if (lane >= off) v += o;
-    }
+    const int v = wave_incl_sum(is_miss);
     if (lane == kWave - 1) sh.wave_tot[wv] = v;
     __syncthreads();
     if (wv == 0) {
-      int t = lane < nw ? sh.wave_tot[lane] : 0;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const int o = __shfl_up(t, off, kWave);
-        if (lane >= off) t += o;
-      }
+      const int t = wave_incl_sum(lane < nw ? sh.wave_tot[lane] : 0);
       if (lane < nw) sh.wave_tot[lane] = t;
     }
     __syncthreads();
@@ -294,28 +288,87 @@ __global__ __launch_bounds__(kLruThreads) void ensure_slots_kernel(BankRefs bk, 
 // Their admitted misses are appended to one list; an entry whose slot was
 // taken again by a later query of the same call is marked superseded (slot -1)
 // so that one copy over the list moves only each slot's final record.
+// prefilled: the chunk planner's dedup already wrote the entries and their
+// slots into sh.pf_e / sh.pf_s (only when they fit, see ensure_prefetches).
+// Queries from valid_queries on hold only sentinels (the tail of a dedup'd
+// list): each is one clock tick and one counted query, as ensure_query would
+// make it, without its barriers.
+__device__ __forceinline__ bool ensure_prefetches(int entries, int S) {
+  return entries <= kEnsPrefetch && S <= kPrefetchSlots;
+}
+
 __device__ __forceinline__ void ensure_batched_block(EnsureShared& sh, const BankRefs& bk, uint64_t* __restrict__ clock,
                                                      const int32_t* __restrict__ distinct, int width, int n_queries,
                                                      int last_width, int record_stats, int32_t* __restrict__ miss_slot,
                                                      int32_t* __restrict__ miss_key, int32_t* __restrict__ n_miss,
-                                                     int32_t* __restrict__ n_total) {
+                                                     int32_t* __restrict__ n_total, bool prefilled = false,
+                                                     int valid_queries = 1 << 30) {
   uint64_t now = *clock;
   const uint64_t pin = now + 1;  // the call is one chunk: its first query's clock
   if (bk.chunk_start && threadIdx.x == 0) *bk.chunk_start = pin;
   const int entries = (n_queries - 1) * width + last_width;
-  const bool pf = entries <= kEnsPrefetch && bk.S <= kPrefetchSlots;
+  const bool pf = ensure_prefetches(entries, bk.S);
   if (pf) {  // every entry's slot in one round of loads
-    for (int i = threadIdx.x; i < entries; i += blockDim.x) {
-      const int e = distinct[i];
-      sh.pf_e[i] = e;
-      sh.pf_s[i] = (e >= 0 && e < bk.E) ? bk.key_to_slot[(size_t)bk.layer * bk.E + e] : -1;
-    }
+    if (!prefilled)
+      for (int i = threadIdx.x; i < entries; i += blockDim.x) {
+        const int e = distinct[i];
+        sh.pf_e[i] = e;
+        sh.pf_s[i] = (e >= 0 && e < bk.E) ? bk.key_to_slot[(size_t)bk.layer * bk.E + e] : -1;
+      }
     for (int i = threadIdx.x; i < (bk.S + 31) / 32; i += blockDim.x) sh.taken[i] = 0;
     __syncthreads();
+    // A chunk whose every valid entry is resident admits nothing, so its
+    // queries need no candidate selection: each hit is touched at its own
+    // query's clock (keys are distinct, so no slot twice), and the counts are
+    // those the per-query path would add.  One barrier for the whole call.
+    int valid = 0, miss = 0;
+    for (int i = threadIdx.x; i < entries; i += blockDim.x) {
+      const int e = sh.pf_e[i];
+      if (e >= 0 && e < bk.E) {
+        ++valid;
+        miss |= sh.pf_s[i] < 0;
+      }
+    }
+    const int wvalid = wave_incl_sum(valid);
+    if (lane_id() == kWave - 1) sh.wave_tot[threadIdx.x / kWave] = wvalid;
+    if (!__syncthreads_or(miss)) {
+      const bool lrfu = bk.policy == SCR_POLICY_LRFU;
+      for (int i = threadIdx.x; i < entries; i += blockDim.x) {
+        const int e = sh.pf_e[i];
+        if (e < 0 || e >= bk.E) continue;
+        const int s = sh.pf_s[i];
+        const uint64_t tq = now + 1 + (uint64_t)(i / width);
+        if (lrfu) {
+          const uint64_t c = crf_decay(bk.slot_crf[s], tq - bk.slot_stamp[s], bk.decay) + kCrfOne;
+          bk.slot_crf[s] = c > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)c;
+        }
+        bk.slot_stamp[s] = tq;
+        if (record_stats) bk.decode_freq[(size_t)bk.layer * bk.E + e] += 1u;
+      }
+      if (threadIdx.x == 0) {
+        if (record_stats) {
+          int hits = 0;
+          for (int w = 0; w < (int)blockDim.x / kWave; ++w) hits += sh.wave_tot[w];
+          bk.stats[0] += (uint64_t)hits;
+          bk.stats[3] += (uint64_t)n_queries;
+        }
+        for (int q = 0; q < n_queries; ++q) n_miss[q] = 0;
+        *clock = now + (uint64_t)n_queries;
+        *n_total = 0;
+      }
+      return;
+    }
   }
   int total = 0;
   for (int q = 0; q < n_queries; ++q) {
     now += 1;
+    if (q >= valid_queries) {  // sentinels only
+      if (threadIdx.x == 0) {
+        if (record_stats) bk.stats[3] += 1;
+        n_miss[q] = 0;
+      }
+      continue;
+    }
     const int w = q + 1 < n_queries ? width : last_width;
     const int m = ensure_query(sh, bk, now, pin, distinct + (size_t)q * width, w, record_stats, miss_slot + total,
                                miss_key + total, pf ? sh.pf_e + q * width : nullptr,
@@ -360,6 +413,10 @@ union PlanShared {
   } al;
 };
 
+static_assert(offsetof(EnsureShared, pf_e) >= sizeof(PlanShared::dd) &&
+                  offsetof(EnsureShared, pf_s) >= sizeof(PlanShared::dd),
+              "the dedup's LDS must not overlap the LRU copy it fills");
+
 __global__ __launch_bounds__(kPlanThreads) void plan_chunk_kernel(
     BankRefs bk, uint64_t* __restrict__ clock, const int32_t* __restrict__ ids, int n, int lmax,
     int32_t* __restrict__ distinct, int32_t* __restrict__ n_distinct, int width, int n_queries, int last_width,
@@ -368,10 +425,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_chunk_kernel(
     int32_t* __restrict__ block_bucket, int32_t* __restrict__ n_post_pad, int32_t* __restrict__ active_buckets,
     int32_t* __restrict__ active_block_begin, int32_t* __restrict__ n_active) {
   __shared__ PlanShared sh;
-  dedup_block(ids, n, bk.E, lmax, distinct, n_distinct, nullptr, sh.dd.pos, sh.dd.wave_tot);
+  // the dedup writes the distinct list and its slots straight into the LRU's
+  // LDS copy (those arrays lie past the dedup's own)
+  const bool pf = ensure_prefetches(lmax, bk.S);
+  dedup_block(ids, n, bk.E, lmax, distinct, n_distinct, nullptr, sh.dd.pos, sh.dd.wave_tot, pf ? sh.ens.pf_e : nullptr,
+              pf ? sh.ens.pf_s : nullptr, bk.key_to_slot + (size_t)bk.layer * bk.E);
+  const int n_dist = sh.dd.wave_tot[kWave];  // valid entries fill the list's head
   __syncthreads();
   ensure_batched_block(sh.ens, bk, clock, distinct, width, n_queries, last_width, record_stats, miss_slot, miss_key,
-                       n_miss, n_total);
+                       n_miss, n_total, pf, (n_dist + width - 1) / width);
   __syncthreads();
   align_small_block(ids, n, bk.key_to_slot + (size_t)bk.layer * bk.E, bk.E, bk.S, B, cap, sorted_routes,
                     block_bucket, n_post_pad, active_buckets, active_block_begin, n_active, sh.al.cnt, sh.al.rb,

@@ -17,20 +17,11 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* wave_tot) {
   const int lane = lane_id();
   const int wv = threadIdx.x / kWave;
   const int nw = blockDim.x / kWave;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o = __shfl_up(v, off, kWave);
-    if (lane >= off) v += o;
-  }
+  v = wave_incl_sum(v);
   if (lane == kWave - 1) wave_tot[wv] = v;
   __syncthreads();
   if (wv == 0) {
-    int t = lane < nw ? wave_tot[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(t, off, kWave);
-      if (lane >= off) t += o;
-    }
+    const int t = wave_incl_sum(lane < nw ? wave_tot[lane] : 0);
     if (lane < nw) wave_tot[lane] = t;
   }
   __syncthreads();
@@ -68,10 +59,14 @@ __device__ __forceinline__ uint64_t bucket_peers(int b, int nbits) {
 
 // Distinct ids as a sorted fixed-length list: marks in LDS, a scan, a
 // scatter (a counting sort over ids).  pos: LDS [kDedupMaxE]; wave_tot: LDS
-// [kWave + 1].
+// [kWave + 1].  With lds_e / lds_s (LDS [lmax], the chunk planner's copy for
+// its LRU queries) the list is also written there with each id's slot
+// slot_of[id] (-1 for the sentinels), so that the queries need no loads.
 __device__ __forceinline__ void dedup_block(const int32_t* __restrict__ ids, int n, int E, int lmax,
                                             int32_t* __restrict__ distinct, int32_t* __restrict__ n_distinct,
-                                            int32_t* __restrict__ inverse, int* pos, int* wave_tot) {
+                                            int32_t* __restrict__ inverse, int* pos, int* wave_tot,
+                                            int* lds_e = nullptr, int* lds_s = nullptr,
+                                            const int32_t* __restrict__ slot_of = nullptr) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) pos[e] = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
@@ -89,11 +84,23 @@ __device__ __forceinline__ void dedup_block(const int32_t* __restrict__ ids, int
   int p = incl - cnt;
   for (int e = e0; e < e1; ++e) {
     const int present = pos[e];
-    if (present) distinct[p] = e;
+    if (present) {
+      distinct[p] = e;
+      if (lds_e) {
+        lds_e[p] = e;
+        lds_s[p] = slot_of[e];
+      }
+    }
     pos[e] = present ? p : -1;
     p += present;
   }
-  for (int i = total + threadIdx.x; i < lmax; i += blockDim.x) distinct[i] = E;
+  for (int i = total + threadIdx.x; i < lmax; i += blockDim.x) {
+    distinct[i] = E;
+    if (lds_e) {
+      lds_e[i] = E;
+      lds_s[i] = -1;
+    }
+  }
   if (threadIdx.x == 0) *n_distinct = total;
   if (inverse) {
     __syncthreads();
@@ -130,7 +137,12 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
   // every position a sentinel and every block unused, in coalesced passes;
   // the layout and the scatter below overwrite the used ones (the barriers in
   // between order the stores)
-  for (int q = tid; q < cap; q += blockDim.x) sorted_routes[q] = n;
+  if ((reinterpret_cast<uintptr_t>(sorted_routes) & 15) == 0 && cap % 4 == 0) {  // 16-byte stores
+    const int4 sv = make_int4(n, n, n, n);
+    for (int q = tid; q < cap / 4; q += blockDim.x) reinterpret_cast<int4*>(sorted_routes)[q] = sv;
+  } else {
+    for (int q = tid; q < cap; q += blockDim.x) sorted_routes[q] = n;
+  }
   for (int j = tid; j < cap / B; j += blockDim.x) block_bucket[j] = -1;
   __syncthreads();
   for (int r = tid; r < n; r += blockDim.x) {
@@ -149,15 +161,7 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
     pad_sum += (c + B - 1) / B * B;
     act_sum += c > 0;
   }
-  int s0 = pad_sum, s1 = act_sum;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int o0 = __shfl_up(s0, off, kWave), o1 = __shfl_up(s1, off, kWave);
-    if (lane >= off) {
-      s0 += o0;
-      s1 += o1;
-    }
-  }
+  const int s0 = wave_incl_sum(pad_sum), s1 = wave_incl_sum(act_sum);
   if (lane == kWave - 1) {
     wave_tot[wv] = s0;
     wave_tot[kWave + wv] = s1;

@@ -139,3 +139,56 @@ def test_plan_at_its_largest_shape_against_the_oracle():
     for key in ("slot_key", "slot_stamp", "key_to_slot", "clock", "stats", "decode_freq", "err"):
         assert np.array_equal(np.asarray(snap[key]), np.asarray(getattr(st, key))), key
     flush(f"plan at 4096 routes / 8192 experts / 8192 slots: {nd} distinct")
+
+
+@pytest.mark.parametrize("planner", ["batched", "plan_chunk"])
+@pytest.mark.parametrize("stats", [0, 1])
+@pytest.mark.parametrize("policy", ["lru", "lrfu"])
+def test_all_hit_chunks_against_the_oracle(policy, stats, planner):
+    """A chunk whose experts are all resident admits nothing, and the planners
+    then touch every hit without selecting candidates.  Three chunks of layer
+    1: one that admits its experts, the same chunk again (all hits), and a
+    chunk of a subset of them (all hits, more trailing queries of sentinels).
+    After each, the bank state (stamps at each query's own clock, the LRFU
+    values, counts, frequencies, clock) and the per-query miss counts equal
+    the oracle's query-by-query run."""
+    import math
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    from oracle import dedup_sorted
+    from oracle.lru import POLICY_LRFU
+    S, E, NL, k, T, width, rec, layer = 200, 128, 2, 4, 30, 16, 256, 1
+    D = math.floor(2 ** 32 * 2 ** (-1.0 / 4))
+    pol = L.SCR_POLICY_LRFU if policy == "lrfu" else L.SCR_POLICY_LRU
+    g = np.random.default_rng(77)
+    ids = np.stack([g.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    chunks = [ids, ids, ids[:9]]
+    pool = LY.HostPool(NL, E, rec, E, payload_of=lambda key: key % E)
+    fill = W.bank_prefilled(5, S, NL, E, 120, exclude_layer=layer)
+    bank = LY.Bank(S, NL, E, 0, rec, policy=pol, lrfu_decay=D)
+    bank.load_fill(fill)
+    st = SlotBankState.from_fill(fill)
+    if policy == "lrfu":
+        st.policy, st.decay_q32 = POLICY_LRFU, D
+    s = torch.cuda.current_stream().cuda_stream
+    for c, chunk in enumerate(chunks):
+        Tc = chunk.shape[0]
+        buf = LY.LayerBuffers(Tc, E, k, 128, 128, S, 0, width=width)
+        buf["topk_ids"].copy_(torch.from_numpy(np.ascontiguousarray(chunk)).reshape(-1))
+        if planner == "plan_chunk":
+            assert LY.plan(buf, bank, pool, layer, bool(stats))
+        else:
+            L.dedup(buf["topk_ids"], buf.R, E, buf["distinct"], buf["n_distinct"], buf["inverse"], s)
+            LY.admit(buf, bank, pool, layer, bool(stats), batched=True)
+        torch.cuda.synchronize()
+        distinct, nd, _ = dedup_sorted(chunk.reshape(-1), E)
+        misses = []
+        for q0 in range(0, len(distinct), width):
+            ms, _ = ensure_slots(st, layer, distinct[q0:q0 + width], bool(stats), chunk_first=(q0 == 0))
+            misses.append(len(ms))
+        assert buf["n_miss"].cpu().numpy()[:len(misses)].tolist() == misses, (c, misses)
+        assert (sum(misses) == 0) == (c > 0), c
+        snap = bank.snapshot()
+        for key in ("slot_key", "slot_stamp", "key_to_slot", "clock", "stats", "decode_freq", "err", "slot_crf"):
+            assert np.array_equal(np.asarray(snap[key]), np.asarray(getattr(st, key))), (c, key)
+    flush(f"all-hit chunks ({policy}, stats {stats}, {planner}): bank state equals the oracle")
