@@ -67,6 +67,17 @@ __device__ __forceinline__ void dedup_block(const int32_t* __restrict__ ids, int
                                             int32_t* __restrict__ inverse, int* pos, int* wave_tot,
                                             int* lds_e = nullptr, int* lds_s = nullptr,
                                             const int32_t* __restrict__ slot_of = nullptr) {
+  // each thread owns a contiguous run of ids [e0, e1), at most
+  // kDedupMaxE / kPlanThreads of them; with lds_e their slots are read first,
+  // so that those loads overlap the marking
+  constexpr int kRun = kDedupMaxE / kPlanThreads;
+  const int per = (E + blockDim.x - 1) / blockDim.x;
+  const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
+  int slot_pre[kRun];
+  if (lds_e) {
+#pragma unroll
+    for (int u = 0; u < kRun; ++u) slot_pre[u] = e0 + u < e1 ? slot_of[e0 + u] : -1;
+  }
   for (int e = threadIdx.x; e < E; e += blockDim.x) pos[e] = 0;
   __syncthreads();
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
@@ -74,21 +85,21 @@ __device__ __forceinline__ void dedup_block(const int32_t* __restrict__ ids, int
     if (e >= 0 && e < E) pos[e] = 1;
   }
   __syncthreads();
-  // each thread owns a contiguous run of ids [e0, e1)
-  const int per = (E + blockDim.x - 1) / blockDim.x;
-  const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
   int cnt = 0;
   for (int e = e0; e < e1; ++e) cnt += pos[e];
   const int incl = block_inclusive_scan(cnt, wave_tot);
   const int total = wave_tot[kWave];
   int p = incl - cnt;
-  for (int e = e0; e < e1; ++e) {
+#pragma unroll
+  for (int u = 0; u < kRun; ++u) {
+    const int e = e0 + u;
+    if (e >= e1) break;
     const int present = pos[e];
     if (present) {
       distinct[p] = e;
       if (lds_e) {
         lds_e[p] = e;
-        lds_s[p] = slot_of[e];
+        lds_s[p] = slot_pre[u];
       }
     }
     pos[e] = present ? p : -1;
@@ -130,10 +141,6 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
   // batch) counts when it fits, else by one wave walking the batches in order
   const bool use_tab = (long long)nb * nchunks <= kAlignTab;
   for (int b = tid; b < nb; b += blockDim.x) cnt[b] = 0;
-  if (use_tab) {
-    uint32_t* t32 = reinterpret_cast<uint32_t*>(tab);
-    for (int i = tid; i < (nb * nchunks + 1) / 2; i += blockDim.x) t32[i] = 0;
-  }
   // every position a sentinel and every block unused, in coalesced passes;
   // the layout and the scatter below overwrite the used ones (the barriers in
   // between order the stores)
@@ -167,20 +174,26 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
     wave_tot[kWave + wv] = s1;
   }
   __syncthreads();
+  // the waves' totals, all loads in flight at once (a workgroup has at most
+  // kPlanThreads / kWave waves)
   int before0 = 0, before1 = 0, total0 = 0, total1 = 0;
-  for (int w = 0; w < nw; ++w) {
+#pragma unroll
+  for (int w = 0; w < kPlanThreads / kWave; ++w) {
+    const int t0 = w < nw ? wave_tot[w] : 0, t1 = w < nw ? wave_tot[kWave + w] : 0;
     if (w < wv) {
-      before0 += wave_tot[w];
-      before1 += wave_tot[kWave + w];
+      before0 += t0;
+      before1 += t1;
     }
-    total0 += wave_tot[w];
-    total1 += wave_tot[kWave + w];
+    total0 += t0;
+    total1 += t1;
   }
   int off = before0 + s0 - pad_sum, idx = before1 + s1 - act_sum;
   for (int b = b0; b < b1; ++b) {
     const int c = cnt[b];
     const int padded = (c + B - 1) / B * B;
     if (c > 0) {
+      if (use_tab)  // only the rows of active buckets are ever read
+        for (int j = 0; j < nchunks; ++j) tab[b * nchunks + j] = 0;
       active_buckets[idx] = b;
       active_block_begin[idx] = off / B;
       ++idx;
@@ -224,6 +237,8 @@ __device__ __forceinline__ void align_small_block(const int32_t* __restrict__ id
   __syncthreads();
   if (use_tab) {
     for (int b = tid; b < nb; b += blockDim.x) {
+      // a bucket is active when its first position differs from the next's
+      if ((b + 1 < nb ? cnt[b + 1] : total0) == cnt[b]) continue;
       uint16_t* row = tab + b * nchunks;
       int run = 0;
       for (int c0 = 0; c0 < nchunks; c0 += 16) {  // 16 reads in flight, then the running counts
