@@ -22,11 +22,12 @@ __device__ __forceinline__ float key_value(unsigned k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// One DPP move of x (lanes whose source lies outside the pattern, or whose
-// row is masked off, keep their own value, which max and min leave alone).
-template <int CTRL, int ROW_MASK>
+// One DPP move of x; lanes whose source lies outside the pattern, or whose
+// row is masked off, get IDENT, the identity of the reduction (so that the
+// compiler folds the move into the max or min itself).
+template <int CTRL, int ROW_MASK, unsigned IDENT>
 __device__ __forceinline__ unsigned dpp_mov(unsigned x) {
-  return (unsigned)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROW_MASK, 0xf, false);
+  return (unsigned)__builtin_amdgcn_update_dpp((int)IDENT, (int)x, CTRL, ROW_MASK, 0xf, false);
 }
 
 // Wave-wide max / min of an unsigned value by DPP: a shift-right ladder of
@@ -36,12 +37,13 @@ __device__ __forceinline__ unsigned dpp_mov(unsigned x) {
 template <bool MAX>
 __device__ __forceinline__ unsigned wave_reduce_u32(unsigned x) {
   auto op = [](unsigned a, unsigned b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-  x = op(x, dpp_mov<0x111, 0xf>(x));  // row_shr:1
-  x = op(x, dpp_mov<0x112, 0xf>(x));  // row_shr:2
-  x = op(x, dpp_mov<0x114, 0xf>(x));  // row_shr:4
-  x = op(x, dpp_mov<0x118, 0xf>(x));  // row_shr:8
-  x = op(x, dpp_mov<0x142, 0xa>(x));  // row_bcast:15
-  x = op(x, dpp_mov<0x143, 0xc>(x));  // row_bcast:31
+  constexpr unsigned I = MAX ? 0u : 0xFFFFFFFFu;  // the identity
+  x = op(x, dpp_mov<0x111, 0xf, I>(x));  // row_shr:1
+  x = op(x, dpp_mov<0x112, 0xf, I>(x));  // row_shr:2
+  x = op(x, dpp_mov<0x114, 0xf, I>(x));  // row_shr:4
+  x = op(x, dpp_mov<0x118, 0xf, I>(x));  // row_shr:8
+  x = op(x, dpp_mov<0x142, 0xa, I>(x));  // row_bcast:15
+  x = op(x, dpp_mov<0x143, 0xc, I>(x));  // row_bcast:31
   return (unsigned)__builtin_amdgcn_readlane((int)x, 63);
 }
 
@@ -97,11 +99,9 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
       gi = (unsigned)__builtin_amdgcn_readlane((int)li, __builtin_ctzll(holders));
     else
       gi = wave_reduce_u32<false>(lk == gk ? li : 0xffffffffu);
-    if ((int)(gi & (kWave - 1)) == lane) {
+    const bool mine = (int)(gi & (kWave - 1)) == lane;  // the owner marks it taken (no branch)
 #pragma unroll
-      for (int i = 0; i < VPL; ++i)
-        if ((int)(gi / kWave) == i) key[i] = 0u;
-    }
+    for (int i = 0; i < VPL; ++i) key[i] = (mine && (int)(gi / kWave) == i) ? 0u : key[i];
     if (lane == j) {
       my_key = gk;
       my_id = (int)gi;
