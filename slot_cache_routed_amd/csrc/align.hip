@@ -17,7 +17,8 @@
 namespace scr {
 
 constexpr int kAlignMatrixBudget = 1 << 20;  // entries of the chunk x bucket count matrix (4 MiB)
-constexpr int kAlignLdsInts = 16384;         // per-wave histograms of the scatter: at most 64 KiB of LDS
+constexpr int kAlignLdsInts = 36864;         // per-wave histograms and stash of the scatter: at most 144 KiB of LDS
+constexpr int kAlignMaxWaves = 16;           // waves of a scatter workgroup
 constexpr int kAlignLoads = 8;               // independent global loads a thread keeps in flight
 
 struct AlignPlan {
@@ -26,7 +27,10 @@ struct AlignPlan {
 
 static AlignPlan align_plan(int n, int nb) {
   AlignPlan p;
-  p.waves = nb <= kAlignLdsInts / 4 ? 4 : nb <= kAlignLdsInts / 2 ? 2 : 1;
+  // as many waves (each with its own histogram) as the LDS holds beside the
+  // chunk's stash: the scatter walks each wave's run in series, so more waves
+  // mean shorter runs
+  p.waves = 1;
   // about 256 chunks for a large input, each of 512..4096 routes (a chunk
   // well past the bucket count keeps the per-bucket work of a workgroup
   // small against its routes), fewer and longer if the matrix would pass its
@@ -46,6 +50,11 @@ static AlignPlan align_plan(int n, int nb) {
   }
   p.chunk = (int)chunk;
   p.nchunks = (int)nchunks;
+  for (int w = kAlignMaxWaves; w >= 1; w /= 2)
+    if ((long long)w * nb + chunk <= kAlignLdsInts || w == 1) {
+      p.waves = w;
+      break;
+    }
   return p;
 }
 
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(kLayoutThreads) void align_layout_kernel(const int3
 // table and the padding: every nchunks-th bucket (from the chunk index on)
 // gets its block ids and the sentinel in its padding, and the blocks past the
 // last bucket are split over the workgroups.
-__global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int n,
+__global__ __launch_bounds__(64 * kAlignMaxWaves) void align_scatter_kernel(const int32_t* __restrict__ ids, int n,
                                                             const int32_t* __restrict__ map, int num_ids,
                                                             int nb, int B, int chunk, int stash_ok,
                                                             const int32_t* __restrict__ cnt,
