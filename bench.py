@@ -194,6 +194,7 @@ def main():
     n_active = int(buf["n_active"].item())
     marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
     handles = [[m.handle for m in ms] for ms in marks]
+    phases = [[ev() for _ in range(4)] for _ in range(args.steps)]   # route + planner, miss copy
     # the same steps without timing events, for the cost of the events themselves
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -203,7 +204,7 @@ def main():
     ms_no_events = (time.perf_counter() - t_start) * 1e3 / args.steps
     t_start = time.perf_counter()
     for i in range(args.steps):
-        step(marks=handles[i])
+        step(marks=handles[i], phase_events=phases[i])
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     assert buf["n_miss"].cpu().numpy().sum() == 0, "warm steps admit nothing"
@@ -274,6 +275,8 @@ def main():
         del g, flush_buf
     except Exception as e:  # capture is an extra measurement; report why it is missing
         graph_ms = f"unavailable: {type(e).__name__}: {e}"
+    plan_us = statistics.mean(p[0].elapsed_ms(p[1]) for p in phases) * 1e3
+    copy_us = statistics.mean(p[1].elapsed_ms(p[2]) for p in phases) * 1e3
     gu_ms = [m[1].elapsed_ms(m[2]) for m in marks]
     dn_ms = [m[2].elapsed_ms(m[3]) for m in marks]
     cb_ms = [m[3].elapsed_ms(m[4]) for m in marks]
@@ -325,7 +328,8 @@ def main():
         "ms_per_step_eager": round(ms_no_events, 4),
         "ms_per_step_hip_graph": graph_ms if not isinstance(graph_ms, float) else round(graph_ms, 4),
         "gemm_tflops": round(gemm_tflops, 3),
-        "kernels_us": {"gate_up": round(gu * 1e3, 2), "down": round(dn * 1e3, 2), "combine": round(cb * 1e3, 2)},
+        "kernels_us": {"route_and_planner": round(plan_us, 2), "miss_copy": round(copy_us, 2),
+                       "gate_up": round(gu * 1e3, 2), "down": round(dn * 1e3, 2), "combine": round(cb * 1e3, 2)},
         "cold": {"ms_per_step": round(cold_ms, 3), "miss_copy_ms": round(copy_ms, 3),
                  "miss_copy_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 2), "misses": 160,
                  "miss_copy_frac_host_link_peak": round(copy_bytes / (copy_ms * 1e-3) / 1e9 / HOST_LINK_PEAK_GBS, 3),
