@@ -199,6 +199,8 @@ typedef struct scr_host_pool {
  *   down_input_scale  device [num_experts]: the same for the down input h;
  *                     may be NULL except for the activation-quantising
  *                     formats (SCR_W_MXFP4_A8, SCR_W_NVFP4_A4).
+ *   The activation-quantising formats divide by the maxima of these arrays:
+ *   they must hold positive finite values (device data: not checked).
  */
 typedef struct scr_routed_experts {
   int32_t layer, num_experts, k, H, I, wdtype, num_buckets;
