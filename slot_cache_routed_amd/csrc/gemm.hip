@@ -834,7 +834,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
   // for F16A) or h (down)
   const void* const abase = GATEUP ? (F16A ? (const void*)a.x16 : (const void*)a.x) : (const void*)a.h;
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)abase, (short)0, GATEUP ? a.T * a.H * 2 : a.h_rows * a.I * 2, 0x00020000);
+      (void*)abase, (short)0, (int)(2u * (unsigned)(GATEUP ? a.T * a.H : a.h_rows * a.I)), 0x00020000);
   // direct-load sources of this lane: the 4 * MTC wave instructions of a K
   // block (each fills 64 16-byte chunks = 4 rows) are dealt round-robin to the
   // EW waves; every wave issues the same count NA (a wave past the end repeats
@@ -843,22 +843,22 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
   // lane of a buffer, i.e. row q / 16, physical chunk q % 16, which holds
   // logical chunk (q % 16) ^ wide_swz(row).
   constexpr int NA = (4 * MTC + EW - 1) / EW;
-  int aoff[NA];  // byte offsets
-  int adst[NA];  // LDS element offsets of the wave's 1 KB destinations
+  unsigned aoff[NA];  // byte offsets (below 2^32: the host bounds T * H and h_rows * I by 2^31)
+  int adst[NA];       // LDS element offsets of the wave's 1 KB destinations
 #pragma unroll
   for (int u = 0; u < NA; ++u) {
     const int j = min(u * EW + wave, 4 * MTC - 1);
     const int q = j * 64 + lane;
     const int r = q >> 4, c = (q & 15) ^ wide_swz<WDT>(r);
     const int off = src_row[r];
-    aoff[u] = 2 * (off >= 0 ? off : 0) + 16 * c;  // padding rows read row 0 (their outputs are dropped)
+    aoff[u] = 2u * (unsigned)(off >= 0 ? off : 0) + 16u * c;  // padding rows read row 0 (outputs dropped)
     adst[u] = j * 512;
   }
   auto load_a = [&](bf16* buf, int kb) {
 #pragma unroll
     for (int u = 0; u < NA; ++u)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (__attribute__((address_space(3))) void*)(buf + adst[u]), 16,
-                                               aoff[u], kb * (2 * kKB), 0, 0);
+                                               (int)aoff[u], kb * (2 * kKB), 0, 0);
   };
   // weights of flat step s = chunk * nkb + kb
   auto load_b = [&](BFrag<WDT, NTW>& f, int s) {
