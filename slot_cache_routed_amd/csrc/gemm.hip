@@ -594,16 +594,17 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
 }
 
 template <int WDT, int MT, int NT, bool GATEUP>
-__global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, int ntx) {
+__global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, int ntx, int pslices) {
   __shared__ __attribute__((aligned(16))) bf16 As[2][MT * 16][kAStride];
   __shared__ int src_row[MT * 16];  // element offset of each staged row, -1 = zero row
 
   // XCD-aware order: consecutive workgroups go to different XCDs, so bucket j
-  // and all its N tiles land on XCD (j mod 8) and share its L2
+  // and all its N tiles and pass slices land on XCD (j mod 8) and share its L2
   if (GATEUP) gateup_prologue(a);
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
-  const int j = 8 * (q / ntx) + xcd;
-  const int tx = q % ntx;
+  const int per_bucket = ntx * pslices;
+  const int j = 8 * (q / per_bucket) + xcd;
+  const int tx = q % ntx, ps = (q % per_bucket) / ntx;
   if (j >= *a.n_active) return;
   const int b = a.active_buckets[j];
   const int p0 = a.active_block_begin[j] * a.B, p1 = a.active_block_begin[j + 1] * a.B;
@@ -652,7 +653,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
                            : 1.0f;
   const int arow_len = K;  // elements per activation row
 
-  for (int m0 = p0; m0 < p1; m0 += MT * 16) {
+  // this workgroup's passes: slice ps of every pslices-th
+  for (int m0 = p0 + ps * (MT * 16); m0 < p1; m0 += pslices * (MT * 16)) {
     c.m0 = m0;
     c.rows = min(MT * 16, p1 - m0);
     for (int i = c.tid; i < MT * 16; i += kGemmThreads) {
@@ -1090,7 +1092,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
 }
 
 template <int WDT, int MT, bool GATEUP, int EW, int NTW>
-__global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int groups) {
+__global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int groups, int pslices) {
   __shared__ __attribute__((aligned(1024))) bf16 As0[MT * 16 * kKB];
   __shared__ __attribute__((aligned(1024))) bf16 As1[MT * 16 * kKB];
   __shared__ __attribute__((aligned(1024))) bf16 As2[MT * 16 * kKB];
@@ -1104,9 +1106,10 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
   __shared__ float row_rs[WideF16A<WDT, GATEUP>::value ? MT * 16 : 1];
   __shared__ __attribute__((aligned(256))) uint32_t stg[EW * kWideStage / 4];  // per-wave epilogue tiles
   if (GATEUP) gateup_prologue(a);
-  // XCD-aware order: all groups of bucket j run on XCD j mod 8
+  // XCD-aware order: all groups and pass slices of bucket j run on XCD j mod 8
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
-  const int j = 8 * (q / groups) + xcd, g = q % groups;
+  const int per_bucket = groups * pslices;
+  const int j = 8 * (q / per_bucket) + xcd, g = q % groups, ps = (q % per_bucket) / groups;
   if (j >= *a.n_active) return;
   const int b = a.active_buckets[j];
   const int p0 = a.active_block_begin[j] * a.B, p1 = a.active_block_begin[j + 1] * a.B;
@@ -1138,7 +1141,8 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
                                : 1.0f;
   // W4A4: the layer's activation scale joins the record's global scale
   if constexpr (WDT == SCR_W_NVFP4_A4) gs *= a.act_scale[GATEUP ? 0 : 1];
-  for (int m0 = p0; m0 < p1; m0 += MT * 16) {
+  // this workgroup's passes: slice ps of every pslices-th
+  for (int m0 = p0 + ps * (MT * 16); m0 < p1; m0 += pslices * (MT * 16)) {
     const int rows = min(MT * 16, p1 - m0);
     for (int i = tid; i < MT * 16; i += kThreads) {
       int off = -1;
@@ -1548,7 +1552,7 @@ __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row,
 }
 
 template <int MT, bool GATEUP, int EW, int NTW, bool RES>
-__global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int groups) {
+__global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int groups, int pslices) {
   __shared__ __attribute__((aligned(1024))) uint8_t As0[MT * 16 * kKB];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[MT * 16 * kKB];
   __shared__ __attribute__((aligned(1024))) uint8_t As2[MT * 16 * kKB];
@@ -1559,7 +1563,8 @@ __global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int group
   __shared__ __attribute__((aligned(256))) uint32_t stg[EW * kWideStage / 4];
   if (GATEUP) gateup_prologue(a);
   const int bid = blockIdx.x, xcd = bid & 7, q = bid >> 3;
-  const int j = 8 * (q / groups) + xcd, g = q % groups;
+  const int per_bucket = groups * pslices;
+  const int j = 8 * (q / per_bucket) + xcd, g = q % groups, ps = (q % per_bucket) / groups;
   if (j >= *a.n_active) return;
   const int b = a.active_buckets[j];
   const int p0 = a.active_block_begin[j] * a.B, p1 = a.active_block_begin[j + 1] * a.B;
@@ -1583,7 +1588,7 @@ __global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int group
     toff0[t] = (int)(GATEUP ? a.lay.w13_off : a.lay.w2_off) + tb * 1024;
     soff0[t] = (int)(GATEUP ? a.lay.w13_scale_off : a.lay.w2_scale_off) + tb * 64;
   }
-  for (int m0 = p0; m0 < p1; m0 += MT * 16) {
+  for (int m0 = p0 + ps * (MT * 16); m0 < p1; m0 += pslices * (MT * 16)) {
     const int rows = min(MT * 16, p1 - m0);
     for (int i = tid; i < MT * 16; i += kThreads) {
       int off = -1;
@@ -1681,6 +1686,23 @@ static bool wide_gemms_fit(const GemmArgs& a) {
          a.H % (16 * NTW * kWideWaves) == 0;
 }
 
+// Pass slices: a bucket walks its rows in passes of pass_rows, and with few
+// buckets and many rows each (a small layer over a long chunk) one workgroup
+// per bucket would leave most CUs idle.  The passes of a bucket are then dealt
+// to pslices workgroups (slice i takes passes i, i + pslices, ...): as many as
+// bring the launch to about kFillWorkgroups, at most the passes of a bucket of
+// average size.  The weights are streamed once per pass either way, so the
+// slices add no weight traffic; a slice past a bucket's last pass exits at
+// once.
+constexpr int kFillWorkgroups = 1024;
+static int pass_slices(const GemmArgs& a, int max_active, int pass_rows, int base_wgs) {
+  const long long avg_rows = ((long long)a.R + max_active - 1) / max_active + a.B - 1;  // padded
+  const long long avg_passes = (avg_rows + pass_rows - 1) / pass_rows;
+  const long long want = (kFillWorkgroups + base_wgs - 1) / base_wgs;
+  const long long ps = want < avg_passes ? want : avg_passes;
+  return ps < 1 ? 1 : (int)ps;
+}
+
 // many rows per expert: both GEMMs as wide-tile workgroups, each walking a
 // contiguous range of one bucket's N chunks (gate/up: one chunk of 128 h
 // columns; down: two chunks of 256 output columns)
@@ -1700,12 +1722,14 @@ static int launch_wide_gemms(const GemmArgs& a, int max_active, hipEvent_t* mark
     const int rc = launch_x_to_f16(a, s);
     if (rc) return rc;
   }
-  hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, true, kWideWaves, NTW>), dim3(8 * rows8 * g_gu), dim3(64 * kWideWaves),
-                     0, s, a, g_gu);
+  const int ps_gu = pass_slices(a, max_active, MT * 16, 8 * rows8 * g_gu);
+  const int ps_dn = pass_slices(a, max_active, MT * 16, 8 * rows8 * g_dn);
+  hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, true, kWideWaves, NTW>), dim3(8 * rows8 * g_gu * ps_gu),
+                     dim3(64 * kWideWaves), 0, s, a, g_gu, ps_gu);
   SCR_CHECK_LAUNCH();
   if (marks && marks[2]) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
-  hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, false, kWideWaves, NTW>), dim3(8 * rows8 * g_dn), dim3(64 * kWideWaves),
-                     0, s, a, g_dn);
+  hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, false, kWideWaves, NTW>), dim3(8 * rows8 * g_dn * ps_dn),
+                     dim3(64 * kWideWaves), 0, s, a, g_dn, ps_dn);
   SCR_CHECK_LAUNCH();
   if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
   return SCR_OK;
@@ -1716,12 +1740,14 @@ static int launch_gemms(const GemmArgs& a, int max_active, hipEvent_t* marks, hi
   const int rows8 = (max_active + 7) / 8;     // buckets per XCD (rounded up)
   const int ntx_gu = (a.I + 4 * 8 * NT - 1) / (4 * 8 * NT);
   const int ntx_dn = (a.H + 4 * 16 * NT - 1) / (4 * 16 * NT);
-  hipLaunchKernelGGL((moe_gemm_kernel<WDT, MT, NT, true>), dim3(8 * rows8 * ntx_gu), dim3(kGemmThreads), 0, s, a,
-                     ntx_gu);
+  const int ps_gu = pass_slices(a, max_active, MT * 16, 8 * rows8 * ntx_gu);
+  const int ps_dn = pass_slices(a, max_active, MT * 16, 8 * rows8 * ntx_dn);
+  hipLaunchKernelGGL((moe_gemm_kernel<WDT, MT, NT, true>), dim3(8 * rows8 * ntx_gu * ps_gu), dim3(kGemmThreads), 0,
+                     s, a, ntx_gu, ps_gu);
   SCR_CHECK_LAUNCH();
   if (marks && marks[2]) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
-  hipLaunchKernelGGL((moe_gemm_kernel<WDT, MT, NT, false>), dim3(8 * rows8 * ntx_dn), dim3(kGemmThreads), 0, s, a,
-                     ntx_dn);
+  hipLaunchKernelGGL((moe_gemm_kernel<WDT, MT, NT, false>), dim3(8 * rows8 * ntx_dn * ps_dn), dim3(kGemmThreads), 0,
+                     s, a, ntx_dn, ps_dn);
   SCR_CHECK_LAUNCH();
   if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
   return SCR_OK;
@@ -1746,16 +1772,18 @@ static int launch_w4a8(const GemmArgs& a, int max_active, hipEvent_t* marks, hip
   const int nch_dn = a.H / (16 * NTW * kWideWaves);
   const int g_gu = many_rows ? 1 : a.I / (8 * NTW * kWideWaves);
   const int g_dn = many_rows ? 1 : (nch_dn >= 2 ? nch_dn / 2 : 1);
-  hipLaunchKernelGGL((moe_w4a8_kernel<7, true, kWideWaves, NTW, false>), dim3(8 * rows8 * g_gu),
-                     dim3(64 * kWideWaves), 0, s, a, g_gu);
+  const int ps_gu = pass_slices(a, max_active, 7 * 16, 8 * rows8 * g_gu);
+  const int ps_dn = pass_slices(a, max_active, 7 * 16, 8 * rows8 * g_dn);
+  hipLaunchKernelGGL((moe_w4a8_kernel<7, true, kWideWaves, NTW, false>), dim3(8 * rows8 * g_gu * ps_gu),
+                     dim3(64 * kWideWaves), 0, s, a, g_gu, ps_gu);
   SCR_CHECK_LAUNCH();
   if (marks && marks[2]) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
   if (a.I / kKB == kWideBufs)
-    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, true>), dim3(8 * rows8 * g_dn),
-                       dim3(64 * kWideWaves), 0, s, a, g_dn);
+    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, true>), dim3(8 * rows8 * g_dn * ps_dn),
+                       dim3(64 * kWideWaves), 0, s, a, g_dn, ps_dn);
   else
-    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, false>), dim3(8 * rows8 * g_dn),
-                       dim3(64 * kWideWaves), 0, s, a, g_dn);
+    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, false>), dim3(8 * rows8 * g_dn * ps_dn),
+                       dim3(64 * kWideWaves), 0, s, a, g_dn, ps_dn);
   SCR_CHECK_LAUNCH();
   if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
   return SCR_OK;

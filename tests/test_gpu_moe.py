@@ -425,6 +425,56 @@ def test_full_size_4096_token_layer_in_every_weight_format(wd):
     torch.cuda.empty_cache()
 
 
+def test_forward_at_the_largest_token_count():
+    """T * H just below 2^31, the forward's bound (T = 524,287 tokens of hidden
+    4096, so x alone is 4 GiB and the activation byte offsets pass 2^31), over
+    a layer of 8 bf16 experts with top-1: about 65,500 rows per expert, so the
+    wide kernels deal each bucket's 112-row passes to many workgroups.  The
+    first, middle and last tokens and a seeded sample are compared with the
+    oracle."""
+    import slot_cache_routed_amd.layer as LY
+    import slot_cache_routed_amd._lib as L
+    E, k, H, I, seed = 8, 1, 4096, 512, 13
+    T = (1 << 31) // H - 1
+    code = wdtype_code("bf16")
+    src = ExpertSource(seed, H, I, "bf16")
+    lay = LY.record_layout(code, H, I)
+    flush(f"largest token count: T={T} H={H} I={I} E={E} k={k}")
+    lb = LY.LayerStreamBuffer(E, lay.record_bytes)
+    for e in range(E):
+        w13, w2 = src.raw(e)
+        lb.data[e * lay.record_bytes:(e + 1) * lay.record_bytes].copy_(
+            torch.from_numpy(LY.pack_record_bf16(lay, w13, w2)))
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, E, size=T).astype(np.int32)
+    b = LY.LayerBuffers(T, E, k, H, I, E, code)
+    b["topk_ids"].copy_(torch.from_numpy(ids))
+    b["topk_w"].fill_(1.0)
+    # x drawn on the device (4 GiB), in row blocks, from a seeded generator
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    for r0 in range(0, T, 1 << 16):
+        r1 = min(T, r0 + (1 << 16))
+        x[r0:r1] = torch.randn((r1 - r0, H), generator=g, device="cuda").to(torch.bfloat16)
+    LY.align(b, None, 0)
+    sc = torch.ones(E, dtype=torch.float32, device="cuda")
+    view = LY.make_view(0, E, k, H, I, code, E, lb.row_table, sc)
+    cfg = LY.forward(b, view, x)
+    torch.cuda.synchronize()
+    assert cfg.m_chunk == 112
+    tokens = np.unique(np.concatenate([[0, 1, T // 2, T - 3, T - 2, T - 1], rng.integers(0, T, size=26)]))
+    sel = torch.from_numpy(tokens).cuda()
+    xs = bf16_bits_to_f64(x[sel].view(torch.int16).cpu().numpy().view(np.uint16))
+    y = b["y"][sel].cpu().numpy()
+    y_ref = moe_layer_tokens(xs, ids[tokens].reshape(-1, 1), np.ones((tokens.size, 1)), src.f64, range(tokens.size))
+    err = rel_max_err(y, y_ref)
+    flush(f"largest token count: rel max err over {tokens.size} tokens = {err:.3e}")
+    assert err <= TOL_BF16
+    del x, b, lb
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("k", [24, 32])
 def test_top_k_past_sixteen(k):
     """k above 16: the combine sums a token's ranks in groups of 16 (the second
