@@ -64,7 +64,9 @@ def _args():
                    help="steps of the graph-replayed and LRFU decode passes")
     p.add_argument("--no-align", action="store_true", help="skip the align measurements")
     p.add_argument("--no-formats", action="store_true",
-                   help="skip the 4096-token grouped GEMM in every weight format (bf16, NVFP4, FP8, MXFP4)")
+                   help="skip the 4096-token grouped GEMMs by weight format (512 experts, and 8 experts)")
+    p.add_argument("--no-few-experts", action="store_true",
+                   help="skip the 4096-token grouped GEMMs over 8 experts (keeps per-kernel profiles to one shape)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gateup_short_prefill_96.json"),
                    help="HBM traffic of the dominant kernel from rocprofv3 counters (JSON), if present")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -349,6 +351,9 @@ def main():
     if not args.no_formats:
         out["formats_4096"] = formats_4096()
         torch.cuda.empty_cache()
+        if not args.no_few_experts:
+            out["few_experts_4096"] = few_experts_4096()
+            torch.cuda.empty_cache()
     if not args.no_align:
         out["align"] = align_bench()
     if not args.no_cpu:
@@ -494,11 +499,11 @@ def long_prefill(args) -> dict:
     }
 
 
-def formats_4096() -> dict:
-    """The grouped GEMM of one 4096-token layer (512 experts, top-10, hidden
-    2048, intermediate 512, every expert resident in HBM) in each weight
-    format.  512 expert records alias 64 generated ones (the kernels read
-    every record's own bytes; aliasing only bounds the host set-up time)."""
+def _gemm_by_format(T: int, E: int, k: int, H: int, I: int, seed: int, names, P: int) -> dict:
+    """Gate/up and down times of one layer's grouped GEMM (every expert
+    resident in HBM, routes from N(0,1) logits) in each named weight format.
+    E expert records alias P generated ones (the kernels read every record's
+    own bytes; aliasing only bounds the host set-up time)."""
     import numpy as np
     import torch
     from concurrent.futures import ThreadPoolExecutor
@@ -507,30 +512,25 @@ def formats_4096() -> dict:
     import slot_cache_routed_amd._lib as L
     import slot_cache_routed_amd.layer as LY
 
-    cfg = W.C5
-    T, E, k, H, I = cfg.T, cfg.shape.E, cfg.shape.k, cfg.shape.H, cfg.shape.I
-    R, P = T * k, 64
+    R = T * k
+    P = min(P, E)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    lg = dev(W.logits_normal(cfg.seed, 0, T, E))
-    x = dev(W.f32_to_bf16_bits(W.activations_normal(cfg.seed, T, H)).view(np.int16))
+    lg = dev(W.logits_normal(seed, 0, T, E))
+    x = dev(W.f32_to_bf16_bits(W.activations_normal(seed, T, H)).view(np.int16))
     sc = dev(W.c3_input_scales(E))        # the layer's input scales (2.0 / 3.0; used by W4A8 and W4A4)
     s = torch.cuda.current_stream().cuda_stream
-    fmts = (("bf16", L.SCR_W_BF16, lambda lay, p: LY.pack_record_bf16(lay, *W.expert_bf16(cfg.seed, p, H, I))),
-            ("nvfp4", L.SCR_W_NVFP4, lambda lay, p: LY.pack_record_nvfp4(lay, W.expert_nvfp4(cfg.seed, p, H, I))),
-            ("fp8", L.SCR_W_FP8, lambda lay, p: LY.pack_record_fp8(lay, W.expert_fp8(cfg.seed, p, H, I))),
-            ("mxfp4", L.SCR_W_MXFP4, lambda lay, p: LY.pack_record_mxfp4(lay, W.expert_mxfp4(cfg.seed, p, H, I))),
-            ("mxfp4_w4a8", L.SCR_W_MXFP4_A8,
-             lambda lay, p: LY.pack_record_mxfp4(lay, W.expert_mxfp4(cfg.seed, p, H, I))),
-            ("nvfp4_w4a4", L.SCR_W_NVFP4_A4,
-             lambda lay, p: LY.pack_record_nvfp4(lay, W.expert_nvfp4(cfg.seed, p, H, I))))
-    out = {"workload": "4096 tokens, 512 experts resident, top-10, hidden 2048, intermediate 512; "
-                       "TFLOP/s = 6*R*H*I / (gate/up + down); nvfp4's gate/up time includes its fp16 copy of x; "
-                       "mxfp4_w4a8 quantises x to FP8 E4M3 under the layer's max input scale (activation_quant_us, "
-                       "added to its GEMM time) and runs the fp8 x fp4 block-scaled MFMA, whose dense peak is 5 "
-                       "PFLOP/s; nvfp4_w4a4 quantises x to NVFP4 under the same scale (also added) and runs the fp16 "
-                       "MFMA on the exact decoded operands (frac_bf16_mfma_peak stays against 2.5)"}
+    fmts = {"bf16": (L.SCR_W_BF16, lambda lay, p: LY.pack_record_bf16(lay, *W.expert_bf16(seed, p, H, I))),
+            "nvfp4": (L.SCR_W_NVFP4, lambda lay, p: LY.pack_record_nvfp4(lay, W.expert_nvfp4(seed, p, H, I))),
+            "fp8": (L.SCR_W_FP8, lambda lay, p: LY.pack_record_fp8(lay, W.expert_fp8(seed, p, H, I))),
+            "mxfp4": (L.SCR_W_MXFP4, lambda lay, p: LY.pack_record_mxfp4(lay, W.expert_mxfp4(seed, p, H, I))),
+            "mxfp4_w4a8": (L.SCR_W_MXFP4_A8,
+                           lambda lay, p: LY.pack_record_mxfp4(lay, W.expert_mxfp4(seed, p, H, I))),
+            "nvfp4_w4a4": (L.SCR_W_NVFP4_A4,
+                           lambda lay, p: LY.pack_record_nvfp4(lay, W.expert_nvfp4(seed, p, H, I)))}
+    out = {}
     flops = 6.0 * R * H * I
-    for name, code, pack in fmts:
+    for name in names:
+        code, pack = fmts[name]
         lay = LY.record_layout(code, H, I)
         rec = int(lay.record_bytes)
         with ThreadPoolExecutor(min(16, os.cpu_count() or 4)) as ex:
@@ -538,7 +538,8 @@ def formats_4096() -> dict:
         lb = LY.LayerStreamBuffer(E, rec)
         host = torch.from_numpy(np.concatenate(recs))
         for e0 in range(0, E, P):
-            lb.data[e0 * rec:(e0 + P) * rec].copy_(host)
+            n = min(P, E - e0)
+            lb.data[e0 * rec:(e0 + n) * rec].copy_(host[:n * rec])
         b = LY.LayerBuffers(T, E, k, H, I, E, code, y_dtype=L.SCR_Y_BF16)
         L.route(lg, T, E, k, b["topk_ids"], b["topk_w"], s)
         LY.align(b, None, 0)
@@ -563,9 +564,37 @@ def formats_4096() -> dict:
                      "gemm_tflops": round(flops / (t * 1e-3) / 1e12, 1),
                      "frac_bf16_mfma_peak": round(flops / (t * 1e-3) / 1e12 / 2500.0, 4),
                      "weight_bytes": wbytes, "weight_GBps": round(wbytes / (t * 1e-3) / 1e9, 1)}
-        _log(f"formats: {name} gate/up {gu * 1e3:.1f} us, down {dn * 1e3:.1f} us")
+        _log(f"formats ({T}x{E}, top-{k}): {name} gate/up {gu * 1e3:.1f} us, down {dn * 1e3:.1f} us")
         del lb, b, host, recs
         torch.cuda.empty_cache()
+    return out
+
+
+_FORMATS_NOTE = ("TFLOP/s = 6*R*H*I / (gate/up + down); nvfp4's gate/up time includes its fp16 copy of x; "
+                 "mxfp4_w4a8 quantises x to FP8 E4M3 under the layer's max input scale (activation_quant_us, "
+                 "added to its GEMM time) and runs the fp8 x fp4 block-scaled MFMA, whose dense peak is 5 "
+                 "PFLOP/s; nvfp4_w4a4 quantises x to NVFP4 under the same scale (also added) and runs the fp16 "
+                 "MFMA on the exact decoded operands (frac_bf16_mfma_peak stays against 2.5)")
+
+
+def formats_4096() -> dict:
+    """The grouped GEMM of one 4096-token layer (512 experts, top-10, hidden
+    2048, intermediate 512, every expert resident in HBM) in each weight
+    format; 512 records alias 64 generated ones."""
+    import workloads as W
+    cfg = W.C5
+    out = {"workload": "4096 tokens, 512 experts resident, top-10, hidden 2048, intermediate 512; " + _FORMATS_NOTE}
+    out.update(_gemm_by_format(cfg.T, cfg.shape.E, cfg.shape.k, cfg.shape.H, cfg.shape.I, cfg.seed,
+                               ("bf16", "nvfp4", "fp8", "mxfp4", "mxfp4_w4a8", "nvfp4_w4a4"), 64))
+    return out
+
+
+def few_experts_4096() -> dict:
+    """The same chunk over a small layer (8 experts, top-2: about 1000 rows
+    per expert), where each expert's row passes are spread over several
+    workgroups."""
+    out = {"workload": "4096 tokens, 8 experts resident, top-2, hidden 2048, intermediate 512; " + _FORMATS_NOTE}
+    out.update(_gemm_by_format(4096, 8, 2, 2048, 512, 17, ("bf16", "nvfp4", "mxfp4_w4a8"), 8))
     return out
 
 
