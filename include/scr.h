@@ -214,8 +214,10 @@ typedef struct scr_routed_experts {
 typedef struct scr_tile_cfg {
   int32_t block_m;   /* align block size (rows of one MFMA M tile)      */
   int32_t m_chunk;   /* rows one workgroup holds per pass over a bucket */
-  int32_t n_tile_gu; /* h columns per gate/up workgroup                 */
-  int32_t n_tile_dn; /* output columns per down workgroup               */
+  int32_t n_tile_gu; /* h columns per gate/up workgroup (per N chunk for
+                        the 112-row kernels, whose workgroups take one or
+                        more chunks)                                     */
+  int32_t n_tile_dn; /* output columns per down workgroup (likewise)     */
   int32_t wdtype;
 } scr_tile_cfg;
 

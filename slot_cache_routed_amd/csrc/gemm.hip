@@ -438,6 +438,15 @@ struct BFrag<SCR_W_MXFP4, NT> {
 template <int NT>
 struct BFrag<SCR_W_NVFP4_A4, NT> : BFrag<SCR_W_NVFP4, NT> {};
 
+// Gate/up operands as fp16 (NVFP4 weights and x's fp16 copy with its row
+// scales; the W4A4 format's exact fp16 values): one packed fp16 multiply
+// finishes each pair of weights, where the bf16 MFMA would need the products
+// rounded through fp32
+template <int WDT, bool GATEUP>
+struct WideF16A {
+  static constexpr bool value = (WDT == SCR_W_NVFP4 && GATEUP) || WDT == SCR_W_NVFP4_A4;
+};
+
 struct PassCtx {
   int tid, lane, wave, col, grp, rows, m0, nkb, ncol0, tx;
   bool active;
@@ -452,8 +461,10 @@ struct PassCtx {
 template <int WDT, int MT, int NT, bool GATEUP, int MTC>
 __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, const uint8_t* const* rowp,
                                           const uint8_t* const* scp, bf16 (*As)[MT * 16][kAStride],
-                                          const int* src_row) {
-  const bf16* abase = GATEUP ? a.x : a.h;
+                                          const int* src_row, const float* row_rs) {
+  // NVFP4 gate/up: x's fp16 copy (row t scaled by 2^xe[t]) on the fp16 MFMA
+  constexpr bool F16A = WideF16A<WDT, GATEUP>::value;
+  const bf16* abase = GATEUP ? (F16A ? reinterpret_cast<const bf16*>(a.x16) : a.x) : a.h;
   const int tid = c.tid, col = c.col, grp = c.grp, nkb = c.nkb;
   constexpr int kRowChunks = kKB / 8;                      // 16-byte chunks per row and block
   constexpr int kChunks = MTC * 16 * kRowChunks;
@@ -503,13 +514,19 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
     for (int st = 0; st < 4; ++st) {
       bf16x8 bf[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bf[t] = bc.get(t, st);
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (F16A) bf[t] = bc.get_f16(t, st);
+        else bf[t] = bc.get_hw(t, st);
+      }
 #pragma unroll
       for (int mt = 0; mt < MTC; ++mt) {
         const bf16x8 av =
             *reinterpret_cast<const bf16x8*>(&As[buf][mt * 16 + col][kcol<WDT>(grp, st)]);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) acc[mt][t] = mfma16(av, bf[t], acc[mt][t]);
+        for (int t = 0; t < NT; ++t) {
+          if constexpr (F16A) acc[mt][t] = mfma16_f16(av, bf[t], acc[mt][t]);
+          else acc[mt][t] = mfma16(av, bf[t], acc[mt][t]);
+        }
       }
     }
   };
@@ -521,7 +538,7 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
   // LDS store does not wait behind the weight loads (the load counter is in
   // order).  Past the last block the loads are clamped to it (redundant, in
   // bounds).  The ring is indexed by compile-time constants.
-  constexpr int D = WDT == SCR_W_BF16 ? 2 : 4;
+  constexpr int D = (WDT == SCR_W_BF16 || NT == 4) ? 2 : 4;  // four 4-bit tiles per wave: two blocks
   BFrag<WDT, NT> ring[D];
   AStage A0;
   // down: the route and top-k weight of each output row of this lane, read
@@ -572,10 +589,12 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
     for (int i = 0; i < 4; ++i) {
       const int pos = c.m0 + mt * 16 + grp * 4 + i;
       if (GATEUP) {
+        // F16A: the row's power of two comes off after the global scale
+        const float rs = F16A ? row_rs[mt * 16 + grp * 4 + i] : 1.0f;
 #pragma unroll
         for (int t = 0; t < NT / 2; ++t) {
           const int hc = c.ncol0 + 16 * t + col;
-          const float hv = silu_mul(c.gs * acc[mt][t][i], c.gs * acc[mt][t + NT / 2][i]);
+          const float hv = silu_mul(c.gs * acc[mt][t][i] * rs, c.gs * acc[mt][t + NT / 2][i] * rs);
           a.h[(size_t)pos * a.I + hc] = static_cast<bf16>(hv);
         }
       } else {
@@ -597,6 +616,8 @@ template <int WDT, int MT, int NT, bool GATEUP>
 __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, int ntx, int pslices) {
   __shared__ __attribute__((aligned(16))) bf16 As[2][MT * 16][kAStride];
   __shared__ int src_row[MT * 16];  // element offset of each staged row, -1 = zero row
+  // F16A gate/up: 2^-xe of each pass row's token, undoing its fp16 scaling
+  __shared__ float row_rs[WideF16A<WDT, GATEUP>::value ? MT * 16 : 1];
 
   // XCD-aware order: consecutive workgroups go to different XCDs, so bucket j
   // and all its N tiles and pass slices land on XCD (j mod 8) and share its L2
@@ -659,26 +680,31 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
     c.rows = min(MT * 16, p1 - m0);
     for (int i = c.tid; i < MT * 16; i += kGemmThreads) {
       int off = -1;
+      float rs = 1.0f;
       if (i < c.rows) {
         if (GATEUP) {
           const int r = a.sorted_routes[m0 + i];
-          if (r >= 0 && r < a.R) off = (r / a.k) * arow_len;
+          if (r >= 0 && r < a.R) {
+            off = (r / a.k) * arow_len;
+            if constexpr (WideF16A<WDT, GATEUP>::value) rs = __builtin_ldexpf(1.0f, -a.xe[r / a.k]);
+          }
         } else {
           off = (m0 + i) * arow_len;
         }
       }
       src_row[i] = off;
+      if constexpr (WideF16A<WDT, GATEUP>::value) row_rs[i] = rs;
     }
     __syncthreads();
     switch (c.rows / 16) {
-      case 1: gemm_pass<WDT, MT, NT, GATEUP, 1>(a, c, rowp, scp, As, src_row); break;
-      case 2: if constexpr (MT >= 2) gemm_pass<WDT, MT, NT, GATEUP, 2>(a, c, rowp, scp, As, src_row); break;
-      case 3: if constexpr (MT >= 3) gemm_pass<WDT, MT, NT, GATEUP, 3>(a, c, rowp, scp, As, src_row); break;
-      case 4: if constexpr (MT >= 4) gemm_pass<WDT, MT, NT, GATEUP, 4>(a, c, rowp, scp, As, src_row); break;
-      case 5: if constexpr (MT >= 5) gemm_pass<WDT, MT, NT, GATEUP, 5>(a, c, rowp, scp, As, src_row); break;
-      case 6: if constexpr (MT >= 6) gemm_pass<WDT, MT, NT, GATEUP, 6>(a, c, rowp, scp, As, src_row); break;
-      case 7: if constexpr (MT >= 7) gemm_pass<WDT, MT, NT, GATEUP, 7>(a, c, rowp, scp, As, src_row); break;
-      case 8: if constexpr (MT >= 8) gemm_pass<WDT, MT, NT, GATEUP, 8>(a, c, rowp, scp, As, src_row); break;
+      case 1: gemm_pass<WDT, MT, NT, GATEUP, 1>(a, c, rowp, scp, As, src_row, row_rs); break;
+      case 2: if constexpr (MT >= 2) gemm_pass<WDT, MT, NT, GATEUP, 2>(a, c, rowp, scp, As, src_row, row_rs); break;
+      case 3: if constexpr (MT >= 3) gemm_pass<WDT, MT, NT, GATEUP, 3>(a, c, rowp, scp, As, src_row, row_rs); break;
+      case 4: if constexpr (MT >= 4) gemm_pass<WDT, MT, NT, GATEUP, 4>(a, c, rowp, scp, As, src_row, row_rs); break;
+      case 5: if constexpr (MT >= 5) gemm_pass<WDT, MT, NT, GATEUP, 5>(a, c, rowp, scp, As, src_row, row_rs); break;
+      case 6: if constexpr (MT >= 6) gemm_pass<WDT, MT, NT, GATEUP, 6>(a, c, rowp, scp, As, src_row, row_rs); break;
+      case 7: if constexpr (MT >= 7) gemm_pass<WDT, MT, NT, GATEUP, 7>(a, c, rowp, scp, As, src_row, row_rs); break;
+      case 8: if constexpr (MT >= 8) gemm_pass<WDT, MT, NT, GATEUP, 8>(a, c, rowp, scp, As, src_row, row_rs); break;
       default: break;
     }
     __syncthreads();  // src_row and As are reused by the next pass
@@ -728,10 +754,6 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
 // the NVFP4 wide gate/up runs on fp16 (half the decode work of bf16: see
 // BFrag<SCR_W_NVFP4>::get_f16); every other wide pass on bf16
 // (W4A4: both GEMMs, whose activations are exact fp16 values)
-template <int WDT, bool GATEUP>
-struct WideF16A {
-  static constexpr bool value = (WDT == SCR_W_NVFP4 && GATEUP) || WDT == SCR_W_NVFP4_A4;
-};
 
 // x as fp16 for the F16A gate/up, one wave per token: the row is scaled by
 // 2^e, e = 15 - (the exponent of its largest magnitude in frexp form), which
@@ -1735,18 +1757,23 @@ static int launch_wide_gemms(const GemmArgs& a, int max_active, hipEvent_t* mark
   return SCR_OK;
 }
 
-template <int WDT, int MT, int NT>
+// NTG / NTD: row tiles of 16 weight rows per wave in gate/up and in down
+template <int WDT, int MT, int NTG, int NTD>
 static int launch_gemms(const GemmArgs& a, int max_active, hipEvent_t* marks, hipStream_t s) {
   const int rows8 = (max_active + 7) / 8;     // buckets per XCD (rounded up)
-  const int ntx_gu = (a.I + 4 * 8 * NT - 1) / (4 * 8 * NT);
-  const int ntx_dn = (a.H + 4 * 16 * NT - 1) / (4 * 16 * NT);
+  const int ntx_gu = (a.I + 4 * 8 * NTG - 1) / (4 * 8 * NTG);
+  const int ntx_dn = (a.H + 4 * 16 * NTD - 1) / (4 * 16 * NTD);
   const int ps_gu = pass_slices(a, max_active, MT * 16, 8 * rows8 * ntx_gu);
   const int ps_dn = pass_slices(a, max_active, MT * 16, 8 * rows8 * ntx_dn);
-  hipLaunchKernelGGL((moe_gemm_kernel<WDT, MT, NT, true>), dim3(8 * rows8 * ntx_gu * ps_gu), dim3(kGemmThreads), 0,
+  if constexpr (WDT == SCR_W_NVFP4) {  // x's fp16 copy for the fp16 gate/up
+    const int rc = launch_x_to_f16(a, s);
+    if (rc) return rc;
+  }
+  hipLaunchKernelGGL((moe_gemm_kernel<WDT, MT, NTG, true>), dim3(8 * rows8 * ntx_gu * ps_gu), dim3(kGemmThreads), 0,
                      s, a, ntx_gu, ps_gu);
   SCR_CHECK_LAUNCH();
   if (marks && marks[2]) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
-  hipLaunchKernelGGL((moe_gemm_kernel<WDT, MT, NT, false>), dim3(8 * rows8 * ntx_dn * ps_dn), dim3(kGemmThreads), 0,
+  hipLaunchKernelGGL((moe_gemm_kernel<WDT, MT, NTD, false>), dim3(8 * rows8 * ntx_dn * ps_dn), dim3(kGemmThreads), 0,
                      s, a, ntx_dn, ps_dn);
   SCR_CHECK_LAUNCH();
   if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
@@ -1794,9 +1821,13 @@ static int launch_w4a8(const GemmArgs& a, int max_active, hipEvent_t* marks, hip
 template <int WDT>
 static int run_gemms(const scr_tile_cfg& cfg, const GemmArgs& a, int max_active, hipEvent_t* marks,
                      hipStream_t s) {
-  if (cfg.m_chunk == 32) return launch_gemms<WDT, 2, 2>(a, max_active, marks, s);
+  // few rows: the 4-bit gate/up streams four tiles per wave (twice the weight
+  // bytes per block and barrier of two; measured 13-17 % faster for NVFP4 at
+  // 2-10 rows per expert, where the down measured slower that way)
+  constexpr int NTG = (WDT == SCR_W_NVFP4 || WDT == SCR_W_MXFP4) ? 4 : 2;
+  if (cfg.m_chunk == 32) return launch_gemms<WDT, 2, NTG, 2>(a, max_active, marks, s);
   if (wide_gemms_fit<WDT>(a)) return launch_wide_gemms<WDT, 7>(a, max_active, marks, s);
-  return launch_gemms<WDT, 7, 2>(a, max_active, marks, s);
+  return launch_gemms<WDT, 7, 2, 2>(a, max_active, marks, s);
 }
 
 // the combine, its rank group the smallest of 4, 8, 12, 16 that holds k
@@ -1836,8 +1867,18 @@ extern "C" int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_c
   // weight format) and wide N tiles (MFMA reuse)
   const bool small = per_expert <= 16;
   cfg->m_chunk = small ? 32 : 112;
-  cfg->n_tile_gu = 4 * 8 * 2;    // h columns per workgroup
-  cfg->n_tile_dn = 4 * 16 * 2;   // output columns per workgroup
+  const bool four_bit = wdtype == SCR_W_NVFP4 || wdtype == SCR_W_MXFP4;
+  if (small) {
+    // four waves; gate/up 8 h columns per weight tile pair, down 16 columns per tile
+    cfg->n_tile_gu = 4 * 8 * (four_bit ? 4 : 2);
+    cfg->n_tile_dn = 4 * 16 * 2;
+  } else {
+    // the wide kernels' N chunk (eight waves of two or four tiles), where the
+    // layer's H and I fit their tiling
+    const int ntw = wdtype == SCR_W_BF16 ? 2 : 4;
+    cfg->n_tile_gu = scr::kWideWaves * 8 * ntw;
+    cfg->n_tile_dn = scr::kWideWaves * 16 * ntw;
+  }
   cfg->wdtype = wdtype;
   return SCR_OK;
 }
