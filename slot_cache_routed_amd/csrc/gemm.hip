@@ -233,13 +233,14 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 
 // ------------------------------------------------------------ grouped GEMM
 //
-// One workgroup = one (active bucket, N tile).  It walks every row of its
-// bucket in passes of up to MT*16 rows; per pass the K dimension is consumed
-// in blocks of 128.  Activation rows (x gathered through sorted_routes for
-// gate/up, contiguous h rows for down) are staged once per block in LDS and
+// One workgroup = one (active bucket, N tile, pass slice).  A bucket's rows
+// are walked in passes of up to MT*16 rows (a workgroup takes every pslices-th
+// pass); per pass the K dimension is consumed in blocks of 128.  Activation
+// rows (x, or for NVFP4 its fp16 copy, gathered through sorted_routes for
+// gate/up; contiguous h rows for down) are staged once per block in LDS and
 // shared by the 4 waves; each wave streams its own weight rows straight into
-// registers one block ahead and decodes NVFP4 there, so every weight byte is
-// fetched and decoded once per pass.
+// registers ahead of use and decodes the narrow formats there, so every
+// weight byte is fetched and decoded once per pass.
 //
 // K order inside a 128-wide block (A and B use the same one, so the sum is the
 // full dot product; it is fixed, so every path that runs this kernel gets the
@@ -714,14 +715,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
 // ------------------------------------------------------- wide-tile GEMM
 //
 // For chunks with many rows per expert (the MFMA-bound shapes).  One
-// workgroup of EW waves owns one active bucket and a contiguous range of its
-// N chunks; the weight stream of that range never restarts (the prefetch ring
-// runs across chunk boundaries).  Each wave owns NTW row tiles of 16 weight
-// rows per chunk (gate/up: NTW/2 gate tiles and the matching up tiles; down:
-// NTW tiles of output columns), so every activation fragment read from LDS
-// feeds NTW MFMAs.  Two workgroups share a CU (256 registers per wave), so
-// the decode, the waits and the barriers of one overlap the MFMAs of the
-// other.
+// workgroup of EW = 8 waves (two per SIMD, 256 registers each, one workgroup
+// per CU) owns one active bucket, a contiguous range of its N chunks and a
+// slice of its row passes; within a pass the weight stream never restarts
+// (the prefetch ring runs across chunk boundaries).  Each wave owns NTW row
+// tiles of 16 weight rows per chunk (gate/up: NTW/2 gate tiles and the
+// matching up tiles; down: NTW tiles of output columns), so every activation
+// fragment read from LDS feeds NTW MFMAs, and the two waves of a SIMD
+// overlap one another's decode, waits and barriers with their MFMAs.
 //
 // Activations reach LDS by direct global-to-LDS loads (no register staging):
 // K-block buffers, each a [rows][128] bf16 tile whose 16-byte chunks are
