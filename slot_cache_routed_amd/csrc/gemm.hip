@@ -570,6 +570,10 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
   auto step = [&](int kb, const BFrag<WDT, NT>& bc, BFrag<WDT, NT>& bl) {
     load_a(A0, min(kb + 1, nkb - 1));
     load_b(bl, min(kb + D - 1, nkb - 1));
+    // the narrow formats' weight loads stay ahead of the block's decode and
+    // products (left to itself the compiler sinks them to the block's end,
+    // so fewer bytes are in flight: measured 3-10 % slower)
+    if constexpr (WDT != SCR_W_BF16) __builtin_amdgcn_sched_barrier(0);
     compute(bc, kb & 1);
     store_a(A0, (kb + 1) & 1);
     __syncthreads();
