@@ -1722,6 +1722,9 @@ static bool wide_gemms_fit(const GemmArgs& a) {
 // slices add no weight traffic; a slice past a bucket's last pass exits at
 // once.
 constexpr int kFillWorkgroups = 1024;
+// below this many buckets one workgroup per bucket cannot fill the chip
+constexpr int kFewBuckets = 256;
+constexpr int kCUs = 256;  // compute units of the chip
 static int pass_slices(const GemmArgs& a, int max_active, int pass_rows, int base_wgs) {
   const long long avg_rows = ((long long)a.R + max_active - 1) / max_active + a.B - 1;  // padded
   const long long avg_passes = (avg_rows + pass_rows - 1) / pass_rows;
@@ -1742,9 +1745,14 @@ static int launch_wide_gemms(const GemmArgs& a, int max_active, hipEvent_t* mark
   // down: one workgroup per bucket walks all of its N chunks (its h block
   // made resident once) at many rows per expert; measured 6-14 % faster for
   // bf16, FP8 and MXFP4 at 80 rows per expert, no faster for NVFP4 (its bf16
-  // weight decode dominates), which keeps two chunks per workgroup
-  const bool one_dn = WDT != SCR_W_NVFP4 && (long long)a.R >= 32ll * a.E;
-  const int g_dn = one_dn ? 1 : (nch_dn >= 2 ? nch_dn / 2 : 1);
+  // weight decode dominates), which keeps two chunks per workgroup.  When
+  // those workgroups (with their pass slices) could not fill the chip, the
+  // chunks go to workgroups of their own instead (bf16 at 8 experts 72 ->
+  // 47 us; at 64 experts the merged grid fills the chip and stays)
+  const bool one_dn = WDT != SCR_W_NVFP4 && (long long)a.R >= 32ll * a.E &&
+                      8 * rows8 * pass_slices(a, max_active, MT * 16, 8 * rows8) >= kCUs;
+  const bool split_dn = WDT != SCR_W_NVFP4 && (long long)a.R >= 32ll * a.E && !one_dn;
+  const int g_dn = one_dn ? 1 : split_dn ? nch_dn : (nch_dn >= 2 ? nch_dn / 2 : 1);
   if constexpr (WDT == SCR_W_NVFP4) {
     const int rc = launch_x_to_f16(a, s);
     if (rc) return rc;
@@ -1799,11 +1807,13 @@ static int launch_w4a8(const GemmArgs& a, int max_active, hipEvent_t* marks, hip
   // (gate/up) or its h block made resident (down) once, not once per
   // workgroup (measured 3 % and 5 % faster at 80 rows per expert; the NVFP4
   // wide kernel, with its weight decode, gained nothing from it).  Few rows:
-  // the chunks split over workgroups, for parallelism.
-  const bool many_rows = (long long)a.R >= 32ll * a.E;
+  // the chunks split over workgroups, for parallelism; and with fewer buckets
+  // than CUs, every chunk a workgroup of its own (8 experts: 98 -> 69 us).
+  const bool few_buckets = max_active < kFewBuckets;
+  const bool many_rows = (long long)a.R >= 32ll * a.E && !few_buckets;
   const int nch_dn = a.H / (16 * NTW * kWideWaves);
   const int g_gu = many_rows ? 1 : a.I / (8 * NTW * kWideWaves);
-  const int g_dn = many_rows ? 1 : (nch_dn >= 2 ? nch_dn / 2 : 1);
+  const int g_dn = many_rows ? 1 : few_buckets ? nch_dn : (nch_dn >= 2 ? nch_dn / 2 : 1);
   const int ps_gu = pass_slices(a, max_active, 7 * 16, 8 * rows8 * g_gu);
   const int ps_dn = pass_slices(a, max_active, 7 * 16, 8 * rows8 * g_dn);
   hipLaunchKernelGGL((moe_w4a8_kernel<7, true, kWideWaves, NTW, false>), dim3(8 * rows8 * g_gu * ps_gu),
