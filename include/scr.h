@@ -403,10 +403,10 @@ int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cf
  *     weight codes times their block scales are exact fp16 values, so both
  *     GEMMs run on the fp16 MFMA over exact operands, the global scales applied
  *     to the fp32 accumulators.
- *   Both need down_input_scale and H, I multiples of 512 (SCR_ENOTSUP
- *   otherwise, nothing launched).
+ *   Both need down_input_scale, H a multiple of 512 and I a multiple of 256
+ *   (SCR_ENOTSUP otherwise, nothing launched).
  * SCR_W_NVFP4 with many rows per expert (the wide kernels: cfg.m_chunk 112,
- * H and I multiples of 512): the gate/up runs on the fp16 MFMA.  Between
+ * H a multiple of 512 and I of 256): the gate/up runs on the fp16 MFMA.  Between
  * marks 1 and 2 (so inside the gate/up time) each row of x is copied to
  * fp16 times 2^e, e putting the row's largest magnitude in [2^14, 2^15); the
  * weights decode exactly to fp16 (e2m1 times e4m3 fits), and the fp32

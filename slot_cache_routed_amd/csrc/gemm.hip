@@ -734,7 +734,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void moe_gemm_kernel(GemmArgs a, i
 // reads hit distinct banks.
 // The buffers are separate arrays so that the compiler can tell a read of one
 // from the direct loads still in flight into the other.
-constexpr int kWideBufs = 4;  // activation K-block buffers in LDS (loaded kWideBufs - 1 blocks ahead)
+// activation K-block buffers in LDS (loaded NBUF - 1 blocks ahead): four
+// where the K blocks of a GEMM come in fours, else two (K a multiple of 256)
+constexpr int kWideBufs = 4;
 constexpr int kWideRing = 2;  // NVFP4 weight ring depth in K blocks (deeper measured slower)
 constexpr int kWideStage = 4096;  // bytes of LDS per wave for the epilogue tile (16 rows x 64 fp32)
 
@@ -844,7 +846,7 @@ struct BLoads {  // vector memory instructions per wave for one K block of weigh
   static constexpr int value = WDT == SCR_W_BF16 ? 4 * NTW : 2 * NTW;  // fp8: two code loads; fp4: codes + scales
 };
 
-template <int WDT, int MT, bool GATEUP, int EW, int NTW, int MTC>
+template <int WDT, int MT, bool GATEUP, int EW, int NTW, int MTC, int NBUF>
 __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row, const int* row_route,
                                           const float* row_w, const float* row_rs, bf16* As0, bf16* As1, bf16* As2,
                                           bf16* As3, uint32_t* stg, int m0, __amdgpu_buffer_rsrc_t wrsrc,
@@ -857,6 +859,7 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
   constexpr int tile_bytes = WFmt<WDT>::tile;
   constexpr int stile_bytes = WFmt<WDT>::stile;
   constexpr bool F16A = WideF16A<WDT, GATEUP>::value;  // fp16 activations and weights
+  static_assert(NBUF == 2 || NBUF == 4, "two or four activation buffers");
   bf16* const bufs[kWideBufs] = {As0, As1, As2, As3};
 
   // activations through a buffer resource over x (gate/up; its fp16 copy
@@ -1041,15 +1044,15 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
   // weight ring depth (blocks): HBM latency under load is about two blocks
   // of compute, so the weights of block s are requested at block s - D + 1
   constexpr int D = WDT == SCR_W_BF16 ? 2 : kWideRing;
-  constexpr int U = D > kWideBufs ? D : kWideBufs;  // unroll: ring and buffers indexed statically
+  constexpr int U = D > NBUF ? D : NBUF;  // unroll: ring and buffers indexed statically
   constexpr int NB = BLoads<WDT, NTW>::value;
   const int s0 = c_begin * nkb, s1 = c_end * nkb;  // flat steps s = chunk * nkb + kb
-  constexpr int LA = kWideBufs - 1;  // activation blocks loaded ahead
+  constexpr int LA = NBUF - 1;  // activation blocks loaded ahead
   BFrag<WDT, NTW> ring[D];
-  // Down (K = I = kWideBufs blocks) keeps the bucket's whole h block resident
+  // Down (K = I = NBUF blocks) keeps the bucket's whole h block resident
   // for all of its chunks: loaded once, no further activation loads or
   // barriers.  Gate/up streams x blocks LA ahead through the buffers.
-  const bool resident = !GATEUP && nkb == kWideBufs;
+  const bool resident = !GATEUP && nkb == NBUF;
   // blocks s0 .. s0+LA-1 of the activations (all of them when resident),
   // then the weights of blocks s0 .. s0+D-2
 #pragma unroll
@@ -1075,11 +1078,11 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
       for (int i = 0; i < U; ++i) {
         const int kb = kb0 + i, s = ch * nkb + kb;
         const BFrag<WDT, NTW>& bc = ring[i % D];
-        const bf16* buf = bufs[i % kWideBufs];
+        const bf16* buf = bufs[i % NBUF];
         // the activations of block kb + LA into the buffer block kb - 1 used
         // (every wave has finished it), then the weights of block s + D - 1
         // into the ring slot block s - 1 used
-        if (!resident) load_a(bufs[(i + LA) % kWideBufs], (kb + LA) % nkb);
+        if (!resident) load_a(bufs[(i + LA) % NBUF], (kb + LA) % nkb);
         load_b(ring[(i + D - 1) % D], min(s + D - 1, s1 - 1));
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
@@ -1118,12 +1121,12 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
   __builtin_amdgcn_s_barrier();
 }
 
-template <int WDT, int MT, bool GATEUP, int EW, int NTW>
+template <int WDT, int MT, bool GATEUP, int EW, int NTW, int NBUF>
 __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int groups, int pslices) {
   __shared__ __attribute__((aligned(1024))) bf16 As0[MT * 16 * kKB];
   __shared__ __attribute__((aligned(1024))) bf16 As1[MT * 16 * kKB];
-  __shared__ __attribute__((aligned(1024))) bf16 As2[MT * 16 * kKB];
-  __shared__ __attribute__((aligned(1024))) bf16 As3[MT * 16 * kKB];
+  __shared__ __attribute__((aligned(1024))) bf16 As2[NBUF > 2 ? MT * 16 * kKB : 8];
+  __shared__ __attribute__((aligned(1024))) bf16 As3[NBUF > 3 ? MT * 16 * kKB : 8];
   __shared__ int src_row[MT * 16];
   // down: the route of each pass row (-1 for padding) and its top-k weight,
   // read once per pass so that the epilogue does no dependent global loads
@@ -1199,7 +1202,7 @@ __global__ __launch_bounds__(64 * EW) void moe_wide_kernel(GemmArgs a, int group
 #define SCR_WIDE_PASS(n)                                                                                   \
   case n:                                                                                                  \
     if constexpr (MT >= n)                                                                                 \
-      wide_pass<WDT, MT, GATEUP, EW, NTW, n>(a, src_row, row_route, row_w, row_rs, As0, As1, As2, As3, stg, m0, \
+      wide_pass<WDT, MT, GATEUP, EW, NTW, n, NBUF>(a, src_row, row_route, row_w, row_rs, As0, As1, As2, As3, stg, m0, \
                                              wrsrc, toff0, soff0, gs, nkb, c_begin, c_end);                     \
     break;
     switch (rows / 16) {
@@ -1404,9 +1407,9 @@ constexpr int kUnitScale = 127;  // e8m0 code of 2^0
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// RES: down with K = I = kWideBufs blocks keeps the bucket's whole h block
+// RES: down with K = I = NBUF blocks keeps the bucket's whole h block
 // resident in LDS (a compile-time choice: the run-time one spills registers)
-template <int MT, bool GATEUP, int EW, int NTW, int MTC, bool RES>
+template <int MT, bool GATEUP, int EW, int NTW, int MTC, bool RES, int NBUF>
 __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row, const int* row_route, const float* row_w, uint8_t* As0, uint8_t* As1,
                                           uint8_t* As2, uint8_t* As3, uint32_t* stg, int m0,
                                           __amdgpu_buffer_rsrc_t wrsrc, const int* toff0, const int* soff0,
@@ -1415,6 +1418,7 @@ __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row,
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   constexpr int CT = GATEUP ? EW * NTW / 2 : EW * NTW;  // row tiles per chunk and tensor half
+  static_assert(NBUF == 2 || NBUF == 4, "two or four activation buffers");
   uint8_t* const bufs[kWideBufs] = {As0, As1, As2, As3};
 
   // MXFP8 activations through a buffer resource over x's codes (gate/up) or h's (down)
@@ -1522,10 +1526,10 @@ __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row,
   };
 
   constexpr int D = kWideRing;
-  constexpr int U = D > kWideBufs ? D : kWideBufs;
+  constexpr int U = D > NBUF ? D : NBUF;
   constexpr int NB = 2 * NTW;  // codes + scale per tile
   const int s0 = c_begin * nkb, s1 = c_end * nkb;
-  constexpr int LA = kWideBufs - 1;
+  constexpr int LA = NBUF - 1;
   BFrag<SCR_W_MXFP4, NTW> ring[D];
   constexpr bool resident = RES;
 #pragma unroll
@@ -1550,8 +1554,8 @@ __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row,
       for (int i = 0; i < U; ++i) {
         const int kb = kb0 + i, s = ch * nkb + kb;
         const BFrag<SCR_W_MXFP4, NTW>& bc = ring[i % D];
-        const uint8_t* buf = bufs[i % kWideBufs];
-        if (!resident) load_a(bufs[(i + LA) % kWideBufs], (kb + LA) % nkb);
+        const uint8_t* buf = bufs[i % NBUF];
+        if (!resident) load_a(bufs[(i + LA) % NBUF], (kb + LA) % nkb);
         load_b(ring[(i + D - 1) % D], min(s + D - 1, s1 - 1));
 #pragma unroll
         for (int mt = 0; mt < MTC; ++mt) {
@@ -1578,12 +1582,12 @@ __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row,
   __builtin_amdgcn_s_barrier();
 }
 
-template <int MT, bool GATEUP, int EW, int NTW, bool RES>
+template <int MT, bool GATEUP, int EW, int NTW, bool RES, int NBUF>
 __global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int groups, int pslices) {
   __shared__ __attribute__((aligned(1024))) uint8_t As0[MT * 16 * kKB];
   __shared__ __attribute__((aligned(1024))) uint8_t As1[MT * 16 * kKB];
-  __shared__ __attribute__((aligned(1024))) uint8_t As2[MT * 16 * kKB];
-  __shared__ __attribute__((aligned(1024))) uint8_t As3[MT * 16 * kKB];
+  __shared__ __attribute__((aligned(1024))) uint8_t As2[NBUF > 2 ? MT * 16 * kKB : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t As3[NBUF > 3 ? MT * 16 * kKB : 16];
   __shared__ int src_row[MT * 16];
   __shared__ int row_route[GATEUP ? 1 : MT * 16];
   __shared__ float row_w[GATEUP ? 1 : MT * 16];
@@ -1640,7 +1644,7 @@ __global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int group
 #define SCR_W4A8_PASS(n)                                                                                     \
   case n:                                                                                                    \
     if constexpr (MT >= n)                                                                                   \
-      w4a8_pass<MT, GATEUP, EW, NTW, n, RES>(a, src_row, row_route, row_w, As0, As1, As2, As3, stg, m0,   \
+      w4a8_pass<MT, GATEUP, EW, NTW, n, RES, NBUF>(a, src_row, row_route, row_w, As0, As1, As2, As3, stg, m0,   \
                                              wrsrc, toff0, soff0, nkb, c_begin, c_end);                        \
     break;
     switch (rows / 16) {
@@ -1699,6 +1703,10 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
 }
 
 constexpr int kWideWaves = 8;  // two waves per SIMD in one workgroup per CU
+static_assert(kWideRing == 2, "the ring steps with either buffer count");
+// activation buffers of a wide GEMM over nkb K blocks: four where they come
+// in fours, two where they come in pairs, 0 (the wide kernels do not fit)
+static int wide_nbuf(int nkb) { return nkb % 4 == 0 ? 4 : nkb % 2 == 0 ? 2 : 0; }
 template <int WDT>
 struct WideNT {  // row tiles per wave: the bf16 weight ring holds four times the registers
   static constexpr int value = WDT == SCR_W_BF16 ? 2 : 4;
@@ -1707,9 +1715,9 @@ struct WideNT {  // row tiles per wave: the bf16 weight ring holds four times th
 template <int WDT>
 static bool wide_gemms_fit(const GemmArgs& a) {
   constexpr int NTW = WideNT<WDT>::value;
-  // K blocks cycle through the LDS buffers and the weight ring in steps of U
-  constexpr int U = WDT == SCR_W_BF16 ? kWideBufs : (kWideRing > kWideBufs ? kWideRing : kWideBufs);
-  return (a.H / kKB) % U == 0 && (a.I / kKB) % U == 0 && a.I % (8 * NTW * kWideWaves) == 0 &&
+  // K blocks cycle through the LDS buffers and the two-block weight ring in
+  // steps of the buffer count (four, or two): an even count of K blocks
+  return wide_nbuf(a.H / kKB) > 0 && wide_nbuf(a.I / kKB) > 0 && a.I % (8 * NTW * kWideWaves) == 0 &&
          a.H % (16 * NTW * kWideWaves) == 0;
 }
 
@@ -1759,12 +1767,17 @@ static int launch_wide_gemms(const GemmArgs& a, int max_active, hipEvent_t* mark
   }
   const int ps_gu = pass_slices(a, max_active, MT * 16, 8 * rows8 * g_gu);
   const int ps_dn = pass_slices(a, max_active, MT * 16, 8 * rows8 * g_dn);
-  hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, true, kWideWaves, NTW>), dim3(8 * rows8 * g_gu * ps_gu),
-                     dim3(64 * kWideWaves), 0, s, a, g_gu, ps_gu);
+  const dim3 grid_gu(8 * rows8 * g_gu * ps_gu), grid_dn(8 * rows8 * g_dn * ps_dn), block(64 * kWideWaves);
+  if (wide_nbuf(a.H / kKB) == 4)
+    hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, true, kWideWaves, NTW, 4>), grid_gu, block, 0, s, a, g_gu, ps_gu);
+  else
+    hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, true, kWideWaves, NTW, 2>), grid_gu, block, 0, s, a, g_gu, ps_gu);
   SCR_CHECK_LAUNCH();
   if (marks && marks[2]) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
-  hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, false, kWideWaves, NTW>), dim3(8 * rows8 * g_dn * ps_dn),
-                     dim3(64 * kWideWaves), 0, s, a, g_dn, ps_dn);
+  if (wide_nbuf(a.I / kKB) == 4)
+    hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, false, kWideWaves, NTW, 4>), grid_dn, block, 0, s, a, g_dn, ps_dn);
+  else
+    hipLaunchKernelGGL((moe_wide_kernel<WDT, MT, false, kWideWaves, NTW, 2>), grid_dn, block, 0, s, a, g_dn, ps_dn);
   SCR_CHECK_LAUNCH();
   if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
   return SCR_OK;
@@ -1816,16 +1829,23 @@ static int launch_w4a8(const GemmArgs& a, int max_active, hipEvent_t* marks, hip
   const int g_dn = many_rows ? 1 : few_buckets ? nch_dn : (nch_dn >= 2 ? nch_dn / 2 : 1);
   const int ps_gu = pass_slices(a, max_active, 7 * 16, 8 * rows8 * g_gu);
   const int ps_dn = pass_slices(a, max_active, 7 * 16, 8 * rows8 * g_dn);
-  hipLaunchKernelGGL((moe_w4a8_kernel<7, true, kWideWaves, NTW, false>), dim3(8 * rows8 * g_gu * ps_gu),
-                     dim3(64 * kWideWaves), 0, s, a, g_gu, ps_gu);
+  const dim3 grid_gu(8 * rows8 * g_gu * ps_gu), grid_dn(8 * rows8 * g_dn * ps_dn), block(64 * kWideWaves);
+  if (wide_nbuf(a.H / kKB) == 4)
+    hipLaunchKernelGGL((moe_w4a8_kernel<7, true, kWideWaves, NTW, false, 4>), grid_gu, block, 0, s, a, g_gu, ps_gu);
+  else
+    hipLaunchKernelGGL((moe_w4a8_kernel<7, true, kWideWaves, NTW, false, 2>), grid_gu, block, 0, s, a, g_gu, ps_gu);
   SCR_CHECK_LAUNCH();
   if (marks && marks[2]) SCR_CHECK_HIP(hipEventRecord(marks[2], s));
-  if (a.I / kKB == kWideBufs)
-    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, true>), dim3(8 * rows8 * g_dn * ps_dn),
-                       dim3(64 * kWideWaves), 0, s, a, g_dn, ps_dn);
+  // down: the bucket's whole h block resident in the buffers when it fits them
+  const int nkb_dn = a.I / kKB, nbuf_dn = wide_nbuf(nkb_dn);
+  if (nbuf_dn == 4 && nkb_dn == 4)
+    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, true, 4>), grid_dn, block, 0, s, a, g_dn, ps_dn);
+  else if (nbuf_dn == 4)
+    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, false, 4>), grid_dn, block, 0, s, a, g_dn, ps_dn);
+  else if (nkb_dn == 2)
+    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, true, 2>), grid_dn, block, 0, s, a, g_dn, ps_dn);
   else
-    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, false>), dim3(8 * rows8 * g_dn * ps_dn),
-                       dim3(64 * kWideWaves), 0, s, a, g_dn, ps_dn);
+    hipLaunchKernelGGL((moe_w4a8_kernel<7, false, kWideWaves, NTW, false, 2>), grid_dn, block, 0, s, a, g_dn, ps_dn);
   SCR_CHECK_LAUNCH();
   if (marks && marks[3]) SCR_CHECK_HIP(hipEventRecord(marks[3], s));
   return SCR_OK;
@@ -1975,7 +1995,7 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   // of the A8/A4 formats; otherwise empty: the gate/up kernel clears the
   // flags and reports the activation scales itself)
   if (act_quant && !scr::act_quant_fits(a, view->wdtype)) {
-    scr::set_error("forward: W4A8 and W4A4 need H and I multiples of 512 (H=%d I=%d)", H, I);
+    scr::set_error("forward: W4A8 and W4A4 need H a multiple of 512 and I of 256 (H=%d I=%d)", H, I);
     return SCR_ENOTSUP;
   }
   if (marks && marks[0]) SCR_CHECK_HIP(hipEventRecord(marks[0], stream));

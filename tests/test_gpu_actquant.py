@@ -222,7 +222,10 @@ def _check_layer(mode, env, T, E, k, H, I, sc, sc2, end_to_end=True):
 # for the fullest buckets), I = 512 resident in down and H streamed
 @pytest.mark.parametrize("mode", ["w4a8", "w4a4"])
 @pytest.mark.parametrize("T,E,k,H,I", [(64, 32, 4, 512, 512), (384, 16, 4, 512, 512), (500, 12, 3, 1024, 512),
-                                       (96, 8, 2, 2048, 512), (200, 16, 4, 512, 1024)])
+                                       (96, 8, 2, 2048, 512), (200, 16, 4, 512, 1024),
+                                       # K blocks in pairs: the two-buffer kernels (I = 768 streams
+                                       # h through them; I = 256 keeps it resident)
+                                       (384, 16, 4, 512, 768), (384, 16, 4, 512, 256)])
 def test_activation_quantising_layer_vs_oracle_and_stream(mode, T, E, k, H, I):
     g = np.random.default_rng(T + E)
     sc = (0.5 + g.random(E)).astype(np.float32)

@@ -203,7 +203,10 @@ def test_layer_view_one_layer_cache_three_per_query():
 # oracle's table decode
 @pytest.mark.parametrize("wd", ["nvfp4", "fp8", "mxfp4"])
 @pytest.mark.parametrize("T,E,k,H,I", [(64, 16, 4, 256, 128), (200, 32, 6, 512, 256), (37, 8, 3, 256, 128),
-                                       (384, 16, 4, 512, 512), (500, 12, 3, 1024, 512)])
+                                       (384, 16, 4, 512, 512), (500, 12, 3, 1024, 512),
+                                       # wide kernels with K blocks in pairs (two activation buffers):
+                                       # h streamed (I = 768) and resident (I = 256) in the down
+                                       (384, 16, 4, 512, 768), (384, 16, 4, 512, 256)])
 def test_narrow_format_layer_vs_oracle_and_stream(wd, T, E, k, H, I):
     s = _setup(f"{wd}_{T}_{E}", S=2 * E, W_=8, wdtype=wd, T=T, E=E, k=k, H=H, I=I, NL=2)
     bank = _bank_for(s)
@@ -240,6 +243,22 @@ def test_bf16_wide_tiles_vs_oracle():
     y_ref, _, _ = _oracle(s)
     err = rel_max_err(_y(d), y_ref)
     flush(f"bf16 wide 384x16: rel max err = {err:.3e}")
+    assert err <= TOL_BF16
+    st = _run_stream(s, sc)
+    assert torch.equal(d["y"], st["y"])
+
+
+def test_bf16_wide_tiles_with_k_blocks_in_pairs_vs_oracle():
+    # hidden and intermediate 768 (six K blocks each): the wide-tile kernels
+    # with two activation buffers in both GEMMs
+    s = _setup("wide_bf16_768", S=40, W_=16, wdtype="bf16", T=384, E=16, k=4, H=768, I=768, NL=2)
+    bank = _bank_for(s)
+    sc = np.ones(s["E"], np.float32)
+    d = _run_demand(s, bank, sc)
+    assert d.cfg_used.m_chunk == 112
+    y_ref, _, _ = _oracle(s)
+    err = rel_max_err(_y(d), y_ref)
+    flush(f"bf16 wide 384x16 H=I=768: rel max err = {err:.3e}")
     assert err <= TOL_BF16
     st = _run_stream(s, sc)
     assert torch.equal(d["y"], st["y"])
