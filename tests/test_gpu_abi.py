@@ -1,5 +1,5 @@
-"""The C ABI on the GPU machine: the argument checks of the CPU suite, run where
-the library drives a device (nothing may be enqueued by a rejected call),
+"""The C ABI with a device present: the argument checks of the CPU suite, run
+where the library drives a device (nothing may be enqueued by a rejected call),
 and scr_bank_init against a state written from the host."""
 import numpy as np
 import pytest
