@@ -467,11 +467,11 @@ def long_prefill(args) -> dict:
     tflops = flops / ((gu + dn) * 1e-3) / 1e12
     wbytes = E * (rec - 256)
     # algorithmic bytes per launch: every weight byte once, x read once and h
-    # written once (gate/up); h read once and the per-route bf16 rows written
-    # once (down)
+    # written once (gate/up); h read once and the per-route fp16 rows with
+    # their int8 exponent per 32 columns written once (down)
     w13 = E * (lay.w13_scale_off + (2 * I) * (H // 16) - lay.w13_off)
     w2 = E * (lay.w2_scale_off + H * (I // 16) - lay.w2_off)
-    alg = {"gate_up": w13 + T * H * 2 + R * I * 2, "down": w2 + R * I * 2 + R * H * 2}
+    alg = {"gate_up": w13 + T * H * 2 + R * I * 2, "down": w2 + R * I * 2 + R * H * 2 + R * (H // 32)}
     hbm = None
     tr = _traffic_profile(os.path.join(ROOT, "profiles", "traffic_wide_long_prefill_4096.json"))
     if tr is not None:

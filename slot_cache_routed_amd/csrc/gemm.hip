@@ -113,8 +113,9 @@ __device__ __forceinline__ unsigned nvfp4_pair_f16(unsigned codes, float bv) {
 // Weight formats: bytes of one tile-block (16 rows x 128 columns) of codes
 // and of its block scales, whether the record carries a per-tensor scale,
 // and the per-route row type: fp32 for bf16 weights (their output tolerance
-// is tighter), bf16 for the narrow formats (half the bytes at the
-// large-chunk shapes).
+// is tighter); for the narrow formats fp16 bits scaled per 32 columns (half
+// the bytes of fp32 at the large-chunk shapes, with 11 significant bits where
+// bf16 rows kept 8; see scaled_row16).
 template <int WDT>
 struct WFmt;
 template <>
@@ -127,19 +128,19 @@ template <>
 struct WFmt<SCR_W_NVFP4> {
   static constexpr int tile = 1024, stile = 128;
   static constexpr bool gscale = true;
-  typedef __bf16 row_t;
+  typedef uint16_t row_t;
 };
 template <>
 struct WFmt<SCR_W_FP8> {
   static constexpr int tile = 2048, stile = 0;
   static constexpr bool gscale = true;
-  typedef __bf16 row_t;
+  typedef uint16_t row_t;
 };
 template <>
 struct WFmt<SCR_W_MXFP4> {
   static constexpr int tile = 1024, stile = 64;
   static constexpr bool gscale = false;
-  typedef __bf16 row_t;
+  typedef uint16_t row_t;
 };
 // W4A4 reads NVFP4 records
 template <>
@@ -160,6 +161,7 @@ struct GemmArgs {
   const int32_t* n_active;
   bf16* h;              // [h_rows][I]
   void* o;              // [R][H] per-route weighted expert outputs (RowT<WDT>)
+  int8_t* oe;           // narrow formats: [R][H / kRowGroup] the rows' group exponents
   int32_t* flags;       // [R]
   const float* input_scale;       // [E] the layer's scales of the gate/up input
   const float* down_input_scale;  // [E] the layer's scales of the down input, or null
@@ -279,6 +281,83 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   unsigned p = __builtin_bit_cast(unsigned, r);
   asm("" : "+v"(p));
   return p;
+}
+
+// Per-route output rows of the narrow formats: fp16 values times 2^e, one e
+// per kRowGroup columns of a row (an int8 beside the row).  e comes from the
+// exponent field f of the group's largest magnitude M: e = 141 - f, capped at
+// 127, puts a normal M in [2^14, 2^15), so every value keeps 11 significant
+// bits relative to the largest of its group.  e lies in [-114, 127]: a zero
+// or tiny group (M < 2^-113) keeps 127, one holding an infinity -114 (inf and
+// NaN values stay what they are).  Magnitudes are compared as their fp32 bit
+// patterns, which order non-negative floats as unsigned integers.
+constexpr int kRowGroup = 32;
+__device__ __forceinline__ int row_group_exp(unsigned mbits) { return min(141 - (int)(mbits >> 23), 127); }
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u32(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+// the largest m over the 16 lanes of a lane group (lanes 16 g .. 16 g + 15,
+// one DPP row): rotations of the row by 1, 2, 4 and 8 lanes leave the row's
+// maximum in every lane (DPP moves, no LDS round trip per step)
+__device__ __forceinline__ unsigned group16_max(unsigned m) {
+  m = max(m, dpp_u32<0x121>(m));  // row_ror:1
+  m = max(m, dpp_u32<0x122>(m));  // row_ror:2
+  m = max(m, dpp_u32<0x124>(m));  // row_ror:4
+  m = max(m, dpp_u32<0x128>(m));  // row_ror:8
+  return m;
+}
+// the largest m over an aligned quad of lanes (two quad_perm DPP steps)
+__device__ __forceinline__ unsigned quad_max(unsigned m) {
+  m = max(m, dpp_u32<0xB1>(m));  // quad_perm [1, 0, 3, 2]
+  m = max(m, dpp_u32<0x4E>(m));  // quad_perm [2, 3, 0, 1]
+  return m;
+}
+// v * 2^e as fp16 bits (nearest even)
+__device__ __forceinline__ uint16_t scaled_row16(float v, float scale) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v * scale));
+}
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+// a and b times 2^e as one packed fp16 pair (a low)
+__device__ __forceinline__ unsigned scaled_pair16(float a, float b, float scale) {
+  const f16x2_t h = {static_cast<_Float16>(a * scale), static_cast<_Float16>(b * scale)};
+  return __builtin_bit_cast(unsigned, h);
+}
+
+// A wave's 16 x OC block of down output (fp32, row-major in LDS) written as
+// fp16 rows scaled per 32 columns: each lane takes 8 consecutive values of a
+// row, so four neighbouring lanes hold one group and share its largest
+// magnitude over two quad DPP steps; the group's first lane writes the
+// exponent.  routes[r] is the route of tile row r (or -1 for padding);
+// c_base the wave's first output column.
+template <int OC>
+__device__ __forceinline__ void store_rows_f16(const float* sf, const int* routes, int lane, uint16_t* o, int8_t* oe,
+                                               int32_t* flags, int H, int c_base, bool set_flag) {
+  static_assert(OC % kRowGroup == 0 && kRowGroup == 32, "four 8-value pieces per group");
+  constexpr int PPR = OC / 8;  // 8-value pieces per row
+  static_assert((16 * PPR) % 64 == 0, "whole rounds of 64 lanes");
+#pragma unroll
+  for (int rd = 0; rd < 16 * PPR / 64; ++rd) {
+    const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
+    const float4 a0 = *reinterpret_cast<const float4*>(sf + rr * OC + pc * 8);
+    const float4 a1 = *reinterpret_cast<const float4*>(sf + rr * OC + pc * 8 + 4);
+    const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) m = fmaxf(m, fabsf(v[c]));
+    const int e = row_group_exp(quad_max(__float_as_uint(m)));
+    const float sc = __builtin_ldexpf(1.0f, e);
+    u32x4 out;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) out[c] = scaled_pair16(v[2 * c], v[2 * c + 1], sc);
+    const int rt = routes[rr];
+    if (rt >= 0) {
+      const int c0 = c_base + pc * 8;
+      *reinterpret_cast<u32x4*>(o + (size_t)rt * H + c0) = out;
+      if ((pc & 3) == 0) oe[(size_t)rt * (H / kRowGroup) + c0 / kRowGroup] = (int8_t)e;
+      if (set_flag && pc == 0) flags[rt] = 1;
+    }
+  }
 }
 
 // 8 e2m1 codes (one dword, low nibble first) times a block scale, as bf16
@@ -604,14 +683,38 @@ __device__ __forceinline__ void gemm_pass(const GemmArgs& a, const PassCtx& c, c
         }
       } else {
         const int r = out_route[mt][i];
-        if (r >= 0 && r < a.R) {
-          const float w = out_w[mt][i];
-          typedef typename RowT<WDT>::type OT;
-          OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + c.ncol0 + col;
+        const float w = out_w[mt][i];
+        typedef typename RowT<WDT>::type OT;
+        float v[NT];
 #pragma unroll
-          for (int t = 0; t < NT; ++t) orow[16 * t] = static_cast<OT>(w * (c.gs * acc[mt][t][i]));
-          if (c.tx == 0 && c.wave == 0 && col == 0) a.flags[r] = 1;
+        for (int t = 0; t < NT; ++t) v[t] = w * (c.gs * acc[mt][t][i]);
+        if constexpr (sizeof(OT) == 4) {
+          if (r >= 0 && r < a.R) {
+            OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + c.ncol0 + col;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) orow[16 * t] = v[t];
+          }
+        } else {
+          // the wave's 16 NT columns of this row are NT / 2 groups of 32 (two
+          // tiles each), spread over the 16 lanes of the lane group; every
+          // lane takes part in the reductions, also those of padding rows
+          static_assert((16 * NT) % kRowGroup == 0, "whole row groups per wave");
+          int e[NT / 2];
+#pragma unroll
+          for (int g = 0; g < NT / 2; ++g)
+            e[g] = row_group_exp(group16_max(__float_as_uint(fmaxf(fabsf(v[2 * g]), fabsf(v[2 * g + 1])))));
+          if (r >= 0 && r < a.R) {
+            OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + c.ncol0 + col;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) orow[16 * t] = scaled_row16(v[t], __builtin_ldexpf(1.0f, e[t / 2]));
+            if (col == 0) {
+#pragma unroll
+              for (int g = 0; g < NT / 2; ++g)
+                a.oe[(size_t)r * (a.H / kRowGroup) + c.ncol0 / kRowGroup + g] = (int8_t)e[g];
+            }
+          }
         }
+        if (r >= 0 && r < a.R && c.tx == 0 && c.wave == 0 && col == 0) a.flags[r] = 1;
       }
     }
   }
@@ -830,7 +933,9 @@ static int launch_x_to_f16(const GemmArgs& a, hipStream_t s) {
   const dim3 grid((a.T + 3) / 4), block(256);
   uint16_t* x16 = const_cast<uint16_t*>(a.x16);
   int32_t* xe = const_cast<int32_t*>(a.xe);
-  switch (a.H / 512) {
+  // rows of exactly 512, 1024, 2048 or 4096 values are held in registers;
+  // every other row length (any multiple of 8) takes the strided loop
+  switch (a.H % 512 == 0 ? a.H / 512 : 0) {
     case 1: hipLaunchKernelGGL(x_to_f16_kernel<1>, grid, block, 0, s, a.x, a.T, a.H, x16, xe); break;
     case 2: hipLaunchKernelGGL(x_to_f16_kernel<2>, grid, block, 0, s, a.x, a.T, a.H, x16, xe); break;
     case 4: hipLaunchKernelGGL(x_to_f16_kernel<4>, grid, block, 0, s, a.x, a.T, a.H, x16, xe); break;
@@ -1008,33 +1113,41 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
       OT* so = reinterpret_cast<OT*>(wst);
 #pragma unroll
       for (int mt = 0; mt < MTC; ++mt) {
-        // row weights carry the global scale; for bf16 rows, rows i and i + 1
-        // of a lane are converted as one pair and stored as halves
+        // row weights carry the global scale
+        if constexpr (sizeof(OT) == 2) {
+          // fp16 rows scaled per 32 columns, through the wave's tile as fp32
+          static_assert(16 * OC * 4 <= kWideStage, "the fp32 tile fits the wave's stage");
+          float* sf = reinterpret_cast<float*>(wst);
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const float w0 = row_w[mt * 16 + grp * 4 + i], w1 = row_w[mt * 16 + grp * 4 + i + 1];
+          for (int i = 0; i < 4; ++i) {
+            const float w0 = row_w[mt * 16 + grp * 4 + i];
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) {
-            const int o0 = (grp * 4 + i) * OC + 16 * t + col;
-            if constexpr (sizeof(OT) == 2) {
-              const unsigned p = pack_bf16(w0 * acc[mt][t][i], w1 * acc[mt][t][i + 1]);
-              reinterpret_cast<uint16_t*>(so)[o0] = (uint16_t)p;
-              reinterpret_cast<uint16_t*>(so)[o0 + OC] = (uint16_t)(p >> 16);
-            } else {
+            for (int t = 0; t < NTW; ++t) sf[(grp * 4 + i) * OC + 16 * t + col] = w0 * acc[mt][t][i];
+          }
+          store_rows_f16<OC>(sf, row_route + mt * 16, lane, static_cast<uint16_t*>(a.o), a.oe, a.flags, a.H,
+                             ch * (OC * EW) + wave * OC, ch == 0 && wave == 0);
+        } else {
+          // rows i and i + 1 of a lane
+#pragma unroll
+          for (int i = 0; i < 4; i += 2) {
+            const float w0 = row_w[mt * 16 + grp * 4 + i], w1 = row_w[mt * 16 + grp * 4 + i + 1];
+#pragma unroll
+            for (int t = 0; t < NTW; ++t) {
+              const int o0 = (grp * 4 + i) * OC + 16 * t + col;
               so[o0] = static_cast<OT>(w0 * acc[mt][t][i]);
               so[o0 + OC] = static_cast<OT>(w1 * acc[mt][t][i + 1]);
             }
           }
-        }
 #pragma unroll
-        for (int rd = 0; rd < ROUNDS; ++rd) {
-          const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(so + (q < 16 * PPR ? rr : 0) * OC + pc * EPP);
-          const int r = q < 16 * PPR ? row_route[mt * 16 + rr] : -1;
-          if (r >= 0) {
-            OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + ch * (OC * EW) + wave * OC + pc * EPP;
-            *reinterpret_cast<u32x4*>(orow) = v;
-            if (ch == 0 && wave == 0 && pc == 0) a.flags[r] = 1;
+          for (int rd = 0; rd < ROUNDS; ++rd) {
+            const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(so + (q < 16 * PPR ? rr : 0) * OC + pc * EPP);
+            const int r = q < 16 * PPR ? row_route[mt * 16 + rr] : -1;
+            if (r >= 0) {
+              OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + ch * (OC * EW) + wave * OC + pc * EPP;
+              *reinterpret_cast<u32x4*>(orow) = v;
+              if (ch == 0 && wave == 0 && pc == 0) a.flags[r] = 1;
+            }
           }
         }
       }
@@ -1228,17 +1341,21 @@ __device__ __forceinline__ void load_row8(const float* p, float* v) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
-__device__ __forceinline__ void load_row8(const bf16* p, float* v) {
+// fp16 rows (their group's 2^-e applied by the caller).  Each dword is split
+// by shifts: a bit_cast of a vector element to a half2 compiled to one dword
+// load whose halves every pair then repeated.
+__device__ __forceinline__ void load_row8(const uint16_t* p, float* v) {
   const u32x4 q = *reinterpret_cast<const u32x4*>(p);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(q[i] << 16);
-    v[2 * i + 1] = __uint_as_float(q[i] & 0xFFFF0000u);
+    const unsigned u = q[i];
+    v[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFFu)));
+    v[2 * i + 1] = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)));
   }
 }
 
 template <typename OT, bool BF16_OUT, int G>
-__global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ o,
+__global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ o, const int8_t* __restrict__ oe,
                                                       const int32_t* __restrict__ flags, int T, int k,
                                                       int H, void* __restrict__ y) {
   const int h8 = H / 8;
@@ -1260,6 +1377,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const OT* __restrict__ o,
         const int f = flags[r];
         fl[u] = j0 + u < k ? f : 0;
         load_row8(o + (size_t)r * H + 8 * c8, v[u]);
+        if constexpr (sizeof(OT) == 2) {  // the group's exponent (8 c8 .. + 7 lie in one group)
+          const float sc = __builtin_ldexpf(1.0f, -(int)oe[(size_t)r * (H / kRowGroup) + (8 * c8) / kRowGroup]);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[u][q] *= sc;
+        }
       }
 #pragma unroll
       for (int u = 0; u < G; ++u)
@@ -1493,34 +1615,19 @@ __device__ __forceinline__ void w4a8_pass(const GemmArgs& a, const int* src_row,
       }
     } else {
       constexpr int OC = 16 * NTW;   // output columns per wave
-      constexpr int EPP = 8;         // bf16 per 16-byte piece
-      constexpr int PPR = OC / EPP;  // pieces per row
-      constexpr int ROUNDS = (16 * PPR + 63) / 64;
-      bf16* so = reinterpret_cast<bf16*>(wst);
+      static_assert(16 * OC * 4 <= kWideStage, "the fp32 tile fits the wave's stage");
+      float* sf = reinterpret_cast<float*>(wst);
 #pragma unroll
       for (int mt = 0; mt < MTC; ++mt) {
+        // fp16 rows scaled per 32 columns, through the wave's tile as fp32
 #pragma unroll
-        for (int i = 0; i < 4; i += 2) {
-          const float w0 = row_w[mt * 16 + grp * 4 + i], w1 = row_w[mt * 16 + grp * 4 + i + 1];
+        for (int i = 0; i < 4; ++i) {
+          const float w0 = row_w[mt * 16 + grp * 4 + i];
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) {
-            const int o0 = (grp * 4 + i) * OC + 16 * t + col;
-            const unsigned p = pack_bf16(w0 * acc[mt][t][i], w1 * acc[mt][t][i + 1]);
-            reinterpret_cast<uint16_t*>(so)[o0] = (uint16_t)p;
-            reinterpret_cast<uint16_t*>(so)[o0 + OC] = (uint16_t)(p >> 16);
-          }
+          for (int t = 0; t < NTW; ++t) sf[(grp * 4 + i) * OC + 16 * t + col] = w0 * acc[mt][t][i];
         }
-#pragma unroll
-        for (int rd = 0; rd < ROUNDS; ++rd) {
-          const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(so + (q < 16 * PPR ? rr : 0) * OC + pc * EPP);
-          const int r = q < 16 * PPR ? row_route[mt * 16 + rr] : -1;
-          if (r >= 0) {
-            bf16* orow = static_cast<bf16*>(a.o) + (size_t)r * a.H + ch * (OC * EW) + wave * OC + pc * EPP;
-            *reinterpret_cast<u32x4*>(orow) = v;
-            if (ch == 0 && wave == 0 && pc == 0) a.flags[r] = 1;
-          }
-        }
+        store_rows_f16<OC>(sf, row_route + mt * 16, lane, static_cast<uint16_t*>(a.o), a.oe, a.flags, a.H,
+                           ch * (OC * EW) + wave * OC, ch == 0 && wave == 0);
       }
     }
   };
@@ -1663,7 +1770,7 @@ __global__ __launch_bounds__(64 * EW) void moe_w4a8_kernel(GemmArgs a, int group
 }
 
 struct WsLayout {
-  size_t h_off, o_off, flags_off, act_off, bytes;
+  size_t h_off, o_off, oe_off, flags_off, act_off, bytes;
   size_t xq_off;          // W4A8: E4M3 codes of x (h_off then holds those of h)
   size_t x16_off, xe_off;  // NVFP4: x as fp16 and its row exponents; W4A4: x's decoded NVFP4 values
   int h_rows;
@@ -1690,7 +1797,10 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
   }
   w.o_off = align256(end);
   const size_t row_bytes = wdtype == SCR_W_BF16 ? sizeof(float) : sizeof(uint16_t);
-  w.flags_off = align256(w.o_off + (size_t)R * H * row_bytes);
+  // the narrow formats' fp16 rows carry one exponent byte per kRowGroup columns
+  w.oe_off = align256(w.o_off + (size_t)R * H * row_bytes);
+  const size_t oe_bytes = wdtype == SCR_W_BF16 ? 0 : (size_t)R * (H / kRowGroup);
+  w.flags_off = align256(w.oe_off + oe_bytes);
   w.act_off = align256(w.flags_off + (size_t)R * sizeof(int32_t));
   w.bytes = align256(w.act_off + 2 * sizeof(float));
   w.x16_off = w.xe_off = 0;
@@ -1867,13 +1977,13 @@ static int run_gemms(const scr_tile_cfg& cfg, const GemmArgs& a, int max_active,
 
 // the combine, its rank group the smallest of 4, 8, 12, 16 that holds k
 template <typename OT>
-static void launch_combine(const OT* o, const int32_t* flags, int T, int k, int H, void* y, bool bf16_out,
-                           int grid, hipStream_t s) {
-#define SCR_COMBINE(G)                                                                                       \
-  if (bf16_out)                                                                                              \
-    hipLaunchKernelGGL((combine_kernel<OT, true, G>), dim3(grid), dim3(256), 0, s, o, flags, T, k, H, y);   \
-  else                                                                                                       \
-    hipLaunchKernelGGL((combine_kernel<OT, false, G>), dim3(grid), dim3(256), 0, s, o, flags, T, k, H, y);
+static void launch_combine(const OT* o, const int8_t* oe, const int32_t* flags, int T, int k, int H, void* y,
+                           bool bf16_out, int grid, hipStream_t s) {
+#define SCR_COMBINE(G)                                                                                          \
+  if (bf16_out)                                                                                                 \
+    hipLaunchKernelGGL((combine_kernel<OT, true, G>), dim3(grid), dim3(256), 0, s, o, oe, flags, T, k, H, y);  \
+  else                                                                                                          \
+    hipLaunchKernelGGL((combine_kernel<OT, false, G>), dim3(grid), dim3(256), 0, s, o, oe, flags, T, k, H, y);
   if (k <= 4) {
     SCR_COMBINE(4)
   } else if (k <= 8) {
@@ -1977,6 +2087,7 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   a.x16 = reinterpret_cast<const uint16_t*>(wsb + wl.x16_off);
   a.xe = reinterpret_cast<const int32_t*>(wsb + wl.xe_off);
   a.o = wsb + wl.o_off;
+  a.oe = reinterpret_cast<int8_t*>(wsb + wl.oe_off);
   a.flags = reinterpret_cast<int32_t*>(wsb + wl.flags_off);
   a.T = T;
   a.k = k;
@@ -2028,9 +2139,11 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   int cgrid = (int)((total + 255) / 256);
   if (cgrid > 4096) cgrid = 4096;
   if (view->wdtype != SCR_W_BF16)
-    scr::launch_combine(static_cast<const scr::bf16*>(a.o), a.flags, T, k, H, y, y_dtype == SCR_Y_BF16, cgrid, stream);
+    scr::launch_combine(static_cast<const uint16_t*>(a.o), a.oe, a.flags, T, k, H, y, y_dtype == SCR_Y_BF16, cgrid,
+                        stream);
   else
-    scr::launch_combine(static_cast<const float*>(a.o), a.flags, T, k, H, y, y_dtype == SCR_Y_BF16, cgrid, stream);
+    scr::launch_combine(static_cast<const float*>(a.o), a.oe, a.flags, T, k, H, y, y_dtype == SCR_Y_BF16, cgrid,
+                        stream);
   SCR_CHECK_LAUNCH();
   if (marks && marks[4]) SCR_CHECK_HIP(hipEventRecord(marks[4], stream));
   return SCR_OK;

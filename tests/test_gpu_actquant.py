@@ -108,8 +108,9 @@ def _layer(mode, T, E, k, H, I, seed, sc, sc2, S=None, fill=None):
 
 def _ws(mode, buf, T, H, I):
     """x's activation values and h's codes/values from the forward's workspace
-    (the layout scr_moe_workspace describes: h, per-route rows, flags, scales,
-    then for W4A4 the fp16 x).  h has R + min(R, E_layer) * 15 rows (block 16)."""
+    (the layout scr_moe_workspace describes: h, per-route rows, their exponent
+    bytes (one per 32 columns), flags, scales, then for W4A4 the fp16 x).  h
+    has R + min(R, E_layer) * 15 rows (block 16)."""
     al = lambda v: (v + 255) // 256 * 256
     ws = buf["moe_ws"].cpu().numpy()
     R = T * buf.k
@@ -119,7 +120,8 @@ def _ws(mode, buf, T, H, I):
         o_off = al(h_off + rows * I)
         return ws[:T * H].reshape(T, H), ws[h_off:h_off + rows * I].reshape(rows, I)
     o_off = al(rows * I * 2)
-    flags_off = al(o_off + R * H * 2)
+    oe_off = al(o_off + R * H * 2)
+    flags_off = al(oe_off + R * (H // 32))
     act_off = al(flags_off + R * 4)
     x16_off = al(act_off + 8)
     h = ws[:rows * I * 2].view(np.float16).reshape(rows, I)

@@ -206,7 +206,10 @@ def test_layer_view_one_layer_cache_three_per_query():
                                        (384, 16, 4, 512, 512), (500, 12, 3, 1024, 512),
                                        # wide kernels with K blocks in pairs (two activation buffers):
                                        # h streamed (I = 768) and resident (I = 256) in the down
-                                       (384, 16, 4, 512, 768), (384, 16, 4, 512, 256)])
+                                       (384, 16, 4, 512, 768), (384, 16, 4, 512, 256),
+                                       # hidden sizes that are not multiples of 512 (x's fp16 copy
+                                       # for the NVFP4 gate/up takes its strided form)
+                                       (64, 16, 4, 768, 128), (300, 12, 3, 640, 256)])
 def test_narrow_format_layer_vs_oracle_and_stream(wd, T, E, k, H, I):
     s = _setup(f"{wd}_{T}_{E}", S=2 * E, W_=8, wdtype=wd, T=T, E=E, k=k, H=H, I=I, NL=2)
     bank = _bank_for(s)
