@@ -3,11 +3,16 @@ hidden and intermediate sizes and weight format drawn per case, so that the
 kernel choices (few-rows or wide kernels, four or two activation buffers,
 pass slices, split or merged N chunks) meet shapes no hand-picked case covers.
 Each case runs the demand path against the oracle (every output element) and
-against the whole-layer stream path (bit for bit)."""
+against the whole-layer stream path (bit for bit).  The activation-quantising
+formats (W4A8, W4A4) draw their own shapes within their tiling (H a multiple
+of 512, I of 256) and per-expert input scales, and are checked as their own
+tests check them: x's codes bit-exact, every h code the oracle's or a rounding
+of a value within the GEMM's error of the oracle's h, y against the oracle."""
 import numpy as np
 import pytest
 import torch
 
+import test_gpu_actquant as A
 import test_gpu_moe as M
 from helpers import flush, rel_max_err
 
@@ -43,3 +48,29 @@ def test_random_layer_shape_vs_oracle_and_stream(i):
     assert err <= (M.TOL_BF16 if wd == "bf16" else M.TOL_FP4)
     st = M._run_stream(s, sc)
     assert torch.equal(d["y"], st["y"]), "slot path equals the whole-layer path bit for bit"
+
+
+N_ACT_CASES = 12
+
+
+def _act_case(i):
+    r = np.random.default_rng(9100 + i)
+    mode = ["w4a8", "w4a4"][i % 2]
+    E = int(r.choice([2, 3, 8, 12, 16, 40, 64, 128]))
+    k = int(r.integers(1, min(E, 8) + 1))
+    T = int(r.integers(1, 48)) if r.random() < 0.4 else int(r.integers(1, 400))
+    H = 512 * int(r.choice([1, 2, 3, 4]))
+    I = 256 * int(r.choice([1, 2, 3, 4]))
+    sc = (0.5 + r.random(E)).astype(np.float32)
+    sc2 = (0.25 + r.random(E)).astype(np.float32)
+    return mode, T, E, k, H, I, sc, sc2
+
+
+@pytest.mark.parametrize("i", range(N_ACT_CASES))
+def test_random_activation_quantising_layer_shape(i):
+    mode, T, E, k, H, I, sc, sc2 = _act_case(i)
+    flush(f"random act case {i}: {mode} T={T} E={E} k={k} H={H} I={I}")
+    env = A._layer(mode, T, E, k, H, I, 9100 + i, sc, sc2)
+    # past about a million h values a near-tie decision may flip (see the
+    # activation-quantising tests); the device-h distance is asserted always
+    A._check_layer(mode, env, T, E, k, H, I, sc, sc2, end_to_end=T * k * I <= (1 << 20))
