@@ -357,7 +357,8 @@ int scr_align_blocks_noalloc(const int32_t* ids, int n, const int32_t* id_to_buc
  * layer's experts, never by the slot count]. */
 int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_cfg* cfg);
 /* workspace of scr_grouped_moe_forward: h [cap][I] bf16 + per-route rows [T*k][H]
- * (fp32 for bf16 weights; for the narrow formats fp16 values times 2^e with one
+ * (fp32 for bf16 weights when cfg->m_chunk is 32 or the shape is one the
+ * long-chunk kernels do not take; otherwise fp16 values times 2^e with one
  * int8 e per 32 columns, [T*k][H/32] after the rows) + per-route flags + the
  * two activation scales; SCR_W_MXFP4_A8 holds the E4M3 codes of x [T][H] and
  * of h [cap][I] in place of h; SCR_W_NVFP4_A4 the decoded NVFP4 values of x

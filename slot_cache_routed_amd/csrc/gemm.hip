@@ -112,10 +112,11 @@ __device__ __forceinline__ unsigned nvfp4_pair_f16(unsigned codes, float bv) {
 
 // Weight formats: bytes of one tile-block (16 rows x 128 columns) of codes
 // and of its block scales, whether the record carries a per-tensor scale,
-// and the per-route row type: fp32 for bf16 weights (their output tolerance
-// is tighter); for the narrow formats fp16 bits scaled per 32 columns (half
-// the bytes of fp32 at the large-chunk shapes, with 11 significant bits where
-// bf16 rows kept 8; see scaled_row16).
+// and the few-rows kernels' per-route row type: fp32 for bf16 weights (their
+// output tolerance is tighter); for the narrow formats fp16 bits scaled per 32
+// columns (half the bytes of fp32, with 11 significant bits where bf16 rows
+// kept 8; see scaled_row16).  The wide kernels write the fp16 rows for every
+// format (rows_f32).
 template <int WDT>
 struct WFmt;
 template <>
@@ -160,7 +161,7 @@ struct GemmArgs {
   const int32_t* active_block_begin;
   const int32_t* n_active;
   bf16* h;              // [h_rows][I]
-  void* o;              // [R][H] per-route weighted expert outputs (RowT<WDT>)
+  void* o;              // [R][H] per-route weighted expert outputs (fp32 or fp16 rows: rows_f32)
   int8_t* oe;           // narrow formats: [R][H / kRowGroup] the rows' group exponents
   int32_t* flags;       // [R]
   const float* input_scale;       // [E] the layer's scales of the gate/up input
@@ -1105,51 +1106,21 @@ __device__ __forceinline__ void wide_pass(const GemmArgs& a, const int* src_row,
         }
       }
     } else {
-      typedef typename RowT<WDT>::type OT;
-      constexpr int OC = 16 * NTW;                  // output columns per wave
-      constexpr int EPP = 16 / (int)sizeof(OT);     // elements per 16-byte piece
-      constexpr int PPR = OC / EPP;                 // pieces per row
-      constexpr int ROUNDS = (16 * PPR + 63) / 64;  // store rounds for 16 rows
-      OT* so = reinterpret_cast<OT*>(wst);
+      // fp16 rows scaled per 32 columns (every format here), through the
+      // wave's tile as fp32; row weights carry the global scale
+      constexpr int OC = 16 * NTW;  // output columns per wave
+      static_assert(16 * OC * 4 <= kWideStage, "the fp32 tile fits the wave's stage");
+      float* sf = reinterpret_cast<float*>(wst);
 #pragma unroll
       for (int mt = 0; mt < MTC; ++mt) {
-        // row weights carry the global scale
-        if constexpr (sizeof(OT) == 2) {
-          // fp16 rows scaled per 32 columns, through the wave's tile as fp32
-          static_assert(16 * OC * 4 <= kWideStage, "the fp32 tile fits the wave's stage");
-          float* sf = reinterpret_cast<float*>(wst);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float w0 = row_w[mt * 16 + grp * 4 + i];
+        for (int i = 0; i < 4; ++i) {
+          const float w0 = row_w[mt * 16 + grp * 4 + i];
 #pragma unroll
-            for (int t = 0; t < NTW; ++t) sf[(grp * 4 + i) * OC + 16 * t + col] = w0 * acc[mt][t][i];
-          }
-          store_rows_f16<OC>(sf, row_route + mt * 16, lane, static_cast<uint16_t*>(a.o), a.oe, a.flags, a.H,
-                             ch * (OC * EW) + wave * OC, ch == 0 && wave == 0);
-        } else {
-          // rows i and i + 1 of a lane
-#pragma unroll
-          for (int i = 0; i < 4; i += 2) {
-            const float w0 = row_w[mt * 16 + grp * 4 + i], w1 = row_w[mt * 16 + grp * 4 + i + 1];
-#pragma unroll
-            for (int t = 0; t < NTW; ++t) {
-              const int o0 = (grp * 4 + i) * OC + 16 * t + col;
-              so[o0] = static_cast<OT>(w0 * acc[mt][t][i]);
-              so[o0 + OC] = static_cast<OT>(w1 * acc[mt][t][i + 1]);
-            }
-          }
-#pragma unroll
-          for (int rd = 0; rd < ROUNDS; ++rd) {
-            const int q = rd * 64 + lane, rr = q / PPR, pc = q % PPR;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(so + (q < 16 * PPR ? rr : 0) * OC + pc * EPP);
-            const int r = q < 16 * PPR ? row_route[mt * 16 + rr] : -1;
-            if (r >= 0) {
-              OT* orow = static_cast<OT*>(a.o) + (size_t)r * a.H + ch * (OC * EW) + wave * OC + pc * EPP;
-              *reinterpret_cast<u32x4*>(orow) = v;
-              if (ch == 0 && wave == 0 && pc == 0) a.flags[r] = 1;
-            }
-          }
+          for (int t = 0; t < NTW; ++t) sf[(grp * 4 + i) * OC + 16 * t + col] = w0 * acc[mt][t][i];
         }
+        store_rows_f16<OC>(sf, row_route + mt * 16, lane, static_cast<uint16_t*>(a.o), a.oe, a.flags, a.H,
+                           ch * (OC * EW) + wave * OC, ch == 0 && wave == 0);
       }
     }
   };
@@ -1778,7 +1749,36 @@ struct WsLayout {
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wdtype) {
+constexpr int kWideWaves = 8;  // two waves per SIMD in one workgroup per CU
+static_assert(kWideRing == 2, "the ring steps with either buffer count");
+// activation buffers of a wide GEMM over nkb K blocks: four where they come
+// in fours, two where they come in pairs, 0 (the wide kernels do not fit)
+static int wide_nbuf(int nkb) { return nkb % 4 == 0 ? 4 : nkb % 2 == 0 ? 2 : 0; }
+template <int WDT>
+struct WideNT {  // row tiles per wave: the bf16 weight ring holds four times the registers
+  static constexpr int value = WDT == SCR_W_BF16 ? 2 : 4;
+};
+
+template <int WDT>
+static bool wide_gemms_fit(int H, int I) {
+  constexpr int NTW = WideNT<WDT>::value;
+  // K blocks cycle through the LDS buffers and the two-block weight ring in
+  // steps of the buffer count (four, or two): an even count of K blocks
+  return wide_nbuf(H / kKB) > 0 && wide_nbuf(I / kKB) > 0 && I % (8 * NTW * kWideWaves) == 0 &&
+         H % (16 * NTW * kWideWaves) == 0;
+}
+
+// Per-route rows are fp32 for bf16 weights in the few-rows kernels (the
+// 96-token chunk's distance to the oracle is 1.08e-2 with them and, by CPU
+// emulation, 1.19e-2 with fp16 rows, which would save 4 MB of its 1 GB) and
+// the scaled fp16 rows everywhere else: every narrow format, and bf16 in the
+// wide kernels, where the rows' write and the combine's read are a large share
+// of a long chunk's traffic
+static bool rows_f32(int wdtype, int m_chunk, int H, int I) {
+  return wdtype == SCR_W_BF16 && (m_chunk == 32 || !wide_gemms_fit<SCR_W_BF16>(H, I));
+}
+
+static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int m_chunk, int wdtype) {
   WsLayout w;
   const long long R = (long long)T * k;
   const long long m = R < E_layer ? R : E_layer;
@@ -1796,10 +1796,11 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
     end = w.h_off + (size_t)rows * I * sizeof(uint16_t);
   }
   w.o_off = align256(end);
-  const size_t row_bytes = wdtype == SCR_W_BF16 ? sizeof(float) : sizeof(uint16_t);
-  // the narrow formats' fp16 rows carry one exponent byte per kRowGroup columns
+  const bool f32 = rows_f32(wdtype, m_chunk, H, I);
+  const size_t row_bytes = f32 ? sizeof(float) : sizeof(uint16_t);
+  // fp16 rows carry one exponent byte per kRowGroup columns
   w.oe_off = align256(w.o_off + (size_t)R * H * row_bytes);
-  const size_t oe_bytes = wdtype == SCR_W_BF16 ? 0 : (size_t)R * (H / kRowGroup);
+  const size_t oe_bytes = f32 ? 0 : (size_t)R * (H / kRowGroup);
   w.flags_off = align256(w.oe_off + oe_bytes);
   w.act_off = align256(w.flags_off + (size_t)R * sizeof(int32_t));
   w.bytes = align256(w.act_off + 2 * sizeof(float));
@@ -1810,25 +1811,6 @@ static WsLayout ws_layout(int T, int k, int E_layer, int H, int I, int B, int wd
     w.bytes = align256(w.xe_off + (size_t)T * sizeof(int32_t));
   }
   return w;
-}
-
-constexpr int kWideWaves = 8;  // two waves per SIMD in one workgroup per CU
-static_assert(kWideRing == 2, "the ring steps with either buffer count");
-// activation buffers of a wide GEMM over nkb K blocks: four where they come
-// in fours, two where they come in pairs, 0 (the wide kernels do not fit)
-static int wide_nbuf(int nkb) { return nkb % 4 == 0 ? 4 : nkb % 2 == 0 ? 2 : 0; }
-template <int WDT>
-struct WideNT {  // row tiles per wave: the bf16 weight ring holds four times the registers
-  static constexpr int value = WDT == SCR_W_BF16 ? 2 : 4;
-};
-
-template <int WDT>
-static bool wide_gemms_fit(const GemmArgs& a) {
-  constexpr int NTW = WideNT<WDT>::value;
-  // K blocks cycle through the LDS buffers and the two-block weight ring in
-  // steps of the buffer count (four, or two): an even count of K blocks
-  return wide_nbuf(a.H / kKB) > 0 && wide_nbuf(a.I / kKB) > 0 && a.I % (8 * NTW * kWideWaves) == 0 &&
-         a.H % (16 * NTW * kWideWaves) == 0;
 }
 
 // Pass slices: a bucket walks its rows in passes of pass_rows, and with few
@@ -1919,7 +1901,7 @@ static int launch_gemms(const GemmArgs& a, int max_active, hipEvent_t* marks, hi
 // W4A8 and W4A4: the wide kernels for every row count (their 16-row passes
 // serve few rows per expert as well); the shape must fit the wide tiling
 static bool act_quant_fits(const GemmArgs& a, int wdtype) {
-  return wdtype == SCR_W_MXFP4_A8 ? wide_gemms_fit<SCR_W_MXFP4>(a) : wide_gemms_fit<SCR_W_NVFP4_A4>(a);
+  return wdtype == SCR_W_MXFP4_A8 ? wide_gemms_fit<SCR_W_MXFP4>(a.H, a.I) : wide_gemms_fit<SCR_W_NVFP4_A4>(a.H, a.I);
 }
 
 static int launch_w4a8(const GemmArgs& a, int max_active, hipEvent_t* marks, hipStream_t s) {
@@ -1971,7 +1953,7 @@ static int run_gemms(const scr_tile_cfg& cfg, const GemmArgs& a, int max_active,
   // 2-10 rows per expert, where the down measured slower that way)
   constexpr int NTG = (WDT == SCR_W_NVFP4 || WDT == SCR_W_MXFP4) ? 4 : 2;
   if (cfg.m_chunk == 32) return launch_gemms<WDT, 2, NTG, 2>(a, max_active, marks, s);
-  if (wide_gemms_fit<WDT>(a)) return launch_wide_gemms<WDT, 7>(a, max_active, marks, s);
+  if (wide_gemms_fit<WDT>(a.H, a.I)) return launch_wide_gemms<WDT, 7>(a, max_active, marks, s);
   return launch_gemms<WDT, 7, 2, 2>(a, max_active, marks, s);
 }
 
@@ -2031,7 +2013,7 @@ extern "C" int scr_tile_config(int T, int k, int E_layer, int wdtype, scr_tile_c
 extern "C" int scr_moe_workspace(int T, int k, int E_layer, int H, int I, const scr_tile_cfg* cfg, size_t* bytes) {
   SCR_CHECK_ARG(cfg && bytes && T >= 0 && k >= 1 && E_layer >= 1 && H >= 1 && I >= 1,
                 "moe_workspace: bad arguments");
-  *bytes = scr::ws_layout(T, k, E_layer, H, I, cfg->block_m, cfg->wdtype).bytes;
+  *bytes = scr::ws_layout(T, k, E_layer, H, I, cfg->block_m, cfg->m_chunk, cfg->wdtype).bytes;
   return SCR_OK;
 }
 
@@ -2066,7 +2048,7 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   scr_record_layout lay;
   rc = scr_record_layout_of(view->wdtype, H, I, &lay);
   if (rc) return rc;
-  const scr::WsLayout wl = scr::ws_layout(T, k, E, H, I, cfg.block_m, view->wdtype);
+  const scr::WsLayout wl = scr::ws_layout(T, k, E, H, I, cfg.block_m, cfg.m_chunk, view->wdtype);
   SCR_CHECK_ARG((long long)wl.h_rows * I < (1ll << 31), "forward: T out of range");
   SCR_CHECK_ARG(ws_bytes >= wl.bytes, "forward: workspace of %zu bytes, %zu needed", ws_bytes, wl.bytes);
 
@@ -2138,7 +2120,7 @@ extern "C" int scr_grouped_moe_forward(const scr_routed_experts* view, const voi
   const size_t total = (size_t)T * (H / 8);
   int cgrid = (int)((total + 255) / 256);
   if (cgrid > 4096) cgrid = 4096;
-  if (view->wdtype != SCR_W_BF16)
+  if (!scr::rows_f32(view->wdtype, cfg.m_chunk, H, I))
     scr::launch_combine(static_cast<const uint16_t*>(a.o), a.oe, a.flags, T, k, H, y, y_dtype == SCR_Y_BF16, cgrid,
                         stream);
   else
