@@ -59,6 +59,39 @@ def test_record_layouts(lib):
     assert m.w2_scale_off == m.w2_off + (512 << 10) and m.record_bytes == m.w2_scale_off + (32 << 10)
 
 
+def _ws_bytes(T, k, E, H, I, B, wd, f32_rows):
+    """The forward's workspace as include/scr.h lays it out, each part 256-byte
+    aligned: h (A8: x's and h's codes), the per-route rows (fp32, or fp16 with
+    one exponent byte per 32 columns), the flags, the two scales, and NVFP4's
+    fp16 copy of x with its row exponents."""
+    al = lambda v: (v + 255) // 256 * 256
+    R = T * k
+    rows = (R + min(R, E) * (B - 1) + B - 1) // B * B
+    end = al(T * H) + rows * I if wd == L.SCR_W_MXFP4_A8 else rows * I * 2
+    o_end = al(end) + R * H * (4 if f32_rows else 2)
+    oe_end = al(o_end) + (0 if f32_rows else R * (H // 32))
+    total = al(al(al(oe_end) + R * 4) + 8)
+    if wd in (L.SCR_W_NVFP4, L.SCR_W_NVFP4_A4):
+        total = al(al(total + T * H * 2) + T * 4)
+    return total
+
+
+@pytest.mark.parametrize("T,k,E,H,I,wd,f32_rows", [
+    (96, 10, 512, 2048, 512, "SCR_W_BF16", True),     # few rows per expert: fp32 rows for bf16
+    (4096, 10, 512, 2048, 512, "SCR_W_BF16", False),  # the long-chunk kernels: fp16 rows
+    (4096, 10, 512, 384, 512, "SCR_W_BF16", True),    # a hidden size those kernels do not take
+    (96, 10, 512, 2048, 512, "SCR_W_NVFP4", False),
+    (4096, 10, 512, 2048, 512, "SCR_W_NVFP4", False),
+    (4096, 10, 512, 2048, 512, "SCR_W_MXFP4_A8", False),
+    (4096, 10, 512, 2048, 512, "SCR_W_NVFP4_A4", False),
+    (0, 2, 8, 256, 128, "SCR_W_FP8", False),
+])
+def test_moe_workspace_follows_its_documented_layout(lib, T, k, E, H, I, wd, f32_rows):
+    code = getattr(L, wd)
+    cfg = L.tile_config(T, k, E, code)
+    assert L.moe_workspace(T, k, E, H, I, cfg) == _ws_bytes(T, k, E, H, I, cfg.block_m, code, f32_rows)
+
+
 def test_align_capacity_formula(lib):
     assert L.align_capacity(960, 1100, 16) == 960 + 960 * 15
     assert L.align_capacity(40960, 512, 16) == 40960 + 512 * 15
