@@ -191,10 +191,13 @@ def _check_layer(mode, env, T, E, k, H, I, sc, sc2, end_to_end=True):
             # the same block scale with the element rounded from the other side
             for sg2 in (-1.0, 1.0):
                 he = (h_ref + sg2 * delta).astype(np.float32)
-                den = np.repeat(E4M3[s_], 16, axis=1).astype(np.float32) * np.float32(a2)
+                blk = np.repeat(E4M3[s_], 16, axis=1)
+                den = blk.astype(np.float32) * np.float32(a2)
                 rcp = np.where(den > 0, np.float32(1.0) / np.where(den > 0, den, np.float32(1.0)), np.float32(0.0))
                 mag = e2m1_encode_array((he * rcp.astype(np.float32)).astype(np.float32)) & 7
-                ok |= (E2M1[mag] * np.sign(he) * den.astype(np.float64)) == h_dev
+                # the decoded value is the exact product e2m1 * block * a2 (as
+                # dequant_nvfp4_act forms it), not e2m1 times the fp32 block * a2
+                ok |= (E2M1[mag] * np.sign(he) * blk * float(a2)) == h_dev
     n_diff = int((h_dev != h_or).sum())
     flush(f"{mode} {T}x{E} k={k} H={H} I={I}: h values differing from the oracle's: {n_diff} of {h_or.size}")
     assert ok.all(), f"{(~ok).sum()} h values are no rounding of a value near the oracle's h"

@@ -74,3 +74,23 @@ def test_random_activation_quantising_layer_shape(i):
     # past about a million h values a near-tie decision may flip (see the
     # activation-quantising tests); the device-h distance is asserted always
     A._check_layer(mode, env, T, E, k, H, I, sc, sc2, end_to_end=T * k * I <= (1 << 20))
+
+
+def test_w4a4_block_scale_on_a_rounding_tie():
+    """A seeded W4A4 layer (79 tokens, 64 experts, top-5, hidden and
+    intermediate 1536) in which one 16-column block of h has amax / (6 a2) on
+    an e4m3 rounding tie to fp32 precision: the device takes the lower block
+    scale, the oracle the upper, and every code of that block must still be a
+    rounding of a value within the GEMM's error of the oracle's h (checked with
+    the decoded values formed exactly, as the decode forms them)."""
+    r = np.random.default_rng(20077)
+    E = int(r.choice([1, 2, 3, 5, 8, 12, 16, 33, 40, 64, 128, 256]))
+    k = int(r.integers(1, min(E, 10) + 1))
+    T = int(r.integers(1, 48)) if r.random() < 0.35 else int(r.integers(1, 900))
+    H = 512 * int(r.choice([1, 2, 3, 4]))
+    I = 256 * int(r.choice([1, 2, 3, 4, 6]))
+    sc = (0.5 + r.random(E)).astype(np.float32)
+    sc2 = (0.25 + r.random(E)).astype(np.float32)
+    assert (T, E, k, H, I) == (79, 64, 5, 1536, 1536)
+    env = A._layer("w4a4", T, E, k, H, I, 20077, sc, sc2)
+    A._check_layer("w4a4", env, T, E, k, H, I, sc, sc2, end_to_end=False)
