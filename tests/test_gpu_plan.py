@@ -192,3 +192,62 @@ def test_all_hit_chunks_against_the_oracle(policy, stats, planner):
         for key in ("slot_key", "slot_stamp", "key_to_slot", "clock", "stats", "decode_freq", "err", "slot_crf"):
             assert np.array_equal(np.asarray(snap[key]), np.asarray(getattr(st, key))), (c, key)
     flush(f"all-hit chunks ({policy}, stats {stats}, {planner}): bank state equals the oracle")
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_seeded_chains_of_chunks_against_the_oracle(i):
+    """One bank through 24 chunks of Zipf-skewed routing over its layers, each
+    planned in one launch: bank state (LRU or LRFU, decode counters on or off,
+    capacity errors included) bit-exact against the oracle's query-by-query
+    admission after every chunk, and resident rows equal to their records."""
+    import math
+    import slot_cache_routed_amd._lib as L
+    import slot_cache_routed_amd.layer as LY
+    from oracle import dedup_sorted, route_topk_softmax
+    from oracle.lru import POLICY_LRFU
+    r = np.random.default_rng(60000 + i)
+    E = int(r.choice([8, 16, 64, 256, 512]))
+    k = int(r.integers(1, min(E, 10) + 1))
+    T = min(int(r.choice([1, 4, 16, 96, 300])), 4096 // k)
+    NL = int(r.choice([1, 2, 4]))
+    S = int(r.choice([k + 2, 16, 64, 200, 1100]))
+    width = int(r.choice([w for w in (1, 4, 16, 32, 128) if w <= S]))
+    lrfu, stats = i % 2 == 1, bool(r.integers(0, 2))
+    D = math.floor(2 ** 32 * 2 ** (-1.0 / int(r.choice([2, 16, 64]))))
+    flush(f"chain {i}: S={S} E={E} k={k} T={T} layers={NL} width={width} lrfu={lrfu} stats={stats}")
+    rec = 512
+    pool = LY.HostPool(NL, E, rec, E, payload_of=lambda key: key % E)
+    g = np.random.default_rng(60000 + i)
+    for p in range(E):
+        pool.write_payload(p, g.integers(0, 256, size=rec, dtype=np.uint8))
+    if lrfu:
+        bank = LY.Bank(S, NL, E, 0, rec, policy=L.SCR_POLICY_LRFU, lrfu_decay=D)
+    else:
+        bank = LY.Bank(S, NL, E, 0, rec)
+    st = SlotBankState(S, NL, E)
+    if lrfu:
+        st.policy, st.decay_q32 = POLICY_LRFU, D
+    buf = LY.LayerBuffers(T, E, k, 128, 128, S, 0, width=width)
+    s = torch.cuda.current_stream().cuda_stream
+    for step in range(24):
+        layer = step % NL
+        lg = W.zipf_gumbel_logits(60000 + i, layer, step, T, E)
+        L.route(torch.from_numpy(np.ascontiguousarray(lg)).cuda(), T, E, k, buf["topk_ids"], buf["topk_w"], s)
+        assert LY.plan(buf, bank, pool, layer, stats)
+        torch.cuda.synchronize()
+        ids, _ = route_topk_softmax(lg, k)
+        distinct, _, _ = dedup_sorted(ids.reshape(-1), E)
+        for q0 in range(0, len(distinct), width):
+            ensure_slots(st, layer, distinct[q0:q0 + width], stats, chunk_first=(q0 == 0))
+        snap = bank.snapshot()
+        for key in STATE_KEYS:
+            assert np.array_equal(np.asarray(snap[key]), np.asarray(getattr(st, key))), (step, key)
+        if lrfu:
+            assert np.array_equal(np.asarray(snap["slot_crf"]), np.asarray(st.slot_crf)), (step, "slot_crf")
+        if int(np.asarray(snap["err"])) == 0:
+            rows = bank.rows.view(S, -1).cpu().numpy()
+            for slot in np.nonzero(np.asarray(snap["slot_key"]) >= 0)[0]:
+                key = int(np.asarray(snap["slot_key"])[slot])
+                assert np.array_equal(rows[slot], pool.key_record(key).numpy()), (step, "row", slot)
+    hits, misses, ev, _ = [int(v) for v in st.stats]
+    flush(f"chain {i}: hits {hits} misses {misses} evictions {ev} err {int(np.asarray(st.err))}")
