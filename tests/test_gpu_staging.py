@@ -28,7 +28,7 @@ def _staging_case(T, n_layers, E, k, H, I, n_res, seed, S):
     bank = LY.Bank(S, n_layers, E, L.SCR_W_NVFP4, lay.record_bytes)
     # make each layer's resident set resident through the library's own admission
     s = torch.cuda.current_stream().cuda_stream
-    for layer in range(n_layers):
+    for layer in range(n_layers if n_res else 0):
         res = W.resident_experts(seed, layer, E, n_res)
         d = _dev(res)
         ms = torch.zeros(n_res, dtype=torch.int32, device="cuda")
@@ -42,6 +42,8 @@ def _staging_case(T, n_layers, E, k, H, I, n_res, seed, S):
 
 @pytest.mark.parametrize("T,n_layers,E,k,H,I,n_res,S", [
     (256, 3, 64, 6, 512, 256, 24, 100),
+    (96, 2, 16, 4, 256, 128, 0, 40),      # nothing resident: every expert staged
+    (96, 3, 16, 4, 256, 128, 16, 48),     # everything resident: nothing staged
     (4096, 2, 512, 10, 2048, 512, 193, 1650),
 ])
 def test_staged_layers_equal_stream_and_oracle(T, n_layers, E, k, H, I, n_res, S):
