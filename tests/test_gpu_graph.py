@@ -219,3 +219,51 @@ def test_short_prefill_96_step_as_the_bench_times_it():
     st = LY.stream_layer(pool, 0, logits, x, sc, lb, L.SCR_W_BF16, y_dtype=L.SCR_Y_BF16, shape=(k, H, I))
     torch.cuda.synchronize()
     assert torch.equal(st["y"], y_warm), "slot path equals the whole-layer path bit for bit"
+
+
+@pytest.mark.parametrize("wd,T,E,k,H,I", [
+    ("nvfp4", 4096, 512, 10, 2048, 512),    # the long-chunk NVFP4 layer: fp16 x copy, wide kernels
+    ("mxfp4_a8", 1024, 64, 4, 2048, 512),   # W4A8: x quantised, fp8 x fp4 kernels
+    ("bf16", 2048, 8, 2, 1024, 512),        # few experts: pass slices, split N chunks
+])
+def test_captured_long_chunk_forward_replays_bitwise(wd, T, E, k, H, I):
+    """Route, align and the grouped GEMM of a long chunk over a resident layer,
+    captured once and replayed three times (output overwritten with NaN and
+    eager work between replays): every replay gives the eager bits."""
+    import slot_cache_routed_amd._lib as L
+    import slot_cache_routed_amd.layer as LY
+    from helpers import wdtype_code
+    code = wdtype_code(wd)
+    lay = LY.record_layout(code, H, I)
+    P = 16
+    src = ExpertSource(41, H, I, wd)
+    pool = LY.HostPool(1, E, lay.record_bytes, P, payload_of=lambda key: key % P)
+    fill_pool(pool, src, lay, range(P))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    g = np.random.default_rng(41)
+    sc = dev((0.5 + g.random(E)).astype(np.float32))
+    sc2 = dev((0.25 + g.random(E)).astype(np.float32))
+    lg = dev(W.logits_normal(41, 0, T, E))
+    x = dev(W.f32_to_bf16_bits(W.activations_normal(41, T, H)).view(np.int16))
+    lb = LY.LayerStreamBuffer(E, lay.record_bytes)
+    kw = dict(shape=(k, H, I), down_input_scale=sc2)
+    eager = LY.stream_layer(pool, 0, lg, x, sc, lb, code, **kw)   # also copies the layer in
+    torch.cuda.synchronize()
+    ref = eager["y"].clone()
+    buf = LY.LayerBuffers(T, E, k, H, I, E, code)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            LY.stream_layer(pool, 0, lg, x, sc, lb, code, buf=buf, copy=False, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    flush(f"graph {wd} {T}x{E} k={k} H={H} I={I}: m_chunk {buf.cfg_used.m_chunk}")
+    for rep in range(3):
+        buf["y"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(buf["y"], ref), f"replay {rep}"
+        _ = (x.float() * 2).sum().item()      # eager work between replays
