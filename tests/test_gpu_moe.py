@@ -471,26 +471,27 @@ def test_full_size_4096_token_layer_in_every_weight_format(wd):
     torch.cuda.empty_cache()
 
 
-def test_forward_at_the_largest_token_count():
+@pytest.mark.parametrize("wd", ["bf16", "nvfp4"])
+def test_forward_at_the_largest_token_count(wd):
     """T * H just below 2^31, the forward's bound (T = 524,287 tokens of hidden
     4096, so x alone is 4 GiB and the activation byte offsets pass 2^31), over
-    a layer of 8 bf16 experts with top-1: about 65,500 rows per expert, so the
-    wide kernels deal each bucket's 112-row passes to many workgroups.  The
+    a layer of 8 experts with top-1: about 65,500 rows per expert, so the wide
+    kernels deal each bucket's 112-row passes to many workgroups.  NVFP4 also
+    reads its 4 GiB fp16 copy of x, whose byte offsets approach 2^32.  The
     first, middle and last tokens and a seeded sample are compared with the
     oracle."""
     import slot_cache_routed_amd.layer as LY
     import slot_cache_routed_amd._lib as L
     E, k, H, I, seed = 8, 1, 4096, 512, 13
     T = (1 << 31) // H - 1
-    code = wdtype_code("bf16")
-    src = ExpertSource(seed, H, I, "bf16")
+    code = wdtype_code(wd)
+    src = ExpertSource(seed, H, I, wd)
     lay = LY.record_layout(code, H, I)
-    flush(f"largest token count: T={T} H={H} I={I} E={E} k={k}")
+    flush(f"largest token count: {wd} T={T} H={H} I={I} E={E} k={k}")
     lb = LY.LayerStreamBuffer(E, lay.record_bytes)
     for e in range(E):
-        w13, w2 = src.raw(e)
-        lb.data[e * lay.record_bytes:(e + 1) * lay.record_bytes].copy_(
-            torch.from_numpy(LY.pack_record_bf16(lay, w13, w2)))
+        rec = LY.pack_record_nvfp4(lay, src.raw(e)) if wd == "nvfp4" else LY.pack_record_bf16(lay, *src.raw(e))
+        lb.data[e * lay.record_bytes:(e + 1) * lay.record_bytes].copy_(torch.from_numpy(rec))
     rng = np.random.default_rng(seed)
     ids = rng.integers(0, E, size=T).astype(np.int32)
     b = LY.LayerBuffers(T, E, k, H, I, E, code)
@@ -515,8 +516,8 @@ def test_forward_at_the_largest_token_count():
     y = b["y"][sel].cpu().numpy()
     y_ref = moe_layer_tokens(xs, ids[tokens].reshape(-1, 1), np.ones((tokens.size, 1)), src.f64, range(tokens.size))
     err = rel_max_err(y, y_ref)
-    flush(f"largest token count: rel max err over {tokens.size} tokens = {err:.3e}")
-    assert err <= TOL_BF16
+    flush(f"largest token count: {wd} rel max err over {tokens.size} tokens = {err:.3e}")
+    assert err <= (TOL_BF16 if wd == "bf16" else TOL_FP4)
     del x, b, lb
     torch.cuda.empty_cache()
 
